@@ -1,0 +1,201 @@
+"""Seeded synthetic inputs for the draft-block verification step.
+
+This module only *draws* data: weights, hidden states, draft noise and uniform
+coins, rounded to bf16 bit patterns.  It holds none of the verification
+arithmetic (no matmul, no softmax, no acceptance rule), so the oracle and the
+GPU library can both consume what it returns without sharing any of the
+method's code.
+
+Recipe (every array is reproducible from ``seed = 20261202 + 100*index + repeat``):
+
+* One child ``SeedSequence`` per stream, in this order: LM head, gate, up,
+  down, target hidden, draft noise, draft-sampling coins, verify coins,
+  per-request parameters.  Large streams are cut into chunks of 2**22
+  elements, each chunk with its own grandchild seed, so generation can run on
+  several threads and still be deterministic.
+* Normals are drawn in fp32, scaled in fp32 and rounded to bf16
+  (round-to-nearest-even on the fp32 bit pattern).
+* ``W_lm ~ N(0, lm_scale**2 / d)``; ``W_gate, W_up ~ N(0, 1/d)``;
+  ``W_down ~ N(0, 1/d_ff)`` (fan-in scaling; the pages give no MLP scale).
+* ``h ~ N(0, 1)`` of shape ``[B, K+1, d]``; the draft hidden is
+  ``gain_b * (h[:, :K] + sigma_b * eps)`` (MTP/EAGLE-style perturbation of the
+  same rows), with ``sigma_b`` fixed or uniform per request and ``gain_b`` 1 or
+  log-uniform per request.
+* Coins are fp32 multiples of 2**-24 in [0, 1): ``draft_coins [B, K]`` drive
+  the drafter's own sampling, ``coins [B, K+1]`` drive verification
+  (``coins[:, j]`` for draft position j+1, ``coins[:, K]`` for the final sample).
+"""
+from __future__ import annotations
+
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, replace
+import os
+
+import numpy as np
+
+BASE_SEED = 20261202
+CHUNK = 1 << 22
+_STREAMS = ("w_lm", "w_gate", "w_up", "w_down", "h", "noise", "draft_coins", "coins", "params")
+
+
+@dataclass(frozen=True)
+class Workload:
+    """Shape and distribution of one synthetic verification batch."""
+
+    name: str
+    index: int            # seed slot
+    B: int                # concurrent requests
+    K: int                # draft tokens per request (K_max in scheduled mode)
+    d: int                # hidden size
+    d_ff: int             # SwiGLU width; 0 = no MLP (y = h)
+    V: int                # vocabulary
+    T: float = 1.0        # temperature used by sampled / scheduled verification
+    sigma: float | tuple = 0.5      # draft noise std, or (lo, hi) uniform per request
+    gain: tuple | None = None       # (lo, hi) log-uniform per-request gain on the draft hidden
+    lm_scale: float = 2.5
+    threshold: float = 0.3          # survival threshold (scheduled mode)
+    budget: int = 0                 # verified-position budget (scheduled mode)
+
+    @property
+    def M_t(self) -> int:
+        return self.B * (self.K + 1)
+
+    def with_batch(self, B: int) -> "Workload":
+        return replace(self, B=B)
+
+    def weight_bytes(self) -> int:
+        return 2 * (self.V * self.d + 3 * self.d * self.d_ff)
+
+
+# Presets.  Shapes follow the pages' workloads: a 16-token parallel-drafter block
+# (K=15), K=7 parallel drafters under load, a DSpark-style scheduled batch, and a
+# short MTP-like draft on a wide model.
+TINY = Workload("tiny", 0, B=1, K=4, d=64, d_ff=0, V=512, T=1.0, sigma=0.5)
+BLOCK16 = Workload("block16", 1, B=1, K=15, d=4096, d_ff=12288, V=151936, T=1.0, sigma=0.7)
+SWEEP = Workload("sweep", 2, B=128, K=7, d=4096, d_ff=12288, V=151936, T=1.0, sigma=(0.3, 1.2))
+SCHED = Workload("sched", 3, B=64, K=15, d=4096, d_ff=12288, V=151936, T=1.0, sigma=(0.3, 1.2),
+                 threshold=0.3, budget=512)
+SCHED_STRESS = replace(SCHED, name="sched_stress", gain=(4.0, 32.0))
+WIDE = Workload("wide", 4, B=32, K=4, d=8192, d_ff=28672, V=128256, T=0.7, sigma=0.6)
+
+# Reduced shapes that the oracle finishes in seconds while still spanning several
+# GPU tiles and a ragged tail in every dimension the kernels tile.
+SMALL = Workload("small", 10, B=3, K=5, d=256, d_ff=512, V=5003, T=1.0, sigma=0.4)
+SMALL_WIDE = Workload("small_wide", 11, B=5, K=4, d=512, d_ff=1536, V=12347, T=0.7, sigma=0.6)
+SMALL_BATCH = Workload("small_batch", 12, B=40, K=7, d=256, d_ff=768, V=4099, T=1.0, sigma=(0.3, 1.2))
+SMALL_SCHED = Workload("small_sched", 13, B=24, K=15, d=256, d_ff=512, V=3001, T=1.0, sigma=(0.3, 1.2),
+                       gain=(4.0, 32.0), threshold=0.3, budget=96)
+
+PRESETS = {w.name: w for w in (TINY, BLOCK16, SWEEP, SCHED, SCHED_STRESS, WIDE,
+                               SMALL, SMALL_WIDE, SMALL_BATCH, SMALL_SCHED)}
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit pattern, round-to-nearest-even on the integer representation."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to fp32."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _normal_bf16(ss: np.random.SeedSequence, shape, scale: float) -> np.ndarray:
+    """N(0, scale**2) drawn in fp32 and rounded to bf16 bits, chunked over threads."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    nchunks = max(1, -(-n // CHUNK))
+    kids = ss.spawn(nchunks)
+    s32 = np.float32(scale)
+
+    def work(i):
+        lo, hi = i * CHUNK, min(n, (i + 1) * CHUNK)
+        g = np.random.Generator(np.random.PCG64(kids[i]))
+        x = g.standard_normal(hi - lo, dtype=np.float32)
+        x *= s32
+        out[lo:hi] = f32_to_bf16_bits(x)
+
+    if nchunks == 1:
+        work(0)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(nchunks)))
+    return out.reshape(shape)
+
+
+def _normal_f32(ss: np.random.SeedSequence, shape) -> np.ndarray:
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32)
+    nchunks = max(1, -(-n // CHUNK))
+    kids = ss.spawn(nchunks)
+    for i in range(nchunks):
+        lo, hi = i * CHUNK, min(n, (i + 1) * CHUNK)
+        np.random.Generator(np.random.PCG64(kids[i])).standard_normal(hi - lo, dtype=np.float32,
+                                                                       out=out[lo:hi])
+    return out.reshape(shape)
+
+
+def _coins(ss: np.random.SeedSequence, shape) -> np.ndarray:
+    g = np.random.Generator(np.random.PCG64(ss))
+    return (g.integers(0, 1 << 24, size=shape, dtype=np.int64).astype(np.float32)
+            * np.float32(2.0 ** -24))
+
+
+def seed_for(w: Workload, repeat: int = 0) -> int:
+    return BASE_SEED + 100 * w.index + repeat
+
+
+def generate(w: Workload, repeat: int = 0, *, weights: bool = True, keep_f32: bool = False) -> dict:
+    """Draw one batch.
+
+    Returns a dict of numpy arrays: bf16 bit patterns (uint16) for ``w_lm``,
+    ``w_gate``, ``w_up``, ``w_down`` (absent when ``d_ff == 0``), ``h``
+    ``[B, K+1, d]`` and ``h_draft`` ``[B, K, d]``; fp32 ``draft_coins [B, K]``,
+    ``coins [B, K+1]``, ``sigma [B]``, ``gain [B]``.  With ``keep_f32`` the
+    unrounded fp32 ``h_f32``, ``h_draft_f32`` and ``w_lm_f32`` are kept too (the
+    tiny configuration's statistics are taken on fp32 values).
+    """
+    root = np.random.SeedSequence(seed_for(w, repeat))
+    ss = dict(zip(_STREAMS, root.spawn(len(_STREAMS))))
+    out: dict = {}
+    B, K, d = w.B, w.K, w.d
+    if weights:
+        if keep_f32:
+            wl = _normal_f32(ss["w_lm"], (w.V, d)) * np.float32(w.lm_scale / np.sqrt(d))
+            out["w_lm_f32"] = wl
+            out["w_lm"] = f32_to_bf16_bits(wl)
+        else:
+            out["w_lm"] = _normal_bf16(ss["w_lm"], (w.V, d), w.lm_scale / np.sqrt(d))
+        if w.d_ff:
+            out["w_gate"] = _normal_bf16(ss["w_gate"], (w.d_ff, d), 1.0 / np.sqrt(d))
+            out["w_up"] = _normal_bf16(ss["w_up"], (w.d_ff, d), 1.0 / np.sqrt(d))
+            out["w_down"] = _normal_bf16(ss["w_down"], (d, w.d_ff), 1.0 / np.sqrt(w.d_ff))
+    g = np.random.Generator(np.random.PCG64(ss["params"]))
+    if isinstance(w.sigma, tuple):
+        sigma = g.uniform(w.sigma[0], w.sigma[1], size=B).astype(np.float32)
+    else:
+        sigma = np.full(B, w.sigma, dtype=np.float32)
+    if w.gain is not None:
+        lo, hi = np.log(w.gain[0]), np.log(w.gain[1])
+        gain = np.exp(g.uniform(lo, hi, size=B)).astype(np.float32)
+    else:
+        gain = np.ones(B, dtype=np.float32)
+    h32 = _normal_f32(ss["h"], (B, K + 1, d))
+    eps = _normal_f32(ss["noise"], (B, K, d))
+    hd32 = gain[:, None, None] * (h32[:, :K, :] + sigma[:, None, None] * eps)
+    out["h"] = f32_to_bf16_bits(h32)
+    out["h_draft"] = f32_to_bf16_bits(hd32)
+    if keep_f32:
+        out["h_f32"] = h32
+        out["h_draft_f32"] = hd32.astype(np.float32)
+    out["draft_coins"] = _coins(ss["draft_coins"], (B, K))
+    out["coins"] = _coins(ss["coins"], (B, K + 1))
+    out["sigma"] = sigma
+    out["gain"] = gain
+    return out

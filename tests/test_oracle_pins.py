@@ -1,0 +1,400 @@
+"""Pins of the fp64 oracle against values and facts fixed by the pages and by mathematics.
+
+Each test is chosen so that a plausible slip in the oracle (a dropped term, a swapped
+p/q, an off-by-one row, a wrong coin, double rounding) makes it fail.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import scipy.stats
+import torch
+
+import oracle
+from draft_block_verification_spec_amd import workload as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------------------- worked numbers
+
+def test_leviathan_worked_numbers():
+    g = _golden("leviathan_worked_numbers.json")
+    for e in g["expected_tokens"]:
+        assert round(oracle.expected_tokens(e["alpha"], e["gamma"]), 2) == e["value"]
+    for e in g["speedup"]:
+        assert round(oracle.speedup(e["alpha"], e["gamma"], e["c"]), 2) == e["value"]
+    for e in g["best_gamma"]:
+        k, s = oracle.best_draft_length(e["alpha"], e["c"])
+        assert k == e["gamma"]
+        assert round(s, 2) == e["value"]
+
+
+def test_expected_tokens_limits():
+    # alpha = 0: only the target's own token; alpha = 1: all K drafts plus the bonus.
+    assert oracle.expected_tokens(0.0, 7) == 1.0
+    assert oracle.expected_tokens(1.0, 7) == 8.0
+    # constant acceptance is the special case of the position-dependent closed form
+    for a, k in [(0.3, 4), (0.8, 5), (0.95, 15)]:
+        assert oracle.tau_closed_form([a] * k) == pytest.approx(oracle.expected_tokens(a, k), rel=1e-12)
+
+
+def test_position_acceptance_worked_example():
+    g = _golden("position_acceptance.json")
+    a = g["a_k"]
+    cond = oracle.conditional_acceptance(a)
+    assert round(cond[0], 2) == g["conditional_first"]
+    assert round(cond[-1], 2) == g["conditional_last"]
+    assert np.all(np.diff(cond) > -0.02)          # "grows with depth"
+    tau = oracle.tau_from_position_acceptance(a)
+    assert abs(tau - g["tau_table_one_user"]) <= g["tau_table_resolution"]
+
+
+def test_ngram_tokens_per_step():
+    g = _golden("ngram_tokens_per_step.json")
+    t = oracle.tokens_per_step(g["share_with_draft"], g["tau_drafted"])
+    assert abs(t - g["tokens_per_step_printed"]) <= g["printed_precision"]
+    assert oracle.tokens_per_step(0.0, 5.0) == 1.0
+    assert oracle.tokens_per_step(1.0, 5.0) == 5.0
+
+
+# ----------------------------------------------------------------------------- numbers
+
+def test_bf16_rne_matches_fp32_conversion():
+    rng = np.random.default_rng(0)
+    x32 = (rng.standard_normal(200_000) * np.exp(rng.uniform(-20, 20, 200_000))).astype(np.float32)
+    ref = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.bf16_rne(x32.astype(np.float64))
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_bf16_rne_ties_and_no_double_rounding():
+    one = 1.0
+    assert oracle.bf16_rne(one + 2.0 ** -8) == 1.0                     # tie -> even (down)
+    assert oracle.bf16_rne(one + 3 * 2.0 ** -8) == one + 2.0 ** -6     # tie -> even (up)
+    # just above a tie by less than an fp32 ulp: direct rounding goes up, fp64->fp32->bf16 would not
+    assert oracle.bf16_rne(one + 2.0 ** -8 + 2.0 ** -40) == one + 2.0 ** -7
+    assert oracle.bf16_rne(-(one + 2.0 ** -8 + 2.0 ** -40)) == -(one + 2.0 ** -7)
+    assert oracle.bf16_rne(0.0) == 0.0
+
+
+def test_from_bf16_bits_exact():
+    bits = np.array([0x3F80, 0xBF80, 0x4049, 0x0000, 0x7F7F], dtype=np.uint16)
+    got = oracle.from_bf16_bits(bits)
+    assert got[0] == 1.0 and got[1] == -1.0 and got[3] == 0.0
+    assert got[2] == 3.140625
+    assert got[4] == (2 - 2 ** -7) * 2.0 ** 127
+
+
+def test_target_hidden_hand_example():
+    # d = 2, d_ff = 1: g = 2, u = 3, silu(2) * 3 = 5.28478... -> bf16 5.28125; y = bf16(h + a W_down^T)
+    w = oracle.Weights(w_lm=np.eye(2), w_gate=np.array([[1.0, 0.0]]), w_up=np.array([[0.0, 1.0]]),
+                       w_down=np.array([[1.0], [0.0]]))
+    y = oracle.target_hidden(np.array([[2.0, 3.0]]), w)
+    np.testing.assert_array_equal(y, [[7.28125, 3.0]])
+    # without an MLP the hidden state passes straight to the head
+    w0 = oracle.Weights(w_lm=np.eye(2))
+    np.testing.assert_array_equal(oracle.target_hidden(np.array([[2.0, 3.0]]), w0), [[2.0, 3.0]])
+    np.testing.assert_array_equal(oracle.lm_logits(np.array([[1.0, 2.0], [0.0, -1.0], [3.0, 0.5]]),
+                                                   np.array([[2.0, 3.0]])), [[8.0, -3.0, 7.5]])
+
+
+def test_silu_values():
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(np.log(3.0)) == pytest.approx(np.log(3.0) * 0.75, rel=1e-15)
+    assert oracle.silu(-800.0) == 0.0
+
+
+def test_softmax_and_stats_against_scipy():
+    rng = np.random.default_rng(1)
+    z = rng.standard_normal((4, 3, 257)) * 3
+    for T in (1.0, 0.7, 2.5):
+        np.testing.assert_allclose(oracle.softmax_t(z, T), scipy.special.softmax(z / T, axis=-1), rtol=1e-12)
+        st = oracle.row_stats(z, T, tokens=np.zeros((4, 3), dtype=int))
+        np.testing.assert_allclose(st["lse"], scipy.special.logsumexp(z / T, axis=-1), rtol=1e-13)
+    z2 = np.array([[1.0, 5.0, 5.0, 2.0], [0.0, -1.0, 0.5, 0.25]])
+    st = oracle.row_stats(z2)
+    assert list(st["argmax"]) == [1, 2]           # lowest index wins a tie
+    assert list(st["gap"]) == [0.0, 0.25]
+    assert list(st["z_x"] if "z_x" in st else []) == []
+
+
+def test_inverse_cdf_interval_lengths():
+    # The set of coins that selects index v is an interval of length w_v / sum(w).
+    w = np.array([0.0, 3.0, 1.0, 0.0, 4.0, 2.0, 0.0])
+    N = 100_000
+    u = (np.arange(N) + 0.5) / N
+    v, lo, hi = oracle.inverse_cdf(np.broadcast_to(w, (N, w.size)), u)
+    counts = np.bincount(v, minlength=w.size)
+    np.testing.assert_allclose(counts, N * w / w.sum(), atol=1.0)
+    assert np.all(w[v] > 0)                        # zero-weight tokens are never drawn
+    assert np.all((lo <= u) & (u < hi))            # the coin lies inside its selected interval
+    v0, _, _ = oracle.inverse_cdf(w, 0.0)
+    assert v0 == 1                                 # u = 0 picks the first positive weight
+
+
+# ----------------------------------------------------------------------------- acceptance rule
+
+def _tiny_dists(rng, K, V, sharp=1.0):
+    zt = rng.standard_normal((K + 1, V)) * 1.5
+    zd = zt[:K] + rng.standard_normal((K, V)) * 1.0
+    return scipy.special.softmax(zt, axis=-1), scipy.special.softmax(sharp * zd, axis=-1)
+
+
+def _exact_law(p, q):
+    """Exact law of (A, emitted tokens) by enumerating every draft sequence and integrating
+    the coins: token j accepted with probability min(1, p_j(x)/q_j(x)); the first rejection
+    draws from max(0, p_j - q_j) normalised; full acceptance draws the bonus from p_{K+1}."""
+    K, V = q.shape
+    law = {}
+    import itertools
+    for xs in itertools.product(range(V), repeat=K):
+        w = np.prod([q[j, xs[j]] for j in range(K)])
+        if w == 0:
+            continue
+        reach = 1.0
+        for j in range(K + 1):
+            if j == K:
+                for v in range(V):
+                    key = (K, xs + (v,))
+                    law[key] = law.get(key, 0.0) + w * reach * p[K, v]
+                break
+            acc = min(1.0, p[j, xs[j]] / q[j, xs[j]])
+            rej = reach * (1.0 - acc)
+            if rej > 0:
+                r = np.maximum(0.0, p[j] - q[j])
+                r = r / r.sum()
+                for v in range(V):
+                    key = (j, xs[:j] + (v,))
+                    law[key] = law.get(key, 0.0) + w * rej * r[v]
+            reach *= acc
+    return law
+
+
+@pytest.mark.parametrize("K,V,seed", [(1, 2, 0), (2, 3, 1), (3, 4, 2), (3, 3, 3)])
+def test_exact_law_properties(K, V, seed):
+    rng = np.random.default_rng(seed)
+    p, q = _tiny_dists(rng, K, V)
+    law = _exact_law(p, q)
+    assert sum(law.values()) == pytest.approx(1.0, abs=1e-12)
+    alphas = [oracle.acceptance_rate(p[j], q[j]) for j in range(K)]
+    for k in range(1, K + 1):
+        pk = sum(v for (a, _), v in law.items() if a >= k)
+        assert pk == pytest.approx(np.prod(alphas[:k]), abs=1e-12)
+    # every emitted position, given it was reached, follows the target row (Statement 1)
+    for j in range(K + 1):
+        reached = sum(v for (a, _), v in law.items() if a >= j)
+        marg = np.zeros(V)
+        for (a, toks), v in law.items():
+            if a >= j:
+                marg[toks[j]] += v
+        np.testing.assert_allclose(marg / reached, p[j], atol=1e-12)
+
+
+@pytest.mark.parametrize("K,V,seed", [(2, 3, 4), (3, 4, 5)])
+def test_oracle_frequencies_match_exact_law(K, V, seed):
+    rng = np.random.default_rng(seed)
+    p, q = _tiny_dists(rng, K, V, sharp=2.0)
+    law = _exact_law(p, q)
+    N = 200_000
+    draft = np.stack([rng.choice(V, size=N, p=q[j]) for j in range(K)], axis=1)
+    coins = rng.random((N, K + 1))
+    res = oracle.accept_sample(np.broadcast_to(p, (N, K + 1, V)), np.broadcast_to(q, (N, K, V)), draft, coins)
+    counts = {}
+    for b in range(N):
+        a = int(res["accepted"][b])
+        key = (a, tuple(int(t) for t in res["emitted"][b, : a + 1]))
+        counts[key] = counts.get(key, 0) + 1
+    assert set(counts) <= set(law)
+    z = scipy.stats.norm.ppf(1 - 0.001 / 2 / len(law))      # Bonferroni over outcomes
+    for key, prob in law.items():
+        c = counts.get(key, 0)
+        sd = np.sqrt(N * prob * (1 - prob))
+        assert abs(c - N * prob) <= z * sd + 1, (key, c, N * prob)
+
+
+def test_statement1_chi_square_and_tau_v8():
+    """V = 8, d = 64, K = 4; h and the draft hidden fixed, fresh draft tokens and coins
+    for each of 10^6 trials.  Emitted tokens follow p (chi-square, alpha = 0.01) and the
+    mean of A + 1 matches 1 + sum_k prod_{i<=k} alpha_i within 1%."""
+    w = wl.Workload("chi8", 20, B=1, K=4, d=64, d_ff=0, V=8, T=1.0, sigma=0.9)
+    data = wl.generate(w, keep_f32=True)
+    W = oracle.Weights(w_lm=data["w_lm_f32"].astype(np.float64))
+    zt = oracle.lm_logits(W.w_lm, data["h_f32"][0].astype(np.float64))
+    zd = oracle.lm_logits(W.w_lm, data["h_draft_f32"][0].astype(np.float64))
+    p, q = oracle.softmax_t(zt, 1.0), oracle.softmax_t(zd, 1.0)
+    K, V = 4, 8
+    rng = np.random.default_rng(123)
+    N, chunk = 1_000_000, 200_000
+    hist = np.zeros((K + 1, V))
+    A_sum = 0.0
+    for _ in range(N // chunk):
+        cdf = np.cumsum(q, axis=1)
+        draft = np.stack([np.minimum(np.searchsorted(cdf[j], rng.random(chunk), side="right"), V - 1)
+                          for j in range(K)], axis=1)
+        coins = rng.random((chunk, K + 1))
+        r = oracle.accept_sample(np.broadcast_to(p, (chunk, K + 1, V)), np.broadcast_to(q, (chunk, K, V)),
+                                 draft, coins)
+        A_sum += (r["accepted"] + 1).sum()
+        for j in range(K + 1):
+            sel = r["accepted"] >= j
+            hist[j] += np.bincount(r["emitted"][sel, j], minlength=V)
+    crit1 = scipy.stats.chi2.ppf(0.99, V - 1)
+    crit_bonf = scipy.stats.chi2.ppf(1 - 0.01 / (K + 1), V - 1)
+    stats = []
+    for j in range(K + 1):
+        n = hist[j].sum()
+        stats.append(((hist[j] - n * p[j]) ** 2 / (n * p[j])).sum())
+    assert stats[0] < crit1, stats
+    assert max(stats) < crit_bonf, stats
+    alphas = [oracle.acceptance_rate(p[j], q[j]) for j in range(K)]
+    tau_emp = A_sum / N
+    assert tau_emp == pytest.approx(oracle.tau_closed_form(alphas), rel=0.01)
+
+
+def test_statement1_gate_has_power():
+    """The chi-square gate separates p from q on the V = 8 case: a verifier that simply
+    passed the draft tokens through would fail it by a wide margin."""
+    w = wl.Workload("chi8", 20, B=1, K=4, d=64, d_ff=0, V=8, T=1.0, sigma=0.9)
+    data = wl.generate(w, keep_f32=True)
+    W = oracle.Weights(w_lm=data["w_lm_f32"].astype(np.float64))
+    p = oracle.softmax_t(oracle.lm_logits(W.w_lm, data["h_f32"][0].astype(np.float64)), 1.0)
+    q = oracle.softmax_t(oracle.lm_logits(W.w_lm, data["h_draft_f32"][0].astype(np.float64)), 1.0)
+    rng = np.random.default_rng(5)
+    N = 1_000_000
+    x = rng.choice(8, size=N, p=q[0])
+    h = np.bincount(x, minlength=8)
+    stat = ((h - N * p[0]) ** 2 / (N * p[0])).sum()
+    assert stat > 100 * scipy.stats.chi2.ppf(0.99, 7)
+
+
+def test_tiny_config_tau_closed_form():
+    """Tiny configuration (B=1, K=4, d=64, V=512, fp32 values, T=1): 10 x 10^4 verify steps
+    with fresh h, noise and coins.  The mean of A + 1 matches the mean of the per-step
+    closed forms within 1%."""
+    emp, cf, n = 0.0, 0.0, 0
+    for rep in range(10):
+        w = wl.TINY.with_batch(10_000)
+        d = wl.generate(w, rep, keep_f32=True)
+        W = oracle.Weights(w_lm=d["w_lm_f32"].astype(np.float64))
+        zt = oracle.lm_logits(W.w_lm, d["h_f32"].astype(np.float64))
+        zd = oracle.lm_logits(W.w_lm, d["h_draft_f32"].astype(np.float64))
+        p, q = oracle.softmax_t(zt, 1.0), oracle.softmax_t(zd, 1.0)
+        draft, _, _ = oracle.inverse_cdf(q, d["draft_coins"])
+        r = oracle.accept_sample(p, q, draft, d["coins"])
+        alphas = np.minimum(p[:, :4], q).sum(axis=-1)
+        emp += (r["accepted"] + 1).sum()
+        cf += (1.0 + np.cumprod(alphas, axis=1).sum(axis=1)).sum()
+        n += w.B
+    assert emp / n == pytest.approx(cf / n, rel=0.01)
+    assert 1.5 < emp / n < 3.5
+
+
+# ----------------------------------------------------------------------------- greedy
+
+def test_greedy_emits_target_argmax_sequence():
+    rng = np.random.default_rng(11)
+    B, K, V = 400, 5, 6
+    z = rng.standard_normal((B, K + 1, V))
+    amax = z.argmax(-1)
+    # drafts that agree with the argmax for a random prefix, then differ
+    draft = amax[:, :K].copy()
+    cut = rng.integers(0, K + 1, size=B)
+    for b in range(B):
+        if cut[b] < K:
+            draft[b, cut[b]] = (amax[b, cut[b]] + 1 + rng.integers(0, V - 1)) % V
+    r = oracle.accept_greedy(z, draft)
+    for b in range(B):
+        A = int(r["accepted"][b])
+        assert A == cut[b]
+        for j in range(A + 1):
+            assert r["emitted"][b, j] == amax[b, j]
+        assert np.all(r["emitted"][b, A + 1:] == -1)
+
+
+def test_greedy_is_sampling_limit():
+    """As T -> 0 the sampled verifier with argmax drafts emits the greedy sequence."""
+    rng = np.random.default_rng(12)
+    B, K, V = 300, 4, 9
+    zt = rng.standard_normal((B, K + 1, V))
+    zd = zt[:, :K] + 0.5 * rng.standard_normal((B, K, V))
+    draft = zd.argmax(-1)
+    g = oracle.accept_greedy(zt, draft)
+    T = 1e-7
+    s = oracle.accept_sample(oracle.softmax_t(zt, T), oracle.softmax_t(zd, T), draft, rng.random((B, K + 1)) * 0.999)
+    np.testing.assert_array_equal(g["accepted"], s["accepted"])
+    np.testing.assert_array_equal(g["emitted"], s["emitted"])
+
+
+# ----------------------------------------------------------------------------- schedule
+
+def _brute_best_key_sum(key, elig, budget):
+    import itertools
+    B, Kmax = key.shape
+    caps = [int(np.cumprod(elig[b]).sum()) for b in range(B)]
+    best = -1
+    for ks in itertools.product(*[range(c + 1) for c in caps]):
+        if sum(ks) + B > budget:
+            continue
+        best = max(best, sum(key[b, :k].sum() for b, k in enumerate(ks)))
+    return best
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_schedule_is_optimal_and_prefix_closed(seed):
+    rng = np.random.default_rng(100 + seed)
+    B, Kmax = int(rng.integers(1, 5)), int(rng.integers(1, 5))
+    conf = np.where(rng.random((B, Kmax)) < 0.3, 1.0, rng.uniform(0.5, 1.0, (B, Kmax)))
+    budget = int(rng.integers(B, B + B * Kmax + 1))
+    r = oracle.survival_schedule(conf, 0.3, budget)
+    k = r["verify_len"]
+    s = np.cumprod(conf, axis=1)
+    assert np.all(np.diff(s, axis=1) <= 0)
+    for b in range(B):
+        assert np.all(s[b, : k[b]] >= 0.3)            # kept positions are eligible ...
+    assert (k + 1).sum() <= max(budget, B)           # ... within the budget
+    got = sum(r["key"][b, : k[b]].sum() for b in range(B))
+    assert got == _brute_best_key_sum(r["key"], r["eligible"], budget)
+
+
+def test_schedule_not_binding_takes_all_eligible():
+    conf = np.array([[0.9, 0.5, 0.9], [0.2, 1.0, 1.0], [1.0, 1.0, 0.31]])
+    r = oracle.survival_schedule(conf, 0.3, 100)
+    # survival: [0.9, 0.45, 0.405], [0.2, ...], [1, 1, 0.31]
+    assert list(r["verify_len"]) == [3, 0, 3]
+    assert not r["budget_bound"]
+
+
+def test_schedule_tie_breaking():
+    conf = np.ones((3, 4))
+    r = oracle.survival_schedule(conf, 0.3, 3 + 5)
+    # all keys equal 1024: lower request first, then lower position
+    assert list(r["verify_len"]) == [4, 1, 0]
+    conf2 = np.array([[0.5, 1.0], [0.9, 0.9], [1.0, 0.4]])
+    r2 = oracle.survival_schedule(conf2, 0.3, 3 + 2)
+    # survival 0.5,0.5 | 0.9,0.81 | 1.0,0.4 -> keys 512,512 | 921,829 | 1024,409
+    assert list(r2["verify_len"]) == [0, 1, 1]
+
+
+def test_scheduled_zero_length_request_samples_first_row():
+    """A request that verifies no draft still emits one token from p_1 and counts tau = 1."""
+    rng = np.random.default_rng(21)
+    V, d, Kmax = 16, 8, 3
+    W = oracle.Weights(w_lm=rng.standard_normal((V, d)))
+    h = rng.standard_normal((1, Kmax + 1, d))
+    hd = rng.standard_normal((1, Kmax, d)) * 0.01      # flat draft -> conf ~ 1/V -> k_b = 0
+    coins = rng.random((1, Kmax + 1))
+    draft = np.zeros((1, Kmax), dtype=int)
+    r = oracle.verify_scheduled(W, h, hd, draft, coins, 1.0, 0.3, 64)
+    assert r["verify_len"][0] == 0 and r["accepted"][0] == 0 and r["tau"] == 1.0
+    p1 = oracle.softmax_t(oracle.lm_logits(W.w_lm, h[0, :1]), 1.0)[0]
+    v, _, _ = oracle.inverse_cdf(p1, coins[0, Kmax])
+    assert r["emitted"][0, 0] == v
+    assert np.all(r["emitted"][0, 1:] == -1)
