@@ -1,0 +1,276 @@
+"""Benchmark of the draft-block verification step on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--config block16] [--no-extra] [--no-cpu]
+
+A step is one call of the whole verification path (MLP, shared LM head over the
+target and draft rows, statistics, acceptance, residual/bonus sampling, tau) on a
+batch of synthetic inputs already resident in HBM.  The headline workload is the
+16-token block (B=1, K=15, d=4096, d_ff=12288, V=151936, T=1 sampled); `value` is
+verified positions per second (B*(K+1) target rows per step).  Rank 0 prints one
+JSON line.  Extra points (greedy at B=1, greedy at B=128) are reported under
+"extra" with their own roofline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+METRIC = "verified positions/sec + accepted tokens/sec @B=1,128; % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="block16", choices=["block16", "sweep", "sched", "sched_stress", "wide"])
+    ap.add_argument("--batch", type=int, default=0, help="override B (sweep)")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--mode", default="", choices=["", "sample", "greedy", "scheduled"])
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    from draft_block_verification_spec_amd import binding as bd
+    from draft_block_verification_spec_amd import workload as wl
+
+    bd.load()  # fail loudly without the HIP library
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def to_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def to_i32(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(dev)
+
+    def to_f32(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+
+    wk = wl.PRESETS[args.config]
+    if args.batch:
+        wk = wk.with_batch(args.batch)
+    mode = args.mode or {"block16": "sample", "sweep": "greedy", "sched": "scheduled",
+                         "sched_stress": "scheduled", "wide": "sample"}[args.config]
+    t0 = time.time()
+    data = wl.generate(wk)
+    log(f"generated {wk.name} inputs in {time.time() - t0:.1f}s")
+    w = bd.Weights(to_bf16(data["w_lm"]), to_bf16(data["w_gate"]) if wk.d_ff else None,
+                   to_bf16(data["w_up"]) if wk.d_ff else None, to_bf16(data["w_down"]) if wk.d_ff else None)
+
+    def prepare(wkc, datac, modec):
+        """Device inputs, drafts from the library's own drafter step, outputs, workspace."""
+        h = to_bf16(datac["h"])
+        hd = to_bf16(datac["h_draft"])
+        u = to_f32(datac["coins"])
+        T = 0.0 if modec == "greedy" else wkc.T
+        draft, _ = bd.spec_draft_propose(w, hd, to_f32(datac["draft_coins"]), T)
+        draft = draft.contiguous()
+        B, K = wkc.B, wkc.K
+        mcode = {"greedy": bd.SV_MODE_GREEDY, "sample": bd.SV_MODE_SAMPLE, "scheduled": bd.SV_MODE_SCHEDULED}[modec]
+        out = bd.make_outputs(B, K, dev, mode=mcode, V=wkc.V, d=wkc.d)
+        ws = bd.workspace(mcode, B, K, w, dev)
+
+        def call():
+            if modec == "greedy":
+                bd.spec_verify_greedy(w, h, draft, out=out, ws=ws)
+            elif modec == "sample":
+                bd.spec_verify_sample(w, h, hd, draft, u, T, out=out, ws=ws)
+            else:
+                bd.spec_verify_scheduled(w, h, hd, draft, u, T, wkc.threshold, wkc.budget, out=out, ws=ws)
+        return call, out
+
+    def timed(call, out, steps, warmup):
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        # clean timed region: whole steps only
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        # same steps again with events around the dominant LM-head GEMM (on the call's stream)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in evs:  # materialise the HIP events; the library re-records them around the GEMM
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e2.record()
+        for i in range(steps):
+            out.ev_lm = evs[i]
+            call()
+        e3.record()
+        torch.cuda.synchronize()
+        out.ev_lm = None
+        lm_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        ms_instr = e2.elapsed_time(e3) / steps
+        return ms, lm_ms, ms_instr
+
+    call, out = prepare(wk, data, mode)
+    ms, lm_ms, ms_instr = timed(call, out, args.steps, args.warmup)
+    st = int(out.dev_status.item())
+    if st != 0:
+        raise SystemExit(f"device status {st}")
+    counters = out.counters.cpu().numpy()
+    tau = float(out.tau.item())
+    B, K, d, V, d_ff = wk.B, wk.K, wk.d, wk.V, wk.d_ff
+    vl = out.verify_len.cpu().numpy() if out.verify_len is not None else None
+    M_t = int((vl + 1).sum()) if vl is not None else B * (K + 1)
+    pos_s = M_t / (ms * 1e-3)
+    tok_s = float(counters[2]) / (ms * 1e-3)
+    rows_lm = (B * K if mode == "scheduled" else (M_t + B * K if mode == "sample" else M_t))
+    lm_bytes = 2.0 * V * d + 2.0 * rows_lm * d
+    lm_flops = 2.0 * rows_lm * d * V
+    ai = lm_flops / lm_bytes
+    if ai < 315:
+        roof = {"bound": "hbm", "achieved": lm_bytes / (lm_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": lm_flops / (lm_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_for(args.config, mode, lm_bytes)
+    roof["kernel"] = "LM-head GEMM (shared head over target and draft rows)"
+    roof["launch_ms"] = lm_ms
+    step_bytes = float(wk.weight_bytes())
+    result = {
+        "metric": METRIC, "value": pos_s, "unit": "positions/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded normals, bf16 weights; no real model)",
+        "config": {"workload": f"{wk.name}: B={B} K={K} d={d} d_ff={d_ff} V={V} mode={mode}"
+                   + (f" T={wk.T}" if mode != "greedy" else ""), "B": B, "K": K, "d": d, "d_ff": d_ff, "V": V,
+                   "mode": mode},
+        "accepted_tokens_per_sec": tok_s, "accepted_drafts_per_sec": float(counters[0]) / (ms * 1e-3),
+        "tau": tau, "step_hbm_fraction": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "ms_per_step_with_lm_events": ms_instr, "roofline": roof,
+    }
+    if mode == "scheduled":
+        result["config"]["budget"] = wk.budget
+        result["config"]["threshold"] = wk.threshold
+        result["verified_rows"] = M_t
+    log(f"{wk.name}/{mode}: {ms:.3f} ms/step, {pos_s:.0f} pos/s, LM head {lm_ms:.3f} ms "
+        f"({roof['achieved']:.0f} {roof['unit']})")
+
+    if not args.no_extra and args.config == "block16":
+        extra = []
+        # greedy on the same block
+        call_g, out_g = prepare(wk, data, "greedy")
+        msg, lmg, _ = timed(call_g, out_g, args.steps, args.warmup)
+        b_lm = 2.0 * V * d + 2.0 * B * (K + 1) * d
+        extra.append({"workload": f"block16 greedy: B=1 K=15", "ms_per_step": msg,
+                      "positions_per_sec": B * (K + 1) / (msg * 1e-3),
+                      "accepted_tokens_per_sec": float(out_g.counters.cpu().numpy()[2]) / (msg * 1e-3),
+                      "tau": float(out_g.tau.item()),
+                      "roofline": {"bound": "hbm", "achieved": b_lm / (lmg * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                                   "unit": "GB/s", "frac": b_lm / (lmg * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                   "kernel": "LM-head GEMM", "launch_ms": lmg},
+                      "step_hbm_fraction": step_bytes / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        log(f"block16/greedy: {msg:.3f} ms/step")
+        # B = 128, K = 7 greedy: the compute-bound end of the batch sweep (same weight shapes)
+        wk2 = wl.SWEEP.with_batch(128)
+        d2 = wl.generate(wk2, weights=False)
+        call2, out2 = prepare(wk2, d2, "greedy")
+        ms2, lm2, _ = timed(call2, out2, max(5, args.steps // 2), max(2, args.warmup // 2))
+        M2 = wk2.B * (wk2.K + 1)
+        flops = 2.0 * M2 * 3 * d * d_ff + 2.0 * M2 * d * V
+        lm_fl = 2.0 * M2 * d * V
+        extra.append({"workload": "sweep greedy: B=128 K=7 (same shapes)", "ms_per_step": ms2,
+                      "positions_per_sec": M2 / (ms2 * 1e-3),
+                      "accepted_tokens_per_sec": float(out2.counters.cpu().numpy()[2]) / (ms2 * 1e-3),
+                      "tau": float(out2.tau.item()),
+                      "step_tflops": flops / (ms2 * 1e-3) / 1e12,
+                      "step_mfma_fraction": flops / (ms2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                      "roofline": {"bound": "mfma", "achieved": lm_fl / (lm2 * 1e-3) / 1e12,
+                                   "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                   "frac": lm_fl / (lm2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                                   "kernel": "LM-head GEMM", "launch_ms": lm2}})
+        log(f"sweep B=128 greedy: {ms2:.3f} ms/step, {flops / (ms2 * 1e-3) / 1e12:.0f} TFLOP/s")
+        result["extra"] = extra
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(wk, data, mode, out, w, bd, torch)
+    print(json.dumps(result), flush=True)
+
+
+def traffic_for(config, mode, lm_bytes):
+    """HBM bytes per launch of the LM-head GEMM from the committed rocprofv3 counter runs,
+    if they were taken on the current kernel source; else None."""
+    path = os.path.join(HERE, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    key = f"{config}/{mode}"
+    ent = rec.get(key)
+    if not ent:
+        return None
+    import hashlib
+    src = os.path.join(HERE, "draft_block_verification_spec_amd", "csrc", ent.get("source", ""))
+    try:
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    return ent["bytes_per_launch"] if h == ent.get("source_sha256_16") else None
+
+
+def cpu_baseline(wk, data, mode, out, w, bd, torch):
+    """The fp64 oracle on the host cores: one full verification step of the same workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    W = oracle.Weights.from_bits(data)
+    B, K = wk.B, wk.K
+    rows = slice(0, min(B, 1 if wk.d >= 4096 else B))
+    nb = rows.stop - rows.start
+    h64 = oracle.from_bf16_bits(data["h"][rows])
+    hd64 = oracle.from_bf16_bits(data["h_draft"][rows])
+    # the drafts the GPU verified (from the library's drafter step)
+    coins = data["coins"][rows].astype(np.float64)
+    t0 = time.time()
+    if mode == "greedy":
+        draft = oracle.propose(W, hd64, 0.0, None)["draft"]
+        t1 = time.time()
+        oracle.verify_greedy(W, h64, draft)
+    else:
+        draft = oracle.propose(W, hd64, wk.T, data["draft_coins"][rows])["draft"]
+        t1 = time.time()
+        if mode == "sample":
+            oracle.verify_sample(W, h64, hd64, draft, coins, wk.T)
+        else:
+            oracle.verify_scheduled(W, h64, hd64, draft, coins, wk.T, wk.threshold, max(nb, wk.budget * nb // B))
+    t2 = time.time()
+    sec = t2 - t1
+    return {"value": nb * (K + 1) / sec, "unit": "positions/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{nb} request(s) x {K + 1} positions of {wk.name} ({mode}), one fp64 verify step, "
+                      f"{sec:.1f} s (drafting {t1 - t0:.1f} s not counted)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,259 @@
+"""ctypes binding of libspecverify (include/spec_verify.h).
+
+Argument marshalling only: every step of the verification runs in the HIP
+kernels of the shared library.  PyTorch supplies device memory and the stream.
+The functions carry the C names; each checks dtypes/devices, allocates the
+outputs and workspace it is not given, and raises ``SpecVerifyError`` on a
+non-zero return code.  There is no fallback: without the built library every
+call fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+
+SV_OK, SV_EINVAL, SV_EWORKSPACE, SV_EHIP = 0, -1, -2, -3
+SV_DEV_OK, SV_DEV_BAD_TOKEN, SV_DEV_NONFINITE = 0, 1, 2
+SV_MODE_GREEDY, SV_MODE_SAMPLE, SV_MODE_SCHEDULED, SV_MODE_PROPOSE = 0, 1, 2, 3
+SV_DIAG_COLS = 8
+
+EXPORTS = ("sv_workspace_bytes", "spec_verify_greedy", "spec_verify_sample", "spec_verify_scheduled",
+           "spec_draft_propose", "sv_version", "sv_strerror")
+
+
+class SpecVerifyError(RuntimeError):
+    pass
+
+
+class SvWeights(ctypes.Structure):
+    _fields_ = [("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+                ("w_lm", ctypes.c_void_p), ("d", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("V", ctypes.c_int32)]
+
+
+class SvOutputs(ctypes.Structure):
+    _fields_ = [("accepted_len", ctypes.c_void_p), ("emitted", ctypes.c_void_p), ("verify_len", ctypes.c_void_p),
+                ("tau", ctypes.c_void_p), ("counters", ctypes.c_void_p), ("dev_status", ctypes.c_void_p),
+                ("diag", ctypes.c_void_p), ("logits", ctypes.c_void_p), ("hidden", ctypes.c_void_p),
+                ("ev_lm_begin", ctypes.c_void_p), ("ev_lm_end", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load the shared library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise SpecVerifyError(f"{p} not found: build it with `python -m draft_block_verification_spec_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.sv_workspace_bytes.restype = sz
+    lib.sv_workspace_bytes.argtypes = [i32, i32, i32, ctypes.POINTER(SvWeights)]
+    lib.spec_verify_greedy.restype = i32
+    lib.spec_verify_greedy.argtypes = [ctypes.POINTER(SvWeights), vp, vp, i32, i32, vp, sz,
+                                       ctypes.POINTER(SvOutputs), vp]
+    lib.spec_verify_sample.restype = i32
+    lib.spec_verify_sample.argtypes = [ctypes.POINTER(SvWeights), vp, vp, vp, vp, f32, i32, i32, vp, sz,
+                                       ctypes.POINTER(SvOutputs), vp]
+    lib.spec_verify_scheduled.restype = i32
+    lib.spec_verify_scheduled.argtypes = [ctypes.POINTER(SvWeights), vp, vp, vp, vp, f32, f32, i32, i32, i32, vp,
+                                          sz, ctypes.POINTER(SvOutputs), vp]
+    lib.spec_draft_propose.restype = i32
+    lib.spec_draft_propose.argtypes = [ctypes.POINTER(SvWeights), vp, vp, f32, i32, vp, sz, vp, vp, vp]
+    lib.sv_version.restype = ctypes.c_char_p
+    lib.sv_strerror.restype = ctypes.c_char_p
+    lib.sv_strerror.argtypes = [i32]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _check_dev(t, dtype, name):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise SpecVerifyError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise SpecVerifyError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise SpecVerifyError(f"{name} must be contiguous")
+
+
+@dataclass
+class Weights:
+    """Device weights (bf16, row-major [out, in]) and the C struct that points at them."""
+
+    w_lm: torch.Tensor
+    w_gate: torch.Tensor | None = None
+    w_up: torch.Tensor | None = None
+    w_down: torch.Tensor | None = None
+    c: SvWeights = field(init=False)
+
+    def __post_init__(self):
+        for n in ("w_lm", "w_gate", "w_up", "w_down"):
+            _check_dev(getattr(self, n), torch.bfloat16, n)
+        V, d = self.w_lm.shape
+        d_ff = 0 if self.w_gate is None else self.w_gate.shape[0]
+        self.c = SvWeights(_ptr(self.w_gate), _ptr(self.w_up), _ptr(self.w_down), _ptr(self.w_lm), d, d_ff, V)
+
+    @property
+    def d(self):
+        return self.c.d
+
+    @property
+    def V(self):
+        return self.c.V
+
+    @property
+    def d_ff(self):
+        return self.c.d_ff
+
+
+@dataclass
+class Outputs:
+    """Output tensors of one verification call (device)."""
+
+    accepted_len: torch.Tensor
+    emitted: torch.Tensor
+    tau: torch.Tensor
+    counters: torch.Tensor
+    dev_status: torch.Tensor
+    verify_len: torch.Tensor | None = None
+    diag: torch.Tensor | None = None
+    logits: torch.Tensor | None = None
+    hidden: torch.Tensor | None = None
+    ev_lm: tuple | None = None  # (torch.cuda.Event, torch.cuda.Event) around the LM-head GEMM
+
+    def c(self) -> SvOutputs:
+        ev0 = ev1 = None
+        if self.ev_lm is not None:
+            ev0, ev1 = (e.cuda_event for e in self.ev_lm)
+        return SvOutputs(_ptr(self.accepted_len), _ptr(self.emitted), _ptr(self.verify_len), _ptr(self.tau),
+                         _ptr(self.counters), _ptr(self.dev_status), _ptr(self.diag), _ptr(self.logits),
+                         _ptr(self.hidden), ev0, ev1)
+
+
+def make_outputs(B: int, K: int, device, *, mode: int, V: int = 0, d: int = 0, diag=False, logits=False,
+                 hidden=False) -> Outputs:
+    i32 = dict(dtype=torch.int32, device=device)
+    rows_t, rows_d = B * (K + 1), (0 if mode == SV_MODE_GREEDY else B * K)
+    return Outputs(
+        accepted_len=torch.empty(B, **i32), emitted=torch.empty(B, K + 1, **i32),
+        tau=torch.empty(1, dtype=torch.float32, device=device),
+        counters=torch.empty(3, dtype=torch.int64, device=device), dev_status=torch.empty(1, **i32),
+        verify_len=torch.empty(B, **i32) if mode == SV_MODE_SCHEDULED else None,
+        diag=torch.full((rows_t + rows_d, SV_DIAG_COLS), float("nan"), dtype=torch.float32, device=device)
+        if diag else None,
+        logits=torch.full((rows_t + rows_d, V), float("nan"), dtype=torch.float32, device=device) if logits else None,
+        hidden=torch.zeros(rows_t, d, dtype=torch.bfloat16, device=device) if hidden else None)
+
+
+def sv_workspace_bytes(mode: int, B: int, K: int, w: Weights) -> int:
+    return int(load().sv_workspace_bytes(mode, B, K, ctypes.byref(w.c)))
+
+
+def workspace(mode: int, B: int, K: int, w: Weights, device=None) -> torch.Tensor:
+    n = sv_workspace_bytes(mode, B, K, w)
+    if n == 0:
+        raise SpecVerifyError("invalid sizes for the workspace")
+    return torch.empty(n, dtype=torch.uint8, device=device or w.w_lm.device)
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _raise(rc: int, what: str):
+    if rc != SV_OK:
+        msg = load().sv_strerror(rc).decode()
+        raise SpecVerifyError(f"{what} failed: {msg} ({rc})")
+
+
+def spec_verify_greedy(w: Weights, h, draft, *, out: Outputs | None = None, ws=None, stream=None, diag=False,
+                       logits=False, hidden=False) -> Outputs:
+    _check_dev(h, torch.bfloat16, "h")
+    _check_dev(draft, torch.int32, "draft")
+    B, K1, _ = h.shape
+    K = K1 - 1
+    out = out or make_outputs(B, K, h.device, mode=SV_MODE_GREEDY, V=w.V, d=w.d, diag=diag, logits=logits,
+                              hidden=hidden)
+    ws = ws if ws is not None else workspace(SV_MODE_GREEDY, B, K, w, h.device)
+    oc = out.c()
+    rc = load().spec_verify_greedy(ctypes.byref(w.c), _ptr(h), _ptr(draft), B, K, _ptr(ws), ws.numel(),
+                                   ctypes.byref(oc), _stream(stream))
+    _raise(rc, "spec_verify_greedy")
+    return out
+
+
+def spec_verify_sample(w: Weights, h, h_draft, draft, u, T: float, *, out: Outputs | None = None, ws=None,
+                       stream=None, diag=False, logits=False, hidden=False) -> Outputs:
+    _check_dev(h, torch.bfloat16, "h")
+    _check_dev(h_draft, torch.bfloat16, "h_draft")
+    _check_dev(draft, torch.int32, "draft")
+    _check_dev(u, torch.float32, "u")
+    B, K1, _ = h.shape
+    K = K1 - 1
+    out = out or make_outputs(B, K, h.device, mode=SV_MODE_SAMPLE, V=w.V, d=w.d, diag=diag, logits=logits,
+                              hidden=hidden)
+    ws = ws if ws is not None else workspace(SV_MODE_SAMPLE, B, K, w, h.device)
+    oc = out.c()
+    rc = load().spec_verify_sample(ctypes.byref(w.c), _ptr(h), _ptr(h_draft), _ptr(draft), _ptr(u), float(T), B, K,
+                                   _ptr(ws), ws.numel(), ctypes.byref(oc), _stream(stream))
+    _raise(rc, "spec_verify_sample")
+    return out
+
+
+def spec_verify_scheduled(w: Weights, h, h_draft, draft, u, T: float, survival_threshold: float, budget_rows: int,
+                          *, out: Outputs | None = None, ws=None, stream=None, diag=False, logits=False,
+                          hidden=False) -> Outputs:
+    _check_dev(h, torch.bfloat16, "h")
+    _check_dev(h_draft, torch.bfloat16, "h_draft")
+    _check_dev(draft, torch.int32, "draft")
+    _check_dev(u, torch.float32, "u")
+    B, K1, _ = h.shape
+    K = K1 - 1
+    out = out or make_outputs(B, K, h.device, mode=SV_MODE_SCHEDULED, V=w.V, d=w.d, diag=diag, logits=logits,
+                              hidden=hidden)
+    ws = ws if ws is not None else workspace(SV_MODE_SCHEDULED, B, K, w, h.device)
+    oc = out.c()
+    rc = load().spec_verify_scheduled(ctypes.byref(w.c), _ptr(h), _ptr(h_draft), _ptr(draft), _ptr(u), float(T),
+                                      float(survival_threshold), int(budget_rows), B, K, _ptr(ws), ws.numel(),
+                                      ctypes.byref(oc), _stream(stream))
+    _raise(rc, "spec_verify_scheduled")
+    return out
+
+
+def spec_draft_propose(w: Weights, h_draft, coins, T: float, *, draft_out=None, conf_out=None, ws=None,
+                       stream=None):
+    """Returns (draft ids int32 [rows], top-1 confidences fp32 [rows]) for h_draft [rows, d] (or [B, K, d])."""
+    _check_dev(h_draft, torch.bfloat16, "h_draft")
+    rows = h_draft.numel() // h_draft.shape[-1]
+    if coins is not None:
+        _check_dev(coins, torch.float32, "coins")
+    dev = h_draft.device
+    draft_out = draft_out if draft_out is not None else torch.empty(rows, dtype=torch.int32, device=dev)
+    conf_out = conf_out if conf_out is not None else torch.empty(rows, dtype=torch.float32, device=dev)
+    ws = ws if ws is not None else workspace(SV_MODE_PROPOSE, rows, 0, w, dev)
+    rc = load().spec_draft_propose(ctypes.byref(w.c), _ptr(h_draft), _ptr(coins), float(T), rows, _ptr(ws),
+                                   ws.numel(), _ptr(draft_out), _ptr(conf_out), _stream(stream))
+    _raise(rc, "spec_draft_propose")
+    return draft_out.view(h_draft.shape[:-1]), conf_out.view(h_draft.shape[:-1])
+
+
+def version() -> str:
+    return load().sv_version().decode()

@@ -1,0 +1,434 @@
+// Host side of libspecverify: argument checks, workspace plan, kernel choice and
+// the launch sequence of each verification mode.  Everything is enqueued on the
+// caller's stream; there is no host synchronisation and no allocation.
+#include <math.h>
+#include <mutex>
+
+#include "sv_internal.h"
+
+#define SV_API extern "C" __attribute__((visibility("default")))
+
+namespace sv {
+
+int num_cus() {
+  static int cus = 0;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    int dev = 0;
+    hipDeviceProp_t p;
+    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&p, dev) == hipSuccess &&
+        p.multiProcessorCount > 0)
+      cus = p.multiProcessorCount;
+    else
+      cus = 256;  // MI355X
+    (void)hipGetLastError();
+  });
+  return cus;
+}
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+size_t up(size_t x) { return (x + ALIGN - 1) & ~(ALIGN - 1); }
+
+struct Gemm {
+  bool stream = true;
+  int grid = 0;    // stream kernel
+  int bm = 0, bn = 128, splits = 1;  // tiled kernel
+  int nslots = 0;  // statistics slots per row (EPI_LOGITS)
+  size_t partial_floats = 0;
+};
+
+Gemm choose(int M, int N, int K, int epi) {
+  Gemm g;
+  if (stream_ok(M, epi)) {
+    g.stream = true;
+    const int ntiles = (N + 15) / 16;
+    g.grid = ntiles < num_cus() ? ntiles : num_cus();
+    g.nslots = g.grid;
+    return g;
+  }
+  g.stream = false;
+  g.bm = M <= 64 ? 64 : (M <= 128 ? 128 : 256);
+  const int Ncols = epi == EPI_SWIGLU ? 2 * N : N;
+  const long tiles = (long)((M + g.bm - 1) / g.bm) * ((Ncols + g.bn - 1) / g.bn);
+  if (epi != EPI_LOGITS && tiles < 2L * num_cus()) {
+    const int want = (int)((2L * num_cus() + tiles - 1) / tiles);
+    int maxs = (K / 64) / 4;
+    if (maxs < 1) maxs = 1;
+    g.splits = want < maxs ? want : maxs;
+    if (g.splits < 1) g.splits = 1;
+  }
+  if (g.splits > 1) g.partial_floats = (size_t)g.splits * M * Ncols;
+  if (epi == EPI_LOGITS) g.nslots = tiled_slots(N, g.bn);
+  return g;
+}
+
+struct Plan {
+  int mode = 0, B = 0, K = 0, d = 0, d_ff = 0, V = 0;
+  int M_t = 0, M_lm = 0, rows_d = 0, budget = 0;
+  Gemm gu, dn, lm, s1;
+  size_t o_a = 0, o_y = 0, o_part = 0, o_parts = 0, o_parts_d = 0, o_logits = 0, o_logits_d = 0,
+         o_jobs = 0, o_sums = 0, o_conf = 0, o_vlen = 0, o_rowoff = 0, o_rowmap = 0, o_mtot = 0,
+         o_hp = 0, total = 0;
+};
+
+bool valid_weights(const sv_weights *w) {
+  if (!w || !w->w_lm) return false;
+  if (w->d <= 0 || (w->d % 64) != 0) return false;
+  if (w->V < 1 || w->V >= (1 << 24)) return false;
+  if (w->d_ff < 0 || (w->d_ff % 64) != 0) return false;
+  const bool has = w->d_ff > 0;
+  if (has != (w->w_gate != nullptr) || has != (w->w_up != nullptr) || has != (w->w_down != nullptr)) return false;
+  return true;
+}
+
+bool make_plan(int mode, int B, int K, const sv_weights *w, int budget, Plan &p) {
+  if (!valid_weights(w) || B < 1 || K < 0) return false;
+  if ((long)B * (K + 1) >= (1L << 31) / 2) return false;
+  p.mode = mode; p.B = B; p.K = K; p.d = w->d; p.d_ff = w->d_ff; p.V = w->V;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += up(bytes); return o; };
+  const int d = w->d, V = w->V;
+  if (mode == SV_MODE_PROPOSE) {
+    p.M_lm = B;
+    p.lm = choose(B, V, d, EPI_LOGITS);
+    p.o_parts = take(sizeof(StatPart) * (size_t)B * p.lm.nslots);
+    p.o_logits = take(sizeof(float) * (size_t)B * V);
+    p.o_jobs = take(sizeof(SampleJob) * (size_t)B);
+    p.o_sums = take(sizeof(float) * 2 * (size_t)B * sample_chunks(V));
+    p.total = off;
+    return true;
+  }
+  int M_mlp;
+  if (mode == SV_MODE_SCHEDULED) {
+    if (budget < B) return false;
+    p.budget = budget;
+    p.rows_d = B * K;
+    M_mlp = budget < B * (K + 1) ? budget : B * (K + 1);
+    p.budget = M_mlp;
+    p.M_t = M_mlp;
+    p.M_lm = M_mlp;
+  } else {
+    p.M_t = B * (K + 1);
+    p.rows_d = B * K;
+    M_mlp = p.M_t;
+    p.M_lm = mode == SV_MODE_SAMPLE ? p.M_t + p.rows_d : p.M_t;
+  }
+  size_t part_floats = 0;
+  if (w->d_ff > 0) {
+    p.gu = choose(M_mlp, w->d_ff, d, EPI_SWIGLU);
+    p.dn = choose(M_mlp, d, w->d_ff, EPI_RESID);
+    part_floats = p.gu.partial_floats > p.dn.partial_floats ? p.gu.partial_floats : p.dn.partial_floats;
+    p.o_a = take(2 * (size_t)M_mlp * w->d_ff);
+    p.o_y = take(2 * (size_t)M_mlp * d);
+  }
+  if (part_floats) p.o_part = take(sizeof(float) * part_floats);
+  p.lm = choose(p.M_lm, V, d, EPI_LOGITS);
+  p.o_parts = take(sizeof(StatPart) * (size_t)p.M_lm * p.lm.nslots);
+  if (mode != SV_MODE_GREEDY) {
+    p.o_logits = take(sizeof(float) * (size_t)p.M_lm * V);
+    p.o_jobs = take(sizeof(SampleJob) * (size_t)B);
+    p.o_sums = take(sizeof(float) * 2 * (size_t)B * sample_chunks(V));
+  }
+  if (mode == SV_MODE_SCHEDULED) {
+    p.s1 = choose(p.rows_d > 0 ? p.rows_d : 1, V, d, EPI_LOGITS);
+    p.o_parts_d = take(sizeof(StatPart) * (size_t)(p.rows_d > 0 ? p.rows_d : 1) * p.s1.nslots);
+    p.o_logits_d = take(sizeof(float) * (size_t)(p.rows_d > 0 ? p.rows_d : 1) * V);
+    p.o_conf = take(sizeof(float) * (size_t)(p.rows_d > 0 ? p.rows_d : 1));
+    p.o_vlen = take(sizeof(int32_t) * (size_t)B);
+    p.o_rowoff = take(sizeof(int32_t) * (size_t)(B + 1));
+    p.o_rowmap = take(sizeof(int32_t) * (size_t)p.budget);
+    p.o_mtot = take(sizeof(int32_t));
+    p.o_hp = take(2 * (size_t)p.budget * d);
+  }
+  p.total = off;
+  return true;
+}
+
+bool aligned16(const void *q) { return ((uintptr_t)q & 15u) == 0; }
+
+template <typename T>
+T *at(void *ws, size_t off) { return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off); }
+
+#define SV_CHECK(expr)                       \
+  do {                                      \
+    if ((expr) != hipSuccess) {             \
+      (void)hipGetLastError();              \
+      return SV_EHIP;                       \
+    }                                       \
+  } while (0)
+
+hipError_t run_gemm(const Gemm &g, GemmArgs a, int epi, hipStream_t st) {
+  if (g.stream) return launch_gemm_stream(a, epi, g.grid, st);
+  if (g.splits > 1) {
+    hipError_t e = launch_gemm_tiled(a, epi, g.bm, g.bn, g.splits, st);
+    if (e != hipSuccess) return e;
+    return launch_splitk_reduce(a, epi, g.splits, g.bn, st);
+  }
+  return launch_gemm_tiled(a, epi, g.bm, g.bn, 1, st);
+}
+
+// The dominant GEMM of a call, bracketed by the caller's optional measurement events.
+hipError_t run_gemm_timed(const Gemm &g, const GemmArgs &a, int epi, const sv_outputs *out, hipStream_t st) {
+  if (out->ev_lm_begin) {
+    hipError_t e = hipEventRecord((hipEvent_t)out->ev_lm_begin, st);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = run_gemm(g, a, epi, st);
+  if (e != hipSuccess) return e;
+  if (out->ev_lm_end) return hipEventRecord((hipEvent_t)out->ev_lm_end, st);
+  return hipSuccess;
+}
+
+GemmArgs base_args() {
+  GemmArgs a = {};
+  a.invT = 1.f;
+  return a;
+}
+
+// S3 + S4: a = bf16(silu(h W_gate^T) * (h W_up^T)), y = bf16(h + a W_down^T).
+hipError_t run_mlp(const Plan &p, const sv_weights *w, const uint16_t *h, int M, const int *M_dev, uint16_t *y,
+                   void *ws, int32_t *status_reset, hipStream_t st) {
+  uint16_t *abuf = at<uint16_t>(ws, p.o_a);
+  GemmArgs g = base_args();
+  g.x1 = h; g.ldx1 = p.d; g.m1 = M; g.x2 = h; g.ldx2 = p.d;
+  g.M = M; g.M_dev = M_dev; g.N = p.d_ff; g.K = p.d;
+  g.w = w->w_gate; g.w2 = w->w_up;
+  g.out = abuf; g.ldo = p.d_ff;
+  g.partial = p.gu.splits > 1 ? at<float>(ws, p.o_part) : nullptr;
+  g.status_reset = status_reset;
+  hipError_t e = run_gemm(p.gu, g, EPI_SWIGLU, st);
+  if (e != hipSuccess) return e;
+  GemmArgs dn = base_args();
+  dn.x1 = abuf; dn.ldx1 = p.d_ff; dn.m1 = M; dn.x2 = abuf; dn.ldx2 = p.d_ff;
+  dn.M = M; dn.M_dev = M_dev; dn.N = p.d; dn.K = p.d_ff;
+  dn.w = w->w_down;
+  dn.out = y; dn.ldo = p.d; dn.resid = h; dn.ldr = p.d;
+  dn.partial = p.dn.splits > 1 ? at<float>(ws, p.o_part) : nullptr;
+  return run_gemm(p.dn, dn, EPI_RESID, st);
+}
+
+int check_common(const sv_weights *w, const uint16_t *h, const int32_t *draft, int B, int K, void *ws,
+                 const sv_outputs *out) {
+  if (!valid_weights(w) || !h || B < 1 || K < 0 || !out) return SV_EINVAL;
+  if (K > 0 && !draft) return SV_EINVAL;
+  if (!out->accepted_len || !out->emitted || !out->tau) return SV_EINVAL;
+  if (!aligned16(h) || !aligned16(w->w_lm)) return SV_EINVAL;
+  if (w->d_ff > 0 && (!aligned16(w->w_gate) || !aligned16(w->w_up) || !aligned16(w->w_down))) return SV_EINVAL;
+  if (ws && ((uintptr_t)ws & (ALIGN - 1))) return SV_EINVAL;
+  return SV_OK;
+}
+
+}  // namespace
+}  // namespace sv
+
+using namespace sv;
+
+SV_API size_t sv_workspace_bytes(int mode, int B, int K, const sv_weights *w) {
+  Plan p;
+  if (mode < SV_MODE_GREEDY || mode > SV_MODE_PROPOSE) return 0;
+  const int budget = mode == SV_MODE_SCHEDULED ? B * (K + 1) : 0;
+  if (!make_plan(mode, B, K, w, budget, p)) return 0;
+  return p.total ? p.total : ALIGN;
+}
+
+SV_API int spec_verify_greedy(const sv_weights *w, const uint16_t *h, const int32_t *draft, int B, int K, void *ws,
+                              size_t ws_bytes, sv_outputs *out, void *stream) {
+  int rc = check_common(w, h, draft, B, K, ws, out);
+  if (rc) return rc;
+  Plan p;
+  if (!make_plan(SV_MODE_GREEDY, B, K, w, 0, p)) return SV_EINVAL;
+  if (ws_bytes < p.total || (p.total && !ws)) return SV_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  int32_t *reset = out->dev_status;
+  const uint16_t *y = h;
+  if (p.d_ff > 0) {
+    uint16_t *ybuf = out->hidden ? out->hidden : at<uint16_t>(ws, p.o_y);
+    SV_CHECK(run_mlp(p, w, h, p.M_t, nullptr, ybuf, ws, reset, st));
+    reset = nullptr;
+    y = ybuf;
+  }
+  GemmArgs g = base_args();
+  g.x1 = y; g.ldx1 = p.d; g.m1 = p.M_t; g.x2 = y; g.ldx2 = p.d;
+  g.M = p.M_t; g.N = p.V; g.K = p.d; g.w = w->w_lm;
+  g.logits = out->logits; g.ldl = p.V;
+  g.parts = at<StatPart>(ws, p.o_parts); g.nslots = p.lm.nslots;
+  g.invT = 1.f; g.want_s = out->diag ? 1 : 0;
+  g.status_reset = reset;
+  SV_CHECK(run_gemm_timed(p.lm, g, EPI_LOGITS, out, st));
+  AcceptArgs a = {};
+  a.B = B; a.K = K; a.V = p.V; a.invT = 1.f;
+  a.parts_t = g.parts; a.nslots_t = p.lm.nslots;
+  a.logits_t = out->logits;
+  a.draft = draft; a.accepted_len = out->accepted_len; a.emitted = out->emitted;
+  a.dev_status = out->dev_status; a.diag = out->diag;
+  SV_CHECK(launch_accept_greedy(a, st));
+  SV_CHECK(launch_finalize(out->accepted_len, nullptr, B, K, out->tau, out->counters, st));
+  return SV_OK;
+}
+
+SV_API int spec_verify_sample(const sv_weights *w, const uint16_t *h, const uint16_t *h_draft, const int32_t *draft,
+                              const float *u, float T, int B, int K, void *ws, size_t ws_bytes, sv_outputs *out,
+                              void *stream) {
+  int rc = check_common(w, h, draft, B, K, ws, out);
+  if (rc) return rc;
+  if (!u || !(T > 0.f) || !isfinite(T)) return SV_EINVAL;
+  if (K > 0 && (!h_draft || !aligned16(h_draft))) return SV_EINVAL;
+  Plan p;
+  if (!make_plan(SV_MODE_SAMPLE, B, K, w, 0, p)) return SV_EINVAL;
+  if (ws_bytes < p.total || !ws) return SV_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const float invT = 1.f / T;
+  int32_t *reset = out->dev_status;
+  const uint16_t *y = h;
+  if (p.d_ff > 0) {
+    uint16_t *ybuf = out->hidden ? out->hidden : at<uint16_t>(ws, p.o_y);
+    SV_CHECK(run_mlp(p, w, h, p.M_t, nullptr, ybuf, ws, reset, st));
+    reset = nullptr;
+    y = ybuf;
+  }
+  float *logits = out->logits ? out->logits : at<float>(ws, p.o_logits);
+  GemmArgs g = base_args();
+  g.x1 = y; g.ldx1 = p.d; g.m1 = p.M_t; g.x2 = K > 0 ? h_draft : y; g.ldx2 = p.d;
+  g.M = p.M_lm; g.N = p.V; g.K = p.d; g.w = w->w_lm;
+  g.logits = logits; g.ldl = p.V;
+  g.parts = at<StatPart>(ws, p.o_parts); g.nslots = p.lm.nslots;
+  g.invT = invT; g.want_s = 1;
+  g.status_reset = reset;
+  SV_CHECK(run_gemm_timed(p.lm, g, EPI_LOGITS, out, st));
+  AcceptArgs a = {};
+  a.B = B; a.K = K; a.V = p.V; a.invT = invT;
+  a.parts_t = g.parts; a.nslots_t = p.lm.nslots;
+  a.parts_d = g.parts + (size_t)p.M_t * p.lm.nslots; a.nslots_d = p.lm.nslots;
+  a.logits_t = logits; a.logits_d = logits + (size_t)p.M_t * p.V;
+  a.draft = draft; a.u = u;
+  a.accepted_len = out->accepted_len; a.emitted = out->emitted;
+  a.jobs = at<SampleJob>(ws, p.o_jobs);
+  a.dev_status = out->dev_status; a.diag = out->diag;
+  SV_CHECK(launch_accept_sample(a, st));
+  SV_CHECK(launch_sample(a.jobs, B, p.V, invT, at<float>(ws, p.o_sums), out->emitted, st));
+  SV_CHECK(launch_finalize(out->accepted_len, nullptr, B, K, out->tau, out->counters, st));
+  return SV_OK;
+}
+
+SV_API int spec_verify_scheduled(const sv_weights *w, const uint16_t *h, const uint16_t *h_draft,
+                                 const int32_t *draft, const float *u, float T, float survival_threshold,
+                                 int budget_rows, int B, int Kmax, void *ws, size_t ws_bytes, sv_outputs *out,
+                                 void *stream) {
+  int rc = check_common(w, h, draft, B, Kmax, ws, out);
+  if (rc) return rc;
+  if (!u || !(T > 0.f) || !isfinite(T)) return SV_EINVAL;
+  if (!(survival_threshold > 0.f) || !(survival_threshold <= 1.f)) return SV_EINVAL;
+  if (budget_rows < B || (long)B * Kmax > 8192) return SV_EINVAL;
+  if (Kmax > 0 && (!h_draft || !aligned16(h_draft))) return SV_EINVAL;
+  Plan p;
+  if (!make_plan(SV_MODE_SCHEDULED, B, Kmax, w, budget_rows, p)) return SV_EINVAL;
+  if (ws_bytes < p.total || !ws) return SV_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const float invT = 1.f / T;
+  const int rows_d = B * Kmax;
+  float *logits_d = (out->logits && rows_d) ? out->logits + (size_t)B * (Kmax + 1) * p.V : at<float>(ws, p.o_logits_d);
+  StatPart *parts_d = at<StatPart>(ws, p.o_parts_d);
+  int32_t *vlen = at<int32_t>(ws, p.o_vlen);
+  int32_t *rowoff = at<int32_t>(ws, p.o_rowoff);
+  int32_t *rowmap = at<int32_t>(ws, p.o_rowmap);
+  int32_t *mtot = at<int32_t>(ws, p.o_mtot);
+  uint16_t *hp = at<uint16_t>(ws, p.o_hp);
+  int32_t *reset = out->dev_status;
+  // S1: confidences of every draft row through the shared LM head
+  if (rows_d > 0) {
+    GemmArgs g = base_args();
+    g.x1 = h_draft; g.ldx1 = p.d; g.m1 = rows_d; g.x2 = h_draft; g.ldx2 = p.d;
+    g.M = rows_d; g.N = p.V; g.K = p.d; g.w = w->w_lm;
+    g.logits = logits_d; g.ldl = p.V;
+    g.parts = parts_d; g.nslots = p.s1.nslots;
+    g.invT = invT; g.want_s = 1;
+    g.status_reset = reset;
+    reset = nullptr;
+    SV_CHECK(run_gemm_timed(p.s1, g, EPI_LOGITS, out, st));
+  }
+  // S2: survival schedule, budget, packing
+  ScheduleArgs sa = {};
+  sa.B = B; sa.Kmax = Kmax; sa.V = p.V; sa.invT = invT; sa.threshold = survival_threshold;
+  sa.budget = p.budget; sa.parts_d = parts_d; sa.nslots_d = p.s1.nslots;
+  sa.verify_len = vlen; sa.row_off = rowoff; sa.row_map = rowmap; sa.m_total = mtot;
+  sa.conf = at<float>(ws, p.o_conf); sa.dev_status = out->dev_status; sa.verify_len_out = out->verify_len;
+  sa.status_reset = reset;
+  sa.diag = out->diag;
+  sa.diag_row0 = (long)B * (Kmax + 1);
+  reset = nullptr;
+  SV_CHECK(launch_schedule(sa, st));
+  SV_CHECK(launch_gather_rows(h, hp, rowmap, mtot, p.budget, p.d, st));
+  // S3-S5 on the packed target rows
+  const uint16_t *y = hp;
+  if (p.d_ff > 0) {
+    uint16_t *ybuf = at<uint16_t>(ws, p.o_y);
+    SV_CHECK(run_mlp(p, w, hp, p.budget, mtot, ybuf, ws, nullptr, st));
+    y = ybuf;
+  }
+  float *logits_t = at<float>(ws, p.o_logits);
+  GemmArgs g = base_args();
+  g.x1 = y; g.ldx1 = p.d; g.m1 = p.budget; g.x2 = y; g.ldx2 = p.d;
+  g.M = p.budget; g.M_dev = mtot; g.N = p.V; g.K = p.d; g.w = w->w_lm;
+  g.logits = logits_t; g.ldl = p.V;
+  g.parts = at<StatPart>(ws, p.o_parts); g.nslots = p.lm.nslots;
+  g.invT = invT; g.want_s = 1;
+  SV_CHECK(run_gemm(p.lm, g, EPI_LOGITS, st));
+  // S6-S9
+  AcceptArgs a = {};
+  a.B = B; a.K = Kmax; a.V = p.V; a.invT = invT;
+  a.parts_t = g.parts; a.nslots_t = p.lm.nslots;
+  a.parts_d = parts_d; a.nslots_d = p.s1.nslots;
+  a.logits_t = logits_t; a.logits_d = logits_d;
+  a.draft = draft; a.u = u; a.verify_len = vlen; a.row_off = rowoff;
+  a.accepted_len = out->accepted_len; a.emitted = out->emitted;
+  a.jobs = at<SampleJob>(ws, p.o_jobs);
+  a.dev_status = out->dev_status; a.diag = out->diag;
+  SV_CHECK(launch_accept_sample(a, st));
+  SV_CHECK(launch_sample(a.jobs, B, p.V, invT, at<float>(ws, p.o_sums), out->emitted, st));
+  SV_CHECK(launch_finalize(out->accepted_len, vlen, B, Kmax, out->tau, out->counters, st));
+  if (out->logits) SV_CHECK(launch_scatter_logits(logits_t, out->logits, rowmap, mtot, p.budget, p.V, st));
+  if (out->hidden && p.d_ff > 0)
+    SV_CHECK(launch_scatter_hidden(at<uint16_t>(ws, p.o_y), out->hidden, rowmap, mtot, p.budget, p.d, st));
+  return SV_OK;
+}
+
+SV_API int spec_draft_propose(const sv_weights *w, const uint16_t *h_draft, const float *coins, float T, int rows,
+                              void *ws, size_t ws_bytes, int32_t *draft_out, float *conf_out, void *stream) {
+  if (!valid_weights(w) || !h_draft || rows < 1 || !draft_out) return SV_EINVAL;
+  if (!(T >= 0.f) || !isfinite(T) || (T > 0.f && !coins)) return SV_EINVAL;
+  if (!aligned16(h_draft) || !aligned16(w->w_lm)) return SV_EINVAL;
+  if (ws && ((uintptr_t)ws & (ALIGN - 1))) return SV_EINVAL;
+  Plan p;
+  if (!make_plan(SV_MODE_PROPOSE, rows, 0, w, 0, p)) return SV_EINVAL;
+  if (ws_bytes < p.total || !ws) return SV_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const bool samp = T > 0.f;
+  const float invT = samp ? 1.f / T : 1.f;
+  float *logits = at<float>(ws, p.o_logits);
+  GemmArgs g = base_args();
+  g.x1 = h_draft; g.ldx1 = p.d; g.m1 = rows; g.x2 = h_draft; g.ldx2 = p.d;
+  g.M = rows; g.N = p.V; g.K = p.d; g.w = w->w_lm;
+  g.logits = samp ? logits : nullptr; g.ldl = p.V;
+  g.parts = at<StatPart>(ws, p.o_parts); g.nslots = p.lm.nslots;
+  g.invT = invT; g.want_s = samp ? 1 : 0;
+  SV_CHECK(run_gemm(p.lm, g, EPI_LOGITS, st));
+  SampleJob *jobs = at<SampleJob>(ws, p.o_jobs);
+  SV_CHECK(launch_propose_finish(g.parts, p.lm.nslots, rows, invT, T, logits, p.V, coins, jobs, draft_out, conf_out,
+                                 nullptr, st));
+  if (samp) SV_CHECK(launch_sample(jobs, rows, p.V, invT, at<float>(ws, p.o_sums), draft_out, st));
+  return SV_OK;
+}
+
+SV_API const char *sv_version(void) { return "specverify 0.1.0 (gfx950)"; }
+
+SV_API const char *sv_strerror(int code) {
+  switch (code) {
+    case SV_OK: return "ok";
+    case SV_EINVAL: return "invalid argument";
+    case SV_EWORKSPACE: return "workspace too small";
+    case SV_EHIP: return "HIP runtime error";
+    default: return "unknown error";
+  }
+}

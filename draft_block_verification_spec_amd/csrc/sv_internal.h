@@ -1,0 +1,147 @@
+// Internal declarations shared by the HIP translation units of libspecverify.
+// Not part of the public ABI (see include/spec_verify.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "spec_verify.h"
+
+namespace sv {
+
+// ---------------------------------------------------------------- vector types
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Per-row partial statistics of a logit row over a subset of its columns:
+// b1 = max z, b2 = second largest z, i1 = lowest column index attaining b1,
+// s = sum over the subset of exp((z - b1) * invT).  Empty: b1 = b2 = -inf, s = 0.
+struct StatPart {
+  float b1, b2, s;
+  int i1;
+};
+
+enum Epilogue : int {
+  EPI_LOGITS = 0,  // fp32 logits (optional) + per-row StatPart partials
+  EPI_SWIGLU = 1,  // a = bf16(silu(g) * u), g/u from paired weight rows
+  EPI_RESID = 2,   // y = bf16(resid + acc)
+  EPI_RAW = 3,     // fp32 split-K partial, no epilogue
+};
+
+// Arguments of the GEMM kernels: out[m, n] = sum_k X[m, k] * W[n, k].
+// X rows m < m1 come from x1 (row stride ldx1), rows m1 <= m < M from x2.
+struct GemmArgs {
+  const uint16_t *x1;
+  const uint16_t *x2;
+  long ldx1, ldx2;
+  int m1;
+  int M;             // rows (upper bound when M_dev is given)
+  const int *M_dev;  // optional device-side row count (scheduled mode)
+  int N;             // output columns (for SWIGLU: columns of a)
+  int K;             // reduction length, multiple of 64
+  const uint16_t *w;   // [N, K] (SWIGLU: gate rows)
+  const uint16_t *w2;  // SWIGLU: up rows [N, K]
+  // EPI_LOGITS
+  float *logits;  // may be null
+  long ldl;
+  StatPart *parts;
+  int nslots;
+  float invT;
+  int want_s;  // compute the sum-exp part of the statistics
+  // EPI_SWIGLU / EPI_RESID
+  uint16_t *out;
+  long ldo;
+  const uint16_t *resid;
+  long ldr;
+  // EPI_RAW (split-K partials [splits][M][Ncols])
+  float *partial;
+  // zeroed by thread 0 of block 0 before anything else (device status of the call)
+  int32_t *status_reset;
+};
+
+// Sampling job: draw v from w_v = max(0, exp(z1_v*invT - lse1) - [z2 ? exp(z2_v*invT - lse2) : 0])
+// by inverse CDF with coin u; if the weights sum to zero, fall back to exp(z1_v*invT - lse1).
+struct SampleJob {
+  const float *z1;
+  const float *z2;  // may be null
+  float lse1, lse2;
+  float u;
+  int out_index;  // index into the int32 output array
+};
+
+// Number of compute units of the current device (cached).
+int num_cus();
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_gemm_stream(const GemmArgs &a, int epi, int grid, hipStream_t st);
+int stream_grid(const GemmArgs &a, int epi);
+bool stream_ok(int M, int epi);
+
+hipError_t launch_gemm_tiled(const GemmArgs &a, int epi, int bm, int bn, int splits, hipStream_t st);
+int tiled_slots(int N, int bn);
+hipError_t launch_splitk_reduce(const GemmArgs &a, int epi, int splits, int bn, hipStream_t st);
+
+struct AcceptArgs {
+  int B, K, V;  // K = Kmax in scheduled mode
+  float invT;
+  const StatPart *parts_t;  // target-row partials [rows][nslots_t]
+  int nslots_t;
+  const StatPart *parts_d;  // draft-row partials [B*K][nslots_d]
+  int nslots_d;
+  const float *logits_t;  // target logits (packed rows in scheduled mode), row stride V
+  const float *logits_d;  // draft logits, row stride V
+  const int32_t *draft;   // [B, K]
+  const float *u;         // [B, K+1]
+  const int32_t *verify_len;  // scheduled: k_b, else null
+  const int32_t *row_off;     // scheduled: packed target row base per request, else null
+  int32_t *accepted_len;
+  int32_t *emitted;
+  SampleJob *jobs;  // one per request (sample / scheduled)
+  int32_t *dev_status;
+  float *diag;  // may be null
+};
+hipError_t launch_accept_sample(const AcceptArgs &a, hipStream_t st);
+hipError_t launch_accept_greedy(const AcceptArgs &a, hipStream_t st);
+
+int sample_chunks(int V);
+hipError_t launch_sample(const SampleJob *jobs, int njobs, int V, float invT, float *chunk_sums,
+                         int32_t *out, hipStream_t st);
+
+hipError_t launch_finalize(const int32_t *accepted_len, const int32_t *verify_len, int B, int K,
+                           float *tau, int64_t *counters, hipStream_t st);
+
+hipError_t launch_init(int32_t *zero_i32, size_t n_i32, int32_t *dev_status, hipStream_t st);
+
+struct ScheduleArgs {
+  int B, Kmax, V;
+  float invT, threshold;
+  int budget;
+  const StatPart *parts_d;
+  int nslots_d;
+  int32_t *verify_len;  // [B]
+  int32_t *row_off;     // [B+1]
+  int32_t *row_map;     // [budget] packed row -> b*(Kmax+1)+j
+  int32_t *m_total;     // [1]
+  float *conf;          // [B*Kmax]
+  int32_t *dev_status;
+  int32_t *verify_len_out;  // optional copy for the caller
+  int32_t *status_reset;    // zeroed first when non-null
+  float *diag;              // optional per-row records; draft rows start at row diag_row0
+  long diag_row0;
+};
+hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t st);
+hipError_t launch_gather_rows(const uint16_t *src, uint16_t *dst, const int32_t *row_map,
+                              const int32_t *m_total, int max_rows, int d, hipStream_t st);
+hipError_t launch_scatter_logits(const float *packed, float *dst, const int32_t *row_map,
+                                 const int32_t *m_total, int max_rows, int V, hipStream_t st);
+hipError_t launch_scatter_hidden(const uint16_t *packed, uint16_t *dst, const int32_t *row_map,
+                                 const int32_t *m_total, int max_rows, int d, hipStream_t st);
+hipError_t launch_propose_finish(const StatPart *parts, int nslots, int rows, float invT, float T,
+                                 const float *logits, int V, const float *coins, SampleJob *jobs,
+                                 int32_t *draft_out, float *conf_out, int32_t *dev_status,
+                                 hipStream_t st);
+
+}  // namespace sv

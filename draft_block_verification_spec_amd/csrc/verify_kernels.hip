@@ -1,0 +1,581 @@
+// Acceptance, sampling, scheduling and bookkeeping kernels of the verification step.
+//
+// Rules implemented (page titles and sections):
+//  * Wildberries page, "A bit of theory", Statement 1: draft token x passes with
+//    probability min(1, p(x)/q(x)), with p and q taken after temperature; at the
+//    first rejection the token is drawn from the normalised max(0, p - q).
+//  * "Let's start over, Misha", "How it works": tokens are checked left to right;
+//    when all K pass the bonus token comes from the same pass.  "Why isn't the
+//    answer spoiled?": at temperature 0 the check is an argmax match.
+//  * DSpark summary page: the verify length of each request follows the
+//    estimated survival probability of its draft prefix, under a capacity budget.
+#include "sv_device.h"
+
+namespace sv {
+
+namespace {
+
+constexpr int NT = 256;  // threads per block for the small kernels
+
+__device__ void set_status(int32_t *st, int code) {
+  if (st) atomicCAS(st, 0, code);
+}
+
+// Merge the nslots partials of one row with one wave; result valid in every lane.
+__device__ StatPart wave_merge_row(const StatPart *parts, int nslots, float invT, bool want_s) {
+  const int lane = threadIdx.x & 63;
+  StatPart st = stat_empty();
+  for (int i = lane; i < nslots; i += 64) st = stat_merge(st, parts[i], invT, want_s);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) st = stat_merge(st, stat_shfl_xor(st, off), invT, want_s);
+  return st;
+}
+
+__global__ void k_init(int32_t *z, long n, int32_t *dev_status) {
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) z[i] = 0;
+  if (dev_status && blockIdx.x == 0 && threadIdx.x == 0) *dev_status = 0;
+}
+
+// One block per request.  Row statistics are merged by one wave per row.
+__global__ __launch_bounds__(NT) void k_accept_sample(const AcceptArgs a) {
+  extern __shared__ float sm[];
+  const int b = blockIdx.x;
+  const int Kmax = a.K;
+  const int Kb = a.verify_len ? a.verify_len[b] : Kmax;
+  const long trow0 = a.row_off ? a.row_off[b] : (long)b * (Kmax + 1);
+  const long drow0 = (long)b * Kmax;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float *lse_t = sm;                  // [Kmax+1]
+  float *lse_d = sm + (Kmax + 1);     // [Kmax]
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+
+  // row statistics: target rows 0..Kb, draft rows 0..Kb-1
+  const int nrows = 2 * Kb + 1;
+  for (int r = wave; r < nrows; r += NT / 64) {
+    const bool is_t = r <= Kb;
+    const int j = is_t ? r : r - Kb - 1;
+    const StatPart *pp = is_t ? a.parts_t + (trow0 + j) * a.nslots_t : a.parts_d + (drow0 + j) * a.nslots_d;
+    const StatPart st = wave_merge_row(pp, is_t ? a.nslots_t : a.nslots_d, a.invT, true);
+    const float lse = st.b1 * a.invT + __logf(st.s);
+    if (lane == 0) {
+      if (is_t) lse_t[j] = lse; else lse_d[j] = lse;
+      if (!isfinite(lse)) bad = SV_DEV_NONFINITE;
+      if (a.diag) {
+        const long drow = is_t ? (long)b * (Kmax + 1) + j : (long)a.B * (Kmax + 1) + drow0 + j;
+        float *dg = a.diag + drow * SV_DIAG_COLS;
+        dg[0] = lse; dg[1] = (float)st.i1; dg[2] = st.b1 - st.b2; dg[3] = st.b1;
+        dg[4] = NAN; dg[5] = NAN; dg[6] = is_t ? NAN : __expf(st.b1 * a.invT - lse); dg[7] = 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  // acceptance decisions: lane j of wave 0 handles draft position j+1
+  if (wave == 0) {
+    bool ok = true;
+    int A = 0;
+    bool rej = false;
+    for (int base = 0; base < Kb; base += 64) {
+      const int j = base + lane;
+      bool acc = false, bad_tok = false;
+      if (j < Kb) {
+        const int x = a.draft[drow0 + j];
+        if (x < 0 || x >= a.V) {
+          bad_tok = true;
+        } else {
+          const float zt = a.logits_t[(trow0 + j) * (long)a.V + x];
+          const float zd = a.logits_d[(drow0 + j) * (long)a.V + x];
+          const float lpt = zt * a.invT - lse_t[j];
+          const float lqd = zd * a.invT - lse_d[j];
+          const float ratio = __expf(lpt - lqd);
+          const float u = a.u[(long)b * (Kmax + 1) + j];
+          acc = u < ratio;
+          if (a.diag) {
+            float *dt = a.diag + ((long)b * (Kmax + 1) + j) * SV_DIAG_COLS;
+            dt[4] = zt; dt[5] = __expf(lpt); dt[6] = ratio;
+            float *dd = a.diag + ((long)a.B * (Kmax + 1) + drow0 + j) * SV_DIAG_COLS;
+            dd[4] = zd; dd[5] = __expf(lqd);
+          }
+        }
+      }
+      if (__any(bad_tok)) ok = false;
+      if (!rej) {
+        const unsigned long long live = (Kb - base >= 64) ? ~0ull : ((1ull << (Kb - base)) - 1ull);
+        const unsigned long long rejm = __ballot(!acc) & live;
+        if (rejm) {
+          A = base + __ffsll((long long)rejm) - 1;
+          rej = true;
+        } else {
+          A = min(Kb, base + 64);
+        }
+      }
+    }
+    if (lane == 0) {
+      if (!ok) set_status(a.dev_status, SV_DEV_BAD_TOKEN);
+      if (bad) set_status(a.dev_status, bad);
+      const bool good = ok && !bad;
+      a.accepted_len[b] = good ? A : -1;
+      SampleJob jb;
+      jb.u = a.u[(long)b * (Kmax + 1) + Kmax];
+      jb.lse1 = lse_t[A];
+      jb.z1 = a.logits_t + (trow0 + A) * (long)a.V;
+      if (A < Kb) {
+        jb.z2 = a.logits_d + (drow0 + A) * (long)a.V;
+        jb.lse2 = lse_d[A];
+      } else {
+        jb.z2 = nullptr;
+        jb.lse2 = 0.f;
+      }
+      jb.out_index = good ? b * (Kmax + 1) + A : -1;
+      a.jobs[b] = jb;
+    }
+    for (int j = lane; j <= Kmax; j += 64) {
+      int v = -1;
+      if (ok && !bad && j < A) v = a.draft[drow0 + j];
+      a.emitted[(long)b * (Kmax + 1) + j] = v;  // position A is written by the sampler
+    }
+  }
+}
+
+__global__ __launch_bounds__(NT) void k_accept_greedy(const AcceptArgs a) {
+  extern __shared__ float sm[];
+  int *amax = reinterpret_cast<int *>(sm);  // [K+1]
+  const int b = blockIdx.x, K = a.K;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long trow0 = (long)b * (K + 1);
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  for (int j = wave; j <= K; j += NT / 64) {
+    const StatPart st = wave_merge_row(a.parts_t + (trow0 + j) * a.nslots_t, a.nslots_t, 1.f, a.diag != nullptr);
+    if (lane == 0) {
+      amax[j] = st.i1;
+      if (!isfinite(st.b1)) bad = SV_DEV_NONFINITE;
+      if (a.diag) {
+        float *dg = a.diag + (trow0 + j) * SV_DIAG_COLS;
+        dg[0] = st.b1 + __logf(st.s); dg[1] = (float)st.i1; dg[2] = st.b1 - st.b2; dg[3] = st.b1;
+        dg[4] = NAN; dg[5] = NAN; dg[6] = NAN; dg[7] = 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    bool ok = true, rej = false;
+    int A = 0;
+    for (int base = 0; base < K; base += 64) {
+      const int j = base + lane;
+      bool match = false;
+      if (j < K) {
+        const int x = a.draft[(long)b * K + j];
+        if (x < 0 || x >= a.V) ok = false;
+        match = (x == amax[j]);
+        if (a.diag && x >= 0 && x < a.V && a.logits_t) a.diag[(trow0 + j) * SV_DIAG_COLS + 4] = a.logits_t[(trow0 + j) * (long)a.V + x];
+      }
+      if (!rej) {
+        const unsigned long long live = (K - base >= 64) ? ~0ull : ((1ull << (K - base)) - 1ull);
+        const unsigned long long mis = __ballot(!match) & live;
+        if (mis) { A = base + __ffsll((long long)mis) - 1; rej = true; }
+        else A = min(K, base + 64);
+      }
+    }
+    const bool allok = !__any(!ok);
+    const bool good = allok && !bad;
+    if (lane == 0) {
+      if (!allok) set_status(a.dev_status, SV_DEV_BAD_TOKEN);
+      if (bad) set_status(a.dev_status, bad);
+      a.accepted_len[b] = good ? A : -1;
+    }
+    for (int j = lane; j <= K; j += 64) {
+      int v = -1;
+      if (good && j < A) v = a.draft[(long)b * K + j];
+      if (good && j == A) v = amax[A];
+      a.emitted[(long)b * (K + 1) + j] = v;
+    }
+  }
+}
+
+// ---- inverse-CDF sampling over V, split in chunks: pass 1 sums each chunk,
+// pass 2 locates the chunk and the token.  Weights are recomputed in both passes
+// from the fp32 logits, in ascending token order.
+__device__ __forceinline__ float job_weight(const SampleJob &jb, int v, float invT, bool resid) {
+  const float p = __expf(jb.z1[v] * invT - jb.lse1);
+  if (!resid) return p;
+  const float q = __expf(jb.z2[v] * invT - jb.lse2);
+  return fmaxf(p - q, 0.f);
+}
+
+__device__ float block_sum(float v, float *red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[w];
+  return t;
+}
+
+__global__ __launch_bounds__(NT) void k_sample_chunks(const SampleJob *jobs, int V, int chunk, float invT,
+                                                      float *sums) {
+  __shared__ float red[NT / 64];
+  const SampleJob jb = jobs[blockIdx.y];
+  const int c = blockIdx.x, C = gridDim.x;
+  const int v0 = c * chunk, v1 = min(V, v0 + chunk);
+  float sr = 0.f, sp = 0.f;
+  if (jb.out_index >= 0) {
+    for (int v = v0 + threadIdx.x; v < v1; v += NT) {
+      const float p = __expf(jb.z1[v] * invT - jb.lse1);
+      sp += p;
+      if (jb.z2) sr += fmaxf(p - __expf(jb.z2[v] * invT - jb.lse2), 0.f);
+    }
+  }
+  const float tr = block_sum(sr, red);
+  const float tp = block_sum(sp, red);
+  if (threadIdx.x == 0) {
+    sums[((long)blockIdx.y * C + c) * 2 + 0] = tr;
+    sums[((long)blockIdx.y * C + c) * 2 + 1] = tp;
+  }
+}
+
+__global__ __launch_bounds__(NT) void k_sample_pick(const SampleJob *jobs, int V, int chunk, int C, float invT,
+                                                    const float *sums, int32_t *out) {
+  __shared__ float red[NT / 64];
+  __shared__ float wsum[NT];
+  __shared__ int s_chunk;
+  __shared__ float s_base, s_target;
+  __shared__ int s_resid;
+  const SampleJob jb = jobs[blockIdx.x];
+  if (jb.out_index < 0) return;
+  const float *cs = sums + (long)blockIdx.x * C * 2;
+  if (threadIdx.x == 0) {
+    // totals in a fixed (ascending chunk) order
+    float tr = 0.f, tp = 0.f;
+    for (int c = 0; c < C; ++c) { tr += cs[2 * c]; tp += cs[2 * c + 1]; }
+    const int resid = (jb.z2 != nullptr && tr > 0.f) ? 1 : 0;
+    const float total = resid ? tr : tp;
+    const float target = jb.u * total;
+    float run = 0.f;
+    int pick = -1;
+    int last_nz = 0;
+    for (int c = 0; c < C; ++c) {
+      const float w = cs[2 * c + (resid ? 0 : 1)];
+      if (w > 0.f) last_nz = c;
+      if (pick < 0 && run + w > target) { pick = c; break; }
+      run += w;
+    }
+    if (pick < 0) {  // rounding put the target past the last chunk: take the last non-empty one
+      pick = last_nz;
+      run = 0.f;
+      for (int c = 0; c < pick; ++c) run += cs[2 * c + (resid ? 0 : 1)];
+    }
+    s_chunk = pick; s_base = run; s_target = target; s_resid = resid;
+  }
+  __syncthreads();
+  const int c = s_chunk;
+  const bool resid = s_resid != 0;
+  const int v0 = c * chunk, v1 = min(V, v0 + chunk);
+  // each thread owns a contiguous run of the chunk
+  const int per = (chunk + NT - 1) / NT;
+  const int a0 = v0 + threadIdx.x * per, a1 = min(v1, a0 + per);
+  float mine = 0.f;
+  for (int v = a0; v < a1; ++v) mine += job_weight(jb, v, invT, resid);
+  wsum[threadIdx.x] = mine;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float run = s_base;
+    int pick_t = -1, last_t = -1;
+    for (int t = 0; t < NT; ++t) {
+      if (wsum[t] > 0.f) last_t = t;
+      if (pick_t < 0 && run + wsum[t] > s_target) { pick_t = t; break; }
+      run += wsum[t];
+    }
+    if (pick_t < 0) pick_t = last_t;
+    if (pick_t < 0) pick_t = 0;
+    // rescan the picked thread's run sequentially
+    float r2 = s_base;
+    for (int t = 0; t < pick_t; ++t) r2 += wsum[t];
+    const int b0 = v0 + pick_t * per, b1 = min(v1, b0 + per);
+    int v_pick = -1, v_last = -1;
+    for (int v = b0; v < b1; ++v) {
+      const float w = job_weight(jb, v, invT, resid);
+      if (w > 0.f) v_last = v;
+      if (r2 + w > s_target) { v_pick = v; break; }
+      r2 += w;
+    }
+    if (v_pick < 0) v_pick = v_last >= 0 ? v_last : b0;
+    out[jb.out_index] = v_pick;
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_finalize(const int32_t *acc, const int32_t *vlen, int B, int K,
+                                                   float *tau, int64_t *counters) {
+  __shared__ long long red[4][16];
+  long long sa = 0, sd = 0, se = 0, nv = 0;
+  for (int b = threadIdx.x; b < B; b += blockDim.x) {
+    const int A = acc[b];
+    if (A < 0) continue;
+    sa += A;
+    sd += vlen ? vlen[b] : K;
+    se += A + 1;
+    nv += 1;
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    sa += __shfl_xor(sa, off);
+    sd += __shfl_xor(sd, off);
+    se += __shfl_xor(se, off);
+    nv += __shfl_xor(nv, off);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) { red[0][wave] = sa; red[1][wave] = sd; red[2][wave] = se; red[3][wave] = nv; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long ta = 0, td = 0, te = 0, valid = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) { ta += red[0][w]; td += red[1][w]; te += red[2][w]; valid += red[3][w]; }
+    *tau = valid ? (float)((double)te / (double)valid) : 0.f;
+    if (counters) { counters[0] = ta; counters[1] = td; counters[2] = te; }
+  }
+}
+
+// Confidence of each draft row: conf = max_v q(v) = 1 / sum_v exp((z_v - max z)/T).  One wave per row.
+__global__ __launch_bounds__(NT) void k_row_conf(const StatPart *parts, int nslots, int rows, float invT,
+                                                 float *conf, int32_t *dev_status, float *diag, long diag_row0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = blockIdx.x * (NT / 64) + wave;
+  if (r >= rows) return;
+  const StatPart st = wave_merge_row(parts + (long)r * nslots, nslots, invT, true);
+  if (lane == 0) {
+    conf[r] = 1.f / st.s;
+    if (!isfinite(st.b1) || !(st.s >= 1.f)) set_status(dev_status, SV_DEV_NONFINITE);
+    if (diag) {
+      float *dg = diag + (diag_row0 + r) * SV_DIAG_COLS;
+      dg[0] = st.b1 * invT + __logf(st.s); dg[1] = (float)st.i1; dg[2] = st.b1 - st.b2; dg[3] = st.b1;
+      dg[4] = NAN; dg[5] = NAN; dg[6] = 1.f / st.s; dg[7] = 0.f;
+    }
+  }
+}
+
+// ---- confidence schedule (single block).
+__global__ __launch_bounds__(1024) void k_schedule(const ScheduleArgs a) {
+  extern __shared__ int smi[];
+  const int B = a.B, Km = a.Kmax, n = B * Km;
+  int *keys = smi;          // [n]   key of eligible entries, -1 otherwise
+  int *hist = smi + n;      // [1025]
+  int *kb = hist + 1025;    // [B]
+  __shared__ int s_cut, s_take_at_cut, s_nelig;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  if (a.status_reset && tid == 0) *a.status_reset = 0;
+  __syncthreads();
+  for (int i = tid; i < 1025; i += nt) hist[i] = 0;
+  __syncthreads();
+  // 2. survival products per request (fp32, ascending k) and keys
+  for (int b = tid; b < B; b += nt) {
+    float s = 1.f;
+    int lead = 0;
+    bool alive = true;
+    for (int k = 0; k < Km; ++k) {
+      s *= a.conf[b * Km + k];
+      const bool el = alive && (s >= a.threshold);
+      alive = el;
+      keys[b * Km + k] = el ? (int)floorf(1024.f * s) : -1;
+      if (el) ++lead;
+    }
+    kb[b] = lead;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int tot = 0;
+    for (int b = 0; b < B; ++b) tot += kb[b];
+    s_nelig = tot;
+  }
+  __syncthreads();
+  const int R = a.budget - B;  // positions that may be added beyond the B target rows
+  if (s_nelig > R) {
+    for (int i = tid; i < n; i += nt)
+      if (keys[i] >= 0) atomicAdd(&hist[min(keys[i], 1024)], 1);
+    __syncthreads();
+    if (tid == 0) {
+      int above = 0, cut = 1024;
+      for (; cut >= 0; --cut) {
+        if (above + hist[cut] >= R) break;
+        above += hist[cut];
+      }
+      s_cut = cut;
+      s_take_at_cut = R - above;  // entries with key == cut to keep, in (b, k) order
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int left = s_take_at_cut;
+      for (int b = 0; b < B; ++b) {
+        int k = 0;
+        for (; k < Km; ++k) {
+          const int key = keys[b * Km + k];
+          if (key > s_cut) continue;
+          if (key == s_cut && left > 0) { --left; continue; }
+          break;
+        }
+        kb[b] = k;
+      }
+    }
+    __syncthreads();
+  }
+  // 3. offsets and the packed row map
+  if (tid == 0) {
+    int off = 0;
+    for (int b = 0; b < B; ++b) {
+      a.row_off[b] = off;
+      for (int j = 0; j <= kb[b]; ++j) a.row_map[off + j] = b * (Km + 1) + j;
+      off += kb[b] + 1;
+    }
+    a.row_off[B] = off;
+    *a.m_total = off;
+  }
+  for (int b = tid; b < B; b += nt) {
+    a.verify_len[b] = kb[b];
+    if (a.verify_len_out) a.verify_len_out[b] = kb[b];
+  }
+}
+
+__global__ void k_gather_rows(const uint16_t *src, uint16_t *dst, const int32_t *row_map, const int32_t *m_total,
+                              int d) {
+  const int r = blockIdx.x;
+  if (r >= *m_total) return;
+  const long s = (long)row_map[r] * d, t = (long)r * d;
+  for (int i = threadIdx.x * 8; i < d; i += blockDim.x * 8)
+    *reinterpret_cast<u32x4 *>(dst + t + i) = *reinterpret_cast<const u32x4 *>(src + s + i);
+}
+
+__global__ void k_scatter_f32(const float *packed, float *dst, const int32_t *row_map, const int32_t *m_total,
+                              int V) {
+  const int r = blockIdx.x;
+  if (r >= *m_total) return;
+  const long s = (long)r * V, t = (long)row_map[r] * V;
+  for (int i = threadIdx.x; i < V; i += blockDim.x) dst[t + i] = packed[s + i];
+}
+
+__global__ void k_scatter_u16(const uint16_t *packed, uint16_t *dst, const int32_t *row_map,
+                              const int32_t *m_total, int d) {
+  const int r = blockIdx.x;
+  if (r >= *m_total) return;
+  const long s = (long)r * d, t = (long)row_map[r] * d;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) dst[t + i] = packed[s + i];
+}
+
+// Propose mode: per draft row, argmax (T == 0) or a sampling job from q.
+__global__ __launch_bounds__(NT) void k_propose_finish(const StatPart *parts, int nslots, int rows, float invT,
+                                                       float T, const float *logits, int V, const float *coins,
+                                                       SampleJob *jobs, int32_t *draft_out, float *conf_out,
+                                                       int32_t *dev_status) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = blockIdx.x * (NT / 64) + wave;
+  if (r >= rows) return;
+  const bool samp = T > 0.f;
+  const StatPart st = wave_merge_row(parts + (long)r * nslots, nslots, samp ? invT : 1.f, samp);
+  if (lane != 0) return;
+  const float lse = st.b1 * invT + __logf(st.s);
+  const bool fin = isfinite(st.b1) && (!samp || isfinite(lse));
+  if (!fin) set_status(dev_status, SV_DEV_NONFINITE);
+  if (!samp) {
+    draft_out[r] = fin ? st.i1 : -1;
+    if (conf_out) conf_out[r] = 1.f;
+    return;
+  }
+  if (conf_out) conf_out[r] = 1.f / st.s;
+  SampleJob jb;
+  jb.z1 = logits + (long)r * V;
+  jb.z2 = nullptr;
+  jb.lse1 = lse;
+  jb.lse2 = 0.f;
+  jb.u = coins[r];
+  jb.out_index = fin ? r : -1;
+  jobs[r] = jb;
+  if (!fin) draft_out[r] = -1;
+}
+
+}  // namespace
+
+hipError_t launch_init(int32_t *zero_i32, size_t n_i32, int32_t *dev_status, hipStream_t st) {
+  const long n = (long)n_i32;
+  long blocks = (n + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(k_init, dim3((unsigned)blocks), dim3(256), 0, st, zero_i32, n, dev_status);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept_sample(const AcceptArgs &a, hipStream_t st) {
+  const size_t shm = sizeof(float) * (2 * a.K + 2);
+  hipLaunchKernelGGL(k_accept_sample, dim3(a.B), dim3(NT), shm, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept_greedy(const AcceptArgs &a, hipStream_t st) {
+  const size_t shm = sizeof(int) * (a.K + 2);
+  hipLaunchKernelGGL(k_accept_greedy, dim3(a.B), dim3(NT), shm, st, a);
+  return hipGetLastError();
+}
+
+int sample_chunks(int V) {
+  int c = (V + 2047) / 2048;
+  if (c > 256) c = 256;
+  if (c < 1) c = 1;
+  return c;
+}
+
+hipError_t launch_sample(const SampleJob *jobs, int njobs, int V, float invT, float *chunk_sums, int32_t *out,
+                         hipStream_t st) {
+  if (njobs <= 0) return hipSuccess;
+  const int C = sample_chunks(V);
+  const int chunk = (V + C - 1) / C;
+  hipLaunchKernelGGL(k_sample_chunks, dim3(C, njobs), dim3(NT), 0, st, jobs, V, chunk, invT, chunk_sums);
+  hipLaunchKernelGGL(k_sample_pick, dim3(njobs), dim3(NT), 0, st, jobs, V, chunk, C, invT,
+                     (const float *)chunk_sums, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const int32_t *accepted_len, const int32_t *verify_len, int B, int K, float *tau,
+                           int64_t *counters, hipStream_t st) {
+  hipLaunchKernelGGL(k_finalize, dim3(1), dim3(1024), 0, st, accepted_len, verify_len, B, K, tau, counters);
+  return hipGetLastError();
+}
+
+hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t st) {
+  const int rows = a.B * a.Kmax;
+  if (rows > 0)
+    hipLaunchKernelGGL(k_row_conf, dim3((rows + (NT / 64) - 1) / (NT / 64)), dim3(NT), 0, st, a.parts_d, a.nslots_d,
+                       rows, a.invT, a.conf, a.dev_status, a.diag, a.diag_row0);
+  const size_t shm = sizeof(int) * ((size_t)a.B * a.Kmax + 1025 + a.B);
+  hipLaunchKernelGGL(k_schedule, dim3(1), dim3(1024), shm, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const uint16_t *src, uint16_t *dst, const int32_t *row_map, const int32_t *m_total,
+                              int max_rows, int d, hipStream_t st) {
+  hipLaunchKernelGGL(k_gather_rows, dim3(max_rows), dim3(256), 0, st, src, dst, row_map, m_total, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_logits(const float *packed, float *dst, const int32_t *row_map, const int32_t *m_total,
+                                 int max_rows, int V, hipStream_t st) {
+  hipLaunchKernelGGL(k_scatter_f32, dim3(max_rows), dim3(256), 0, st, packed, dst, row_map, m_total, V);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_hidden(const uint16_t *packed, uint16_t *dst, const int32_t *row_map,
+                                 const int32_t *m_total, int max_rows, int d, hipStream_t st) {
+  hipLaunchKernelGGL(k_scatter_u16, dim3(max_rows), dim3(256), 0, st, packed, dst, row_map, m_total, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_propose_finish(const StatPart *parts, int nslots, int rows, float invT, float T,
+                                 const float *logits, int V, const float *coins, SampleJob *jobs, int32_t *draft_out,
+                                 float *conf_out, int32_t *dev_status, hipStream_t st) {
+  const int blocks = (rows + (NT / 64) - 1) / (NT / 64);
+  hipLaunchKernelGGL(k_propose_finish, dim3(blocks), dim3(NT), 0, st, parts, nslots, rows, invT, T, logits, V,
+                     coins, jobs, draft_out, conf_out, dev_status);
+  return hipGetLastError();
+}
+
+}  // namespace sv

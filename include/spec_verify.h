@@ -1,0 +1,167 @@
+/*
+ * spec_verify.h -- C ABI of libspecverify, the draft-block verification step of
+ * speculative decoding on AMD Instinct MI355X (gfx950).
+ *
+ * One call scores the K draft tokens of each of B requests plus a bonus position
+ * in a single pass over the weights of the target's final SwiGLU MLP and its LM
+ * head, then runs the acceptance rule over the full vocabulary.
+ *
+ * The operation (sources are cited by page title and section):
+ *  - "Speculative decoding in production: comparing methods in the Wildberries
+ *    shopping assistant", "Where speculative decoding came from": one target pass
+ *    scores every draft token; the longest correct prefix is accepted and the
+ *    target's own token is put at the first error.  "A bit of theory", Statement 1:
+ *    a draft token x is accepted with probability min(1, p(x)/q(x)), where p is the
+ *    target distribution after temperature and q the draft's; on rejection a token
+ *    is drawn from the normalised remainder max(0, p - q).
+ *  - "Let's start over, Misha: speculative decoding from draft to verification",
+ *    "How it works": when every draft token passes, the same pass yields one more
+ *    target token; "Why isn't the answer spoiled?": at temperature 0 the check
+ *    is an argmax comparison.
+ *  - "DSpark: speculative decoding with confidence-scheduled verification and
+ *    semi-autoregressive generation": each request's verify length is chosen from
+ *    the estimated survival probability of its draft prefix under the engine's
+ *    capacity.
+ *
+ * Model of the scored tail (one reading where the pages are silent): for every
+ * target row, a = bf16(silu(h W_gate^T) * (h W_up^T)), y = bf16(h + a W_down^T),
+ * target logits z = y W_lm^T; draft logits are h_draft W_lm^T with the same
+ * (shared) LM head.  With d_ff == 0 there is no MLP and y = h.
+ *
+ * Conventions for every entry point
+ *  - All array pointers are DEVICE pointers owned by the caller; the library never
+ *    allocates, frees or keeps them.  Weights and hidden rows must be 16-byte
+ *    aligned.  bf16 values are passed as their uint16_t bit patterns.  Arrays are
+ *    dense and row-major; weights are [out, in].
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *    work; outputs are valid once the stream has passed the call.  There is no
+ *    host synchronisation inside a call.  Concurrent calls are safe if they use
+ *    distinct workspaces and outputs.
+ *  - `ws` is caller-provided device scratch of at least sv_workspace_bytes(...)
+ *    bytes, 256-byte aligned.  Its contents on entry do not matter.
+ *  - Row order: request b, position j is row b*(K+1)+j of `h` ([B, K+1, d]) and
+ *    row b*K+j of `h_draft` / `draft` ([B, K, ...]).  Target row j scores draft
+ *    token j+1 (draft[b*K+j]); target row K is the bonus position.
+ *  - Coins `u` [B, K+1] are fp32 in [0, 1): u[b, j] (j < K) is the acceptance coin
+ *    of draft token j+1; u[b, K] is the single coin of the final (residual or
+ *    bonus) sample.  In scheduled mode K is Kmax and the final coin is u[b, Kmax].
+ *  - Return value: SV_OK, or a negative SV_E* code; nothing is enqueued when the
+ *    arguments are rejected.  Data errors only visible on the device (a draft id
+ *    outside [0, V), a non-finite row statistic) set *dev_status to the first
+ *    SV_DEV_* code seen and make that request's outputs -1.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_OK 0
+#define SV_EINVAL (-1)      /* bad sizes, NULL required pointer, misalignment, T <= 0, budget < B */
+#define SV_EWORKSPACE (-2)  /* ws_bytes smaller than sv_workspace_bytes() */
+#define SV_EHIP (-3)        /* a HIP launch or runtime call failed */
+
+#define SV_DEV_OK 0
+#define SV_DEV_BAD_TOKEN 1  /* a draft id outside [0, V) */
+#define SV_DEV_NONFINITE 2  /* a row statistic (max or log-sum-exp) is not finite */
+
+#define SV_MODE_GREEDY 0
+#define SV_MODE_SAMPLE 1
+#define SV_MODE_SCHEDULED 2
+#define SV_MODE_PROPOSE 3
+
+/* Per-row diagnostic record (floats), written when sv_outputs.diag != NULL:
+ * [0] log-sum-exp of z/T (greedy: T = 1)   [1] argmax (lowest index, as float)
+ * [2] top-1 minus top-2 logit (z units)    [3] max logit
+ * [4] logit of the row's draft token (NaN on bonus rows / when unused)
+ * [5] probability of that token: p(x) on target rows, q(x) on draft rows
+ * [6] acceptance ratio p(x)/q(x) (target rows), top-1 probability (draft rows)
+ * [7] reserved (0) */
+#define SV_DIAG_COLS 8
+
+typedef struct sv_weights {
+  const uint16_t *w_gate; /* [d_ff, d]; NULL iff d_ff == 0 */
+  const uint16_t *w_up;   /* [d_ff, d]; NULL iff d_ff == 0 */
+  const uint16_t *w_down; /* [d, d_ff]; NULL iff d_ff == 0 */
+  const uint16_t *w_lm;   /* [V, d] shared LM head */
+  int32_t d;              /* hidden size, multiple of 64 */
+  int32_t d_ff;           /* MLP width, multiple of 64, or 0 */
+  int32_t V;              /* vocabulary, 1 <= V < 2^24 */
+} sv_weights;
+
+typedef struct sv_outputs {
+  int32_t *accepted_len; /* [B] required: A_b, accepted draft tokens (-1 on a bad request) */
+  int32_t *emitted;      /* [B, K+1] required: first A_b+1 entries valid, the rest -1 */
+  int32_t *verify_len;   /* [B] scheduled mode: k_b drafts verified; may be NULL */
+  float *tau;            /* [1] required: mean over requests of A_b + 1 */
+  int64_t *counters;     /* [3] accepted drafts, verified drafts, emitted tokens; may be NULL */
+  int32_t *dev_status;   /* [1] SV_DEV_* code; may be NULL */
+  float *diag;           /* per-row SV_DIAG_COLS records; may be NULL.  Rows: target rows
+                            [B*(K+1)] then draft rows [B*K] (greedy: target rows only) */
+  float *logits;         /* fp32 logits, same row order as diag, [rows, V]; may be NULL.
+                            Scheduled mode writes only the verified target rows */
+  uint16_t *hidden;      /* bf16 MLP output y [B*(K+1), d]; may be NULL; written only when
+                            d_ff > 0 (scheduled mode: verified rows only) */
+  void *ev_lm_begin;     /* optional hipEvent_t pair recorded on `stream` right before and */
+  void *ev_lm_end;       /* after the dominant LM-head GEMM (scheduled mode: the draft-row
+                            pass); both NULL to skip.  For measurement only. */
+} sv_outputs;
+
+/* Bytes of device workspace a call with these sizes needs (0 on invalid sizes).
+ * mode: SV_MODE_*; K is Kmax in scheduled mode (the size covers any budget); in
+ * propose mode B is the number of draft rows and K is ignored. */
+size_t sv_workspace_bytes(int mode, int B, int K, const sv_weights *w);
+
+/* Greedy verification (temperature 0).  h: [B, K+1, d] bf16 target hidden rows;
+ * draft: [B, K] int32.  A_b is the first j with draft[b, j] != argmax of target row
+ * j (K if none); the emitted tokens are draft[b, 0..A_b-1] then the argmax of row
+ * A_b.  Ties in the argmax go to the lowest index.  The diag records use T = 1. */
+int spec_verify_greedy(const sv_weights *w, const uint16_t *h, const int32_t *draft, int B, int K,
+                       void *ws, size_t ws_bytes, sv_outputs *out, void *stream);
+
+/* Rejection-sampling verification at temperature T > 0.  h: [B, K+1, d];
+ * h_draft: [B, K, d] draft hidden rows scored by the same LM head; draft: [B, K];
+ * u: [B, K+1].  Draft token j+1 is accepted while u[b, j] < p_j(x)/q_j(x); at the
+ * first rejection the emitted token is drawn from max(0, p_j - q_j) (falling back to
+ * p_j if that is all zero) and when all K pass, from p_K, both by inverse CDF over
+ * ascending token ids with the coin u[b, K]. */
+int spec_verify_sample(const sv_weights *w, const uint16_t *h, const uint16_t *h_draft,
+                       const int32_t *draft, const float *u, float T, int B, int K, void *ws,
+                       size_t ws_bytes, sv_outputs *out, void *stream);
+
+/* Confidence-scheduled verification at temperature T > 0.  Shapes as in
+ * spec_verify_sample with K = Kmax.  The LM head first scores all B*Kmax draft rows;
+ * c[b, k] = max_v q_{b,k}(v), survival s_b(k) = prod_{i<=k} c[b, i].  Positions with
+ * s_b(k) >= survival_threshold are eligible; each request always verifies its own
+ * target row, and when B + #eligible > budget_rows only the budget_rows - B eligible
+ * positions with the largest floor(1024 * s) are kept (ties: lower request, then lower
+ * position).  Request b then runs the sampled rule on its first k_b drafts, with
+ * u[b, 0..k_b-1] and the final coin u[b, Kmax].  Requires budget_rows >= B and
+ * 0 < survival_threshold <= 1 and B*Kmax <= 8192.  verify_len (if given) receives k_b. */
+int spec_verify_scheduled(const sv_weights *w, const uint16_t *h, const uint16_t *h_draft,
+                          const int32_t *draft, const float *u, float T, float survival_threshold,
+                          int budget_rows, int B, int Kmax, void *ws, size_t ws_bytes,
+                          sv_outputs *out, void *stream);
+
+/* The drafter's step on the shared LM head (the call before verification in
+ * MTP/EAGLE-style drafting).  h_draft: [rows, d]; coins: [rows] (unused when T == 0).
+ * draft_out[r] = token drawn from q = softmax(h_draft[r] W_lm^T / T) by inverse CDF
+ * with coins[r], or the argmax when T == 0; conf_out[r] (may be NULL) = max_v q(v)
+ * (1 when T == 0). */
+int spec_draft_propose(const sv_weights *w, const uint16_t *h_draft, const float *coins, float T,
+                       int rows, void *ws, size_t ws_bytes, int32_t *draft_out, float *conf_out,
+                       void *stream);
+
+/* Library version string and a text for an SV_E* code. */
+const char *sv_version(void);
+const char *sv_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

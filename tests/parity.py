@@ -1,0 +1,92 @@
+"""Helpers shared by the GPU parity tests: moving seeded inputs to the device,
+computing the oracle's answer, and comparing decisions with the tolerance classes.
+
+Tolerances (fixed by the verification spec this library follows):
+* logits: max |gpu - oracle| <= 2e-2 (bf16 inputs, fp32 accumulation);
+* probabilities p(x), q(x): |gpu - oracle| <= 1e-4;
+* accepted lengths and tokens bit-exact, except where the first differing decision
+  is a near tie: |u - p/q| < 1e-4 for an acceptance, a top-1/top-2 logit gap below
+  1e-3 for an argmax, the final coin within 1e-4 of a boundary of the oracle's
+  normalised CDF, or a survival product within 1e-5 of the threshold or of a
+  1/1024 key boundary.  Such cases are counted and must stay below 0.1%.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from draft_block_verification_spec_amd import binding as bd
+
+LOGIT_TOL = 2e-2
+PROB_TOL = 1e-4
+RATIO_BAND = 1e-4
+GAP_BAND = 1e-3
+CDF_BAND = 1e-4
+SURV_BAND = 1e-5
+
+
+def dev_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def dev_weights(data: dict, device="cuda") -> bd.Weights:
+    g = data.get("w_gate")
+    return bd.Weights(dev_bf16(data["w_lm"], device),
+                      None if g is None else dev_bf16(g, device),
+                      None if g is None else dev_bf16(data["w_up"], device),
+                      None if g is None else dev_bf16(data["w_down"], device))
+
+
+def oracle_drafts(W: oracle.Weights, data: dict, T: float, rows=None) -> dict:
+    """Draft tokens drawn by the oracle's drafter (x ~ q at T, or argmax when T == 0)."""
+    hd = oracle.from_bf16_bits(data["h_draft"] if rows is None else data["h_draft"][rows])
+    coins = data["draft_coins"] if rows is None else data["draft_coins"][rows]
+    return oracle.propose(W, hd, T, coins)
+
+
+def first_diff_sample(ref: dict, A_g: int, em_g: np.ndarray, b: int, coins: np.ndarray, K_b: int) -> str | None:
+    """Classify the first decision where GPU and oracle differ for request b.
+    Returns None if it is an allowed near tie, else a description."""
+    A_o = int(ref["accepted"][b])
+    if A_g != A_o:
+        j = min(A_g, A_o)
+        r = float(ref["ratio"][b, j])
+        if abs(coins[b, j] - min(1.0, r)) < RATIO_BAND:
+            return None
+        return f"acceptance differs at position {j}: u={coins[b, j]:.6f} ratio={r:.6f} (gpu A={A_g}, oracle A={A_o})"
+    em_o = ref["emitted"][b]
+    if np.array_equal(em_o[: A_o + 1], em_g[: A_o + 1]):
+        return f"tail differs: {em_g} vs {em_o}"
+    u = coins[b, -1]
+    if min(abs(u - ref["cdf_lo"][b]), abs(u - ref["cdf_hi"][b])) < CDF_BAND:
+        return None
+    return f"final token differs: gpu {em_g[A_o]} oracle {em_o[A_o]} (u={u:.6f}, cdf [{ref['cdf_lo'][b]:.6f}, {ref['cdf_hi'][b]:.6f}])"
+
+
+def compare_requests(ref: dict, acc_g: np.ndarray, em_g: np.ndarray, classify) -> tuple[int, list]:
+    """Count mismatching requests; return (mismatches, unexplained descriptions)."""
+    bad = []
+    mism = 0
+    B = len(acc_g)
+    for b in range(B):
+        A_o = int(ref["accepted"][b])
+        same = int(acc_g[b]) == A_o and np.array_equal(em_g[b], ref["emitted"][b])
+        if same:
+            continue
+        mism += 1
+        why = classify(b)
+        if why is not None:
+            bad.append(f"request {b}: {why}")
+    return mism, bad
+
+
+def assert_decisions(ref, acc_g, em_g, classify, what=""):
+    mism, bad = compare_requests(ref, acc_g, em_g, classify)
+    B = len(acc_g)
+    assert not bad, f"{what}: {len(bad)} unexplained mismatches, e.g. {bad[:3]}"
+    if B >= 1000:
+        assert mism < 0.001 * B, f"{what}: {mism} near-tie mismatches out of {B}"
+    else:
+        assert mism <= 1, f"{what}: {mism} near-tie mismatches out of {B}"
+    return mism

@@ -1,0 +1,140 @@
+"""C-ABI checks that run without a GPU: the library loads, exports exactly what the
+header declares, sizes its workspace, and rejects bad arguments before touching the
+device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from draft_block_verification_spec_amd import binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:sv|spec)_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(b.LIB_PATH):
+        from draft_block_verification_spec_amd import build
+        build.build()
+    return b.load()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("spec_verify_greedy", "spec_verify_sample", "spec_verify_scheduled", "sv_workspace_bytes"):
+        assert n in names
+    assert set(names) == set(b.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in _declared():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(_declared()) <= exported
+    # nothing else of ours leaks out of the shared object
+    ours = {s for s in exported if s.startswith(("sv_", "spec_", "_ZN2sv"))}
+    assert ours == set(_declared())
+
+
+def test_version_and_strerror(lib):
+    assert b"gfx950" in lib.sv_version()
+    assert lib.sv_strerror(b.SV_EINVAL) == b"invalid argument"
+    assert lib.sv_strerror(b.SV_EWORKSPACE) == b"workspace too small"
+
+
+def _w(d=4096, d_ff=12288, V=151936, mlp=True):
+    z = 1 << 20
+    return b.SvWeights(z if mlp else None, 2 * z if mlp else None, 3 * z if mlp else None, 4 * z, d, d_ff if mlp else 0, V)
+
+
+def test_workspace_sizes(lib):
+    w = _w()
+    g = lib.sv_workspace_bytes(b.SV_MODE_GREEDY, 1, 15, ctypes.byref(w))
+    s = lib.sv_workspace_bytes(b.SV_MODE_SAMPLE, 1, 15, ctypes.byref(w))
+    sch = lib.sv_workspace_bytes(b.SV_MODE_SCHEDULED, 64, 15, ctypes.byref(w))
+    p = lib.sv_workspace_bytes(b.SV_MODE_PROPOSE, 15, 0, ctypes.byref(w))
+    assert 0 < g < s                       # sampled mode keeps fp32 logits of 31 rows
+    assert s >= 31 * 151936 * 4
+    assert sch >= 64 * 15 * 151936 * 4     # scheduled mode keeps every draft row's logits
+    assert p >= 15 * 151936 * 4
+    assert all(x % 256 == 0 for x in (g, s, sch, p))
+    # larger batches never need less
+    assert lib.sv_workspace_bytes(b.SV_MODE_GREEDY, 128, 7, ctypes.byref(w)) > g
+
+
+@pytest.mark.parametrize("bad", [
+    dict(d=100), dict(d=0), dict(d_ff=100), dict(V=0), dict(V=1 << 24), dict(mlp=False, d_ff=12288),
+])
+def test_workspace_rejects_bad_shapes(lib, bad):
+    kw = dict(d=4096, d_ff=12288, V=151936, mlp=True)
+    kw.update(bad)
+    if "mlp" in bad and not bad["mlp"]:
+        w = b.SvWeights(None, None, None, 1 << 20, kw["d"], kw["d_ff"], kw["V"])
+    else:
+        w = _w(kw["d"], kw["d_ff"], kw["V"], kw["mlp"])
+    assert lib.sv_workspace_bytes(b.SV_MODE_SAMPLE, 1, 4, ctypes.byref(w)) == 0
+    assert lib.sv_workspace_bytes(7, 1, 4, ctypes.byref(_w())) == 0
+    assert lib.sv_workspace_bytes(b.SV_MODE_SAMPLE, 0, 4, ctypes.byref(_w())) == 0
+
+
+def _outs():
+    z = 1 << 24
+    return b.SvOutputs(z, z + 4096, None, z + 8192, None, None, None, None, None)
+
+
+def test_entry_points_reject_invalid_arguments(lib):
+    w, o = _w(), _outs()
+    P = 1 << 28
+    ws, wsn = 1 << 30, 1 << 40
+    # NULL hidden states / outputs / weights
+    assert lib.spec_verify_greedy(ctypes.byref(w), None, P, 1, 4, ws, wsn, ctypes.byref(o), None) == b.SV_EINVAL
+    assert lib.spec_verify_greedy(None, P, P, 1, 4, ws, wsn, ctypes.byref(o), None) == b.SV_EINVAL
+    assert lib.spec_verify_greedy(ctypes.byref(w), P, P, 1, 4, ws, wsn, None, None) == b.SV_EINVAL
+    assert lib.spec_verify_greedy(ctypes.byref(w), P, None, 1, 4, ws, wsn, ctypes.byref(o), None) == b.SV_EINVAL
+    # misaligned hidden pointer, bad batch
+    assert lib.spec_verify_greedy(ctypes.byref(w), P + 2, P, 1, 4, ws, wsn, ctypes.byref(o), None) == b.SV_EINVAL
+    assert lib.spec_verify_greedy(ctypes.byref(w), P, P, 0, 4, ws, wsn, ctypes.byref(o), None) == b.SV_EINVAL
+    assert lib.spec_verify_greedy(ctypes.byref(w), P, P, 1, -1, ws, wsn, ctypes.byref(o), None) == b.SV_EINVAL
+    # temperature must be positive and finite in sampled mode
+    for T in (0.0, -1.0, float("inf"), float("nan")):
+        assert lib.spec_verify_sample(ctypes.byref(w), P, P, P, P, T, 1, 4, ws, wsn, ctypes.byref(o), None) == b.SV_EINVAL
+    assert lib.spec_verify_sample(ctypes.byref(w), P, P, P, None, 1.0, 1, 4, ws, wsn, ctypes.byref(o), None) == b.SV_EINVAL
+    assert lib.spec_verify_sample(ctypes.byref(w), P, None, P, P, 1.0, 1, 4, ws, wsn, ctypes.byref(o), None) == b.SV_EINVAL
+    # scheduled: budget below B, threshold outside (0, 1]
+    assert lib.spec_verify_scheduled(ctypes.byref(w), P, P, P, P, 1.0, 0.3, 3, 4, 15, ws, wsn, ctypes.byref(o),
+                                     None) == b.SV_EINVAL
+    for thr in (0.0, 1.5, float("nan")):
+        assert lib.spec_verify_scheduled(ctypes.byref(w), P, P, P, P, 1.0, thr, 64, 4, 15, ws, wsn, ctypes.byref(o),
+                                         None) == b.SV_EINVAL
+    # required outputs
+    o2 = b.SvOutputs(None, 1 << 24, None, 1 << 24, None, None, None, None, None)
+    assert lib.spec_verify_greedy(ctypes.byref(w), P, P, 1, 4, ws, wsn, ctypes.byref(o2), None) == b.SV_EINVAL
+    # propose
+    assert lib.spec_draft_propose(ctypes.byref(w), P, None, 1.0, 4, ws, wsn, P, None, None) == b.SV_EINVAL
+    assert lib.spec_draft_propose(ctypes.byref(w), P, P, -1.0, 4, ws, wsn, P, None, None) == b.SV_EINVAL
+    assert lib.spec_draft_propose(ctypes.byref(w), P, P, 1.0, 0, ws, wsn, P, None, None) == b.SV_EINVAL
+
+
+def test_entry_points_reject_small_workspace(lib):
+    w, o = _w(), _outs()
+    P = 1 << 28
+    need = lib.sv_workspace_bytes(b.SV_MODE_SAMPLE, 1, 15, ctypes.byref(w))
+    assert lib.spec_verify_sample(ctypes.byref(w), P, P, P, P, 1.0, 1, 15, 1 << 30, need - 256, ctypes.byref(o),
+                                  None) == b.SV_EWORKSPACE
+    need = lib.sv_workspace_bytes(b.SV_MODE_GREEDY, 2, 7, ctypes.byref(w))
+    assert lib.spec_verify_greedy(ctypes.byref(w), P, P, 2, 7, 1 << 30, need - 1, ctypes.byref(o), None) == b.SV_EWORKSPACE
+    need = lib.sv_workspace_bytes(b.SV_MODE_PROPOSE, 15, 0, ctypes.byref(w))
+    assert lib.spec_draft_propose(ctypes.byref(w), P, P, 1.0, 15, 1 << 30, need - 1, P, None, None) == b.SV_EWORKSPACE
+    # misaligned workspace
+    assert lib.spec_verify_greedy(ctypes.byref(w), P, P, 2, 7, (1 << 30) + 16, 1 << 40, ctypes.byref(o),
+                                  None) == b.SV_EINVAL
