@@ -24,7 +24,7 @@ SV_MODE_GREEDY, SV_MODE_SAMPLE, SV_MODE_SCHEDULED, SV_MODE_PROPOSE = 0, 1, 2, 3
 SV_DIAG_COLS = 8
 
 EXPORTS = ("sv_workspace_bytes", "spec_verify_greedy", "spec_verify_sample", "spec_verify_scheduled",
-           "spec_draft_propose", "sv_version", "sv_strerror")
+           "spec_draft_propose", "sv_version", "sv_strerror", "sv_last_hip_error")
 
 
 class SpecVerifyError(RuntimeError):
@@ -72,6 +72,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sv_version.restype = ctypes.c_char_p
     lib.sv_strerror.restype = ctypes.c_char_p
     lib.sv_strerror.argtypes = [i32]
+    lib.sv_last_hip_error.restype = ctypes.c_char_p
     if path is None:
         _lib = lib
     return lib
@@ -181,6 +182,8 @@ def _stream(stream) -> int | None:
 def _raise(rc: int, what: str):
     if rc != SV_OK:
         msg = load().sv_strerror(rc).decode()
+        if rc == SV_EHIP:
+            msg += ": " + load().sv_last_hip_error().decode()
         raise SpecVerifyError(f"{what} failed: {msg} ({rc})")
 
 

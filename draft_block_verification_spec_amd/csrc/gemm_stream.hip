@@ -28,13 +28,27 @@ constexpr int STEPS = 16;     // MFMA k-steps (32 values) per wave per chunk
 constexpr int WAVES = 8;
 constexpr int CHUNK_KS = STEPS * WAVES;  // k-steps per chunk (4096 values)
 
-template <int MB, int EPI>
+// KM (K mode): 1 = K is one 4096-value chunk, 2 = K is several whole chunks, 0 = any
+// other K.  With whole chunks (FULL) every wave owns exactly STEPS
+// k-steps of every chunk and the hot loop has no data-dependent control flow:
+// every load is issued unconditionally from a valid (clamped) address, which lets
+// the compiler keep the 16 loads of a step in flight with partial vmcnt waits.
+// Rows beyond M read a clamped row and their results are dropped; weight rows
+// beyond N likewise.  The general path masks the tail of K with zero operands.
+template <int MB, int EPI, int KM>
 __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
+  constexpr bool FULL = KM != 0;
+  constexpr bool RELOAD_A = KM != 1;  // activations change with the chunk
   constexpr bool PAIR = (EPI == EPI_SWIGLU);
   constexpr int NACC = PAIR ? 2 * MB : MB;
   __shared__ float red[2][WAVES * NACC * 4 * 64];
+  // Outputs of the workgroup's whole column range are kept in LDS and written once at
+  // the end (when a.buf_cols > 0): stores inside the streaming loop would share the
+  // vector-memory counter with the weight loads and stall them.
+  extern __shared__ float obuf[];
 
   if (a.status_reset && blockIdx.x == 0 && threadIdx.x == 0) *a.status_reset = 0;
+  if (a.counter_reset && blockIdx.x == 0 && threadIdx.x == 0) *a.counter_reset = 0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int M = a.M_dev ? min(a.M, *a.M_dev) : a.M;
   const int N = a.N;
@@ -49,6 +63,7 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
   const long K = a.K;
 
   auto xrow = [&](int m) -> const uint16_t * {
+    m = min(m, max(M, 1) - 1);
     return m < a.m1 ? a.x1 + (long)m * a.ldx1 : a.x2 + (long)(m - a.m1) * a.ldx2;
   };
 
@@ -57,18 +72,21 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
   bf16x8 Ur[PAIR ? STEPS : 1];
   const bf16x8 zero8 = {};
 
+  auto kstep = [&](int chunk, int s) { return chunk * CHUNK_KS + wave * STEPS + s; };
   auto load_a = [&](int chunk, int s, int mb) -> bf16x8 {
-    const int ks = chunk * CHUNK_KS + wave * STEPS + s;
-    const int m = mb * 16 + r16;
-    if (ks < nks && m < M) return as_bf16x8(ld16(xrow(m) + ks * 32 + kq));
-    return zero8;
+    const int ks = kstep(chunk, s);
+    if constexpr (FULL) {
+      return as_bf16x8(ld16(xrow(mb * 16 + r16) + ks * 32 + kq));
+    } else {
+      if (ks < nks) return as_bf16x8(ld16(xrow(mb * 16 + r16) + ks * 32 + kq));
+      return zero8;
+    }
   };
   auto wptr = [&](const uint16_t *base, int tile, int chunk, int s) -> const uint16_t * {
-    const int ks = chunk * CHUNK_KS + wave * STEPS + s;
+    const int ks = min(kstep(chunk, s), nks - 1);
     const int n = min(tile * 16 + r16, N - 1);
     return base + (long)n * K + ks * 32 + kq;
   };
-  auto kvalid = [&](int chunk, int s) { return chunk * CHUNK_KS + wave * STEPS + s < nks; };
 
   // statistics of the row this thread reduces (EPI_LOGITS)
   StatPart st = stat_empty();
@@ -85,9 +103,8 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
       for (int mb = 0; mb < MB; ++mb) A[mb][s] = load_a(0, s, mb);
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
-      const bool kv = kvalid(0, s);
-      Wr[s] = kv ? as_bf16x8(ld_nt(wptr(a.w, t_begin, 0, s))) : zero8;
-      if constexpr (PAIR) Ur[s] = kv ? as_bf16x8(ld_nt(wptr(a.w2, t_begin, 0, s))) : zero8;
+      Wr[s] = as_bf16x8(ld16(wptr(a.w, t_begin, 0, s)));
+      if constexpr (PAIR) Ur[s] = as_bf16x8(ld16(wptr(a.w2, t_begin, 0, s)));
     }
   }
 
@@ -95,8 +112,8 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
   int parity = 0;
   for (int stp = 0; stp < nsteps; ++stp) {
     const int tile = t_begin + stp / nch, c = stp % nch;
-    const int nstp = stp + 1;
-    const bool has_next = nstp < nsteps;
+    // the last step re-loads its own operands: harmless, and keeps the loop free of branches
+    const int nstp = min(stp + 1, nsteps - 1);
     const int ntile = t_begin + nstp / nch, nc = nstp % nch;
     if (c == 0) {
 #pragma unroll
@@ -114,15 +131,14 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
           acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][s], Wr[s], acc[mb], 0, 0, 0);
         }
       }
-      if (has_next) {
-        const bool kv = kvalid(nc, s);
-        Wr[s] = kv ? as_bf16x8(ld_nt(wptr(a.w, ntile, nc, s))) : zero8;
-        if constexpr (PAIR) Ur[s] = kv ? as_bf16x8(ld_nt(wptr(a.w2, ntile, nc, s))) : zero8;
-        if (nch > 1) {
+      Wr[s] = as_bf16x8(ld16(wptr(a.w, ntile, nc, s)));
+      if constexpr (PAIR) Ur[s] = as_bf16x8(ld16(wptr(a.w2, ntile, nc, s)));
+      if constexpr (RELOAD_A) {
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) A[mb][s] = load_a(nc, s, mb);
-        }
+        for (int mb = 0; mb < MB; ++mb) A[mb][s] = load_a(nc, s, mb);
       }
+      // keep "use slot s, refill slot s" in program order so loads stay spread over the step
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (c != nch - 1) continue;
 
@@ -144,15 +160,24 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
         if constexpr (PAIR) v1 += rb[((w * NACC + q0 + 1) * 4 + e_r) * 64 + e_ln];
       }
       if (m < M && n < N) {
+        const int bc = n - t_begin * 16;  // column within the workgroup's range
         if constexpr (EPI == EPI_LOGITS) {
-          if (a.logits) a.logits[(long)m * a.ldl + n] = v0;
+          if (a.logits) {
+            if (a.buf_cols) obuf[m * a.buf_cols + bc] = v0;
+            else a.logits[(long)m * a.ldl + n] = v0;
+          }
           stat_push(st, v0, n, a.invT, a.want_s != 0);
-        } else if constexpr (EPI == EPI_SWIGLU) {
-          const float sg = v0 / (1.f + __expf(-v0));
-          a.out[(long)m * a.ldo + n] = f32_to_bf16(sg * v1);
-        } else if constexpr (EPI == EPI_RESID) {
-          const float hv = bf16_to_f32(a.resid[(long)m * a.ldr + n]);
-          a.out[(long)m * a.ldo + n] = f32_to_bf16(hv + v0);
+        } else {
+          uint16_t o;
+          if constexpr (EPI == EPI_SWIGLU) {
+            const float sg = v0 / (1.f + __expf(-v0));
+            o = f32_to_bf16(sg * v1);
+          } else {
+            const float hv = bf16_to_f32(a.resid[(long)m * a.ldr + n]);
+            o = f32_to_bf16(hv + v0);
+          }
+          if (a.buf_cols) reinterpret_cast<uint16_t *>(obuf)[m * a.buf_cols + bc] = o;
+          else a.out[(long)m * a.ldo + n] = o;
         }
       }
     }
@@ -169,6 +194,18 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
     }
     if (has_elem && e_n16 == 0 && e_m < M) a.parts[(long)e_m * a.nslots + g] = st;
   }
+  // flush the buffered outputs: each row's column range is contiguous in memory
+  if (a.buf_cols && nsteps > 0 && (EPI != EPI_LOGITS || a.logits)) {
+    __syncthreads();
+    const int cols = min(N, t_end * 16) - t_begin * 16;
+    const int n0 = t_begin * 16;
+    const int rows = min(M, MB * 16);
+    for (int idx = threadIdx.x; idx < rows * cols; idx += blockDim.x) {
+      const int m = idx / cols, c = idx % cols;
+      if constexpr (EPI == EPI_LOGITS) a.logits[(long)m * a.ldl + n0 + c] = obuf[m * a.buf_cols + c];
+      else a.out[(long)m * a.ldo + n0 + c] = reinterpret_cast<const uint16_t *>(obuf)[m * a.buf_cols + c];
+    }
+  }
 }
 
 }  // namespace
@@ -181,25 +218,51 @@ int stream_grid(const GemmArgs &a, int epi) {
   return ntiles < num_cus() ? ntiles : num_cus();
 }
 
-hipError_t launch_gemm_stream(const GemmArgs &a, int epi, int grid, hipStream_t st) {
+// Output buffer per workgroup: up to 32 rows x its column range (fp32 logits or bf16).
+constexpr size_t OBUF_MAX = 96 * 1024;
+
+template <int MB, int EPI, int KM>
+hipError_t launch_one(GemmArgs a, int grid, hipStream_t st) {
+  const int ntiles = (a.N + 15) / 16;
+  const int cols = 16 * ((ntiles + grid - 1) / grid);
+  const size_t esz = EPI == EPI_LOGITS ? 4 : 2;
+  size_t shm = (size_t)MB * 16 * cols * esz;
+  a.buf_cols = 0;
+  if (shm <= OBUF_MAX && (EPI != EPI_LOGITS || a.logits)) {
+    a.buf_cols = cols;
+    static bool attr_set = false;  // one instantiation per (MB, EPI, KM)
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_stream<MB, EPI, KM>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)OBUF_MAX);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+  } else {
+    shm = 0;
+  }
+  hipLaunchKernelGGL((k_stream<MB, EPI, KM>), dim3(grid), dim3(512), shm, st, a);
+  return hipGetLastError();
+}
+
+template <int KM>
+hipError_t launch_stream_t(const GemmArgs &a, int epi, int grid, hipStream_t st) {
   const bool two = a.M > 16;
-  dim3 blk(512), grd(grid);
   switch (epi) {
     case EPI_LOGITS:
-      if (two) hipLaunchKernelGGL((k_stream<2, EPI_LOGITS>), grd, blk, 0, st, a);
-      else hipLaunchKernelGGL((k_stream<1, EPI_LOGITS>), grd, blk, 0, st, a);
-      break;
+      return two ? launch_one<2, EPI_LOGITS, KM>(a, grid, st) : launch_one<1, EPI_LOGITS, KM>(a, grid, st);
     case EPI_SWIGLU:
-      hipLaunchKernelGGL((k_stream<1, EPI_SWIGLU>), grd, blk, 0, st, a);
-      break;
+      return launch_one<1, EPI_SWIGLU, KM>(a, grid, st);
     case EPI_RESID:
-      if (two) hipLaunchKernelGGL((k_stream<2, EPI_RESID>), grd, blk, 0, st, a);
-      else hipLaunchKernelGGL((k_stream<1, EPI_RESID>), grd, blk, 0, st, a);
-      break;
+      return two ? launch_one<2, EPI_RESID, KM>(a, grid, st) : launch_one<1, EPI_RESID, KM>(a, grid, st);
     default:
       return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+}
+
+hipError_t launch_gemm_stream(const GemmArgs &a, int epi, int grid, hipStream_t st) {
+  if (a.K == CHUNK_KS * 32) return launch_stream_t<1>(a, epi, grid, st);
+  if (a.K % (CHUNK_KS * 32) == 0) return launch_stream_t<2>(a, epi, grid, st);
+  return launch_stream_t<0>(a, epi, grid, st);
 }
 
 }  // namespace sv

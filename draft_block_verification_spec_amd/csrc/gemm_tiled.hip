@@ -20,15 +20,18 @@ constexpr int LDK = BK + 8;
 
 // PAIR: the weight rows of a tile are [32 gate | 32 up] groups of the same outputs.
 template <int BM, int BN, int EPI, bool PAIR>
-__global__ __launch_bounds__(256) void k_tiled(const GemmArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_tiled(const GemmArgs a) {
   constexpr int WTM = BM / 2, WTN = BN / 2, TM = WTM / 32, TN = WTN / 32;
   constexpr int ACH = BM * 8 / 256, BCH = BN * 8 / 256;
   static_assert(ACH >= 1 && BCH >= 1, "tile too small");
   static_assert(!PAIR || (WTN % 64) == 0, "paired tiles need gate/up block pairs");
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDK];
+  // operand tiles, double-buffered; reused by the statistics epilogue after the main loop
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDK];
+  uint16_t(*As)[BM * LDK] = reinterpret_cast<uint16_t(*)[BM * LDK]>(smem);
+  uint16_t(*Bs)[BN * LDK] = reinterpret_cast<uint16_t(*)[BN * LDK]>(smem + 2 * BM * LDK);
 
   if (a.status_reset && blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0) *a.status_reset = 0;
+  if (a.counter_reset && blockIdx.x == 0 && threadIdx.x == 0) *a.counter_reset = 0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   int M = a.M;
@@ -49,38 +52,37 @@ __global__ __launch_bounds__(256) void k_tiled(const GemmArgs a) {
   const int kt1 = min(nkt_total, kt0 + per);
   const int nkt = kt1 > kt0 ? kt1 - kt0 : 0;
 
-  // ---- global -> register staging
+  // ---- global -> register staging.  Rows past M (or N) read a clamped valid row;
+  // their results are never stored, and the loads stay free of branches.
   const uint16_t *arow[ACH];
   const uint16_t *brow[BCH];
+  const int mlast = max(M, 1) - 1;
 #pragma unroll
   for (int i = 0; i < ACH; ++i) {
     const int q = tid + i * 256, r = q >> 3;
-    const int m = m0 + r;
-    arow[i] = nullptr;
-    if (m < M) arow[i] = (m < a.m1 ? a.x1 + (long)m * a.ldx1 : a.x2 + (long)(m - a.m1) * a.ldx2) + (q & 7) * 8;
+    const int m = min(m0 + r, mlast);
+    arow[i] = (m < a.m1 ? a.x1 + (long)m * a.ldx1 : a.x2 + (long)(m - a.m1) * a.ldx2) + (q & 7) * 8;
   }
 #pragma unroll
   for (int i = 0; i < BCH; ++i) {
     const int q = tid + i * 256, r = q >> 3;
-    brow[i] = nullptr;
     if constexpr (PAIR) {
       // tile columns: 64-wide groups of [32 gate rows | 32 up rows] of the same outputs
       const int p = r >> 6, half = (r >> 5) & 1, rr = r & 31;
-      const int n = (n0 >> 1) + p * 32 + rr;
-      if (n < a.N) brow[i] = (half ? a.w2 : a.w) + (long)n * a.K + (q & 7) * 8;
+      const int n = min((n0 >> 1) + p * 32 + rr, a.N - 1);
+      brow[i] = (half ? a.w2 : a.w) + (long)n * a.K + (q & 7) * 8;
     } else {
-      const int n = n0 + r;
-      if (n < a.N) brow[i] = a.w + (long)n * a.K + (q & 7) * 8;
+      const int n = min(n0 + r, a.N - 1);
+      brow[i] = a.w + (long)n * a.K + (q & 7) * 8;
     }
   }
   u32x4 ra[ACH], rb[BCH];
-  const u32x4 z4 = {0u, 0u, 0u, 0u};
   auto gload = [&](int kt) {
     const long ko = (long)kt * BK;
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) ra[i] = arow[i] ? ld16(arow[i] + ko) : z4;
+    for (int i = 0; i < ACH; ++i) ra[i] = ld16(arow[i] + ko);
 #pragma unroll
-    for (int i = 0; i < BCH; ++i) rb[i] = brow[i] ? ld_nt(brow[i] + ko) : z4;
+    for (int i = 0; i < BCH; ++i) rb[i] = ld_nt(brow[i] + ko);
   };
   auto sstore = [&](int buf) {
 #pragma unroll
@@ -112,20 +114,30 @@ __global__ __launch_bounds__(256) void k_tiled(const GemmArgs a) {
   for (int t = 0; t < nkt; ++t) {
     const int buf = t & 1;
     if (t + 1 < nkt) gload(kt0 + t + 1);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[TM], bfr[TN];
+    // operand fragments are double-buffered in registers: the LDS reads of step
+    // kk+1 are issued before the MFMAs of step kk
+    bf16x8 af[2][TM], bfr[2][TN];
+    auto lfrag = [&](int set, int kk) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8 *>(&As[buf][(wm * WTM + i * 32 + l32) * LDK + kk * 16 + khalf]);
+        af[set][i] = *reinterpret_cast<const bf16x8 *>(&As[buf][(wm * WTM + i * 32 + l32) * LDK + kk * 16 + khalf]);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8 *>(&Bs[buf][(wn * WTN + j * 32 + l32) * LDK + kk * 16 + khalf]);
+        bfr[set][j] = *reinterpret_cast<const bf16x8 *>(&Bs[buf][(wn * WTN + j * 32 + l32) * LDK + kk * 16 + khalf]);
+    };
+    lfrag(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < BK / 16) lfrag(cur ^ 1, kk + 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (t + 1 < nkt) sstore(buf ^ 1);
     __syncthreads();
@@ -182,30 +194,42 @@ __global__ __launch_bounds__(256) void k_tiled(const GemmArgs a) {
         }
       }
   } else {  // EPI_LOGITS
+    // Logits go out straight from the accumulators (32 consecutive columns per
+    // register).  For the row statistics each wave stages one 32-row group of its
+    // tile in LDS at a time (row stride padded to 65 floats), then lane l scans row
+    // l%32 over half l/32 of the wave's columns in increasing order and the two
+    // halves are merged with one shuffle.
     const bool ws = a.want_s != 0;
     const int slot = tni * 2 + wn;
+    constexpr int SROW = WTN + 1;
+    static_assert(4 * 32 * SROW * 4 <= 2 * (BM + BN) * LDK * 2, "staging area too small");
+    __syncthreads();
+    float *stage = reinterpret_cast<float *>(smem) + wave * (32 * SROW);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
-        StatPart st = stat_empty();
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn * WTN + j * 32 + l32;
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int n = n0 + wn * WTN + j * 32 + l32;
-          if (n < a.N && m < M) {
-            const float v = acc[i][j][r];
-            if (a.logits) a.logits[(long)m * a.ldl + n] = v;
-            stat_push(st, v, n, a.invT, ws);
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int rr = (r >> 2) * 8 + rsub + (r & 3);
+          const int m = m0 + wm * WTM + i * 32 + rr;
+          stage[rr * SROW + j * 32 + l32] = acc[i][j][r];
+          if (a.logits && m < M && n < a.N) a.logits[(long)m * a.ldl + n] = acc[i][j][r];
         }
-#pragma unroll
-        for (int off = 1; off < 32; off <<= 1) {
-          StatPart o = stat_shfl_xor(st, off);
-          st = stat_merge(st, o, a.invT, ws);
-        }
-        if (l32 == 0 && m < M) a.parts[(long)m * a.nslots + slot] = st;
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are done
+      const int rr = l32, half = lane >> 5;
+      const int m = m0 + wm * WTM + i * 32 + rr;
+      StatPart st = stat_empty();
+      const int c0 = half * (WTN / 2);
+      for (int c = 0; c < WTN / 2; ++c) {
+        const int n = n0 + wn * WTN + c0 + c;
+        if (n < a.N) stat_push(st, stage[rr * SROW + c0 + c], n, a.invT, ws);
+      }
+      st = stat_merge(st, stat_shfl_xor(st, 32), a.invT, ws);
+      if (half == 0 && m < M) a.parts[(long)m * a.nslots + slot] = st;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next group
     }
   }
 }
@@ -264,6 +288,7 @@ hipError_t launch_bm_bn(const GemmArgs &a, int epi, int splits, hipStream_t st) 
 int tiled_slots(int N, int bn) { return ((N + bn - 1) / bn) * 2; }
 
 hipError_t launch_gemm_tiled(const GemmArgs &a, int epi, int bm, int bn, int splits, hipStream_t st) {
+  if (bn == 256 && bm == 256) return launch_bm_bn<256, 256>(a, epi, splits, st);
   if (bn != 128) return hipErrorInvalidValue;
   switch (bm) {
     case 64: return launch_bm_bn<64, 128>(a, epi, splits, st);

@@ -50,6 +50,7 @@ Gemm choose(int M, int N, int K, int epi) {
   }
   g.stream = false;
   g.bm = M <= 64 ? 64 : (M <= 128 ? 128 : 256);
+  g.bn = M > 256 ? 256 : 128;
   const int Ncols = epi == EPI_SWIGLU ? 2 * N : N;
   const long tiles = (long)((M + g.bm - 1) / g.bm) * ((Ncols + g.bn - 1) / g.bn);
   if (epi != EPI_LOGITS && tiles < 2L * num_cus()) {
@@ -70,13 +71,13 @@ struct Plan {
   Gemm gu, dn, lm, s1;
   size_t o_a = 0, o_y = 0, o_part = 0, o_parts = 0, o_parts_d = 0, o_logits = 0, o_logits_d = 0,
          o_jobs = 0, o_sums = 0, o_conf = 0, o_vlen = 0, o_rowoff = 0, o_rowmap = 0, o_mtot = 0,
-         o_hp = 0, total = 0;
+         o_hp = 0, o_sync = 0, total = 0;
 };
 
 bool valid_weights(const sv_weights *w) {
   if (!w || !w->w_lm) return false;
   if (w->d <= 0 || (w->d % 64) != 0) return false;
-  if (w->V < 1 || w->V >= (1 << 24)) return false;
+  if (w->V < 1 || w->V > (1 << 19)) return false;  // sampling keeps at most 256 chunks of 2048 tokens
   if (w->d_ff < 0 || (w->d_ff % 64) != 0) return false;
   const bool has = w->d_ff > 0;
   if (has != (w->w_gate != nullptr) || has != (w->w_up != nullptr) || has != (w->w_down != nullptr)) return false;
@@ -97,6 +98,7 @@ bool make_plan(int mode, int B, int K, const sv_weights *w, int budget, Plan &p)
     p.o_logits = take(sizeof(float) * (size_t)B * V);
     p.o_jobs = take(sizeof(SampleJob) * (size_t)B);
     p.o_sums = take(sizeof(float) * 2 * (size_t)B * sample_chunks(V));
+    p.o_sync = take(sizeof(int32_t) * (size_t)(B + 1));
     p.total = off;
     return true;
   }
@@ -131,6 +133,7 @@ bool make_plan(int mode, int B, int K, const sv_weights *w, int budget, Plan &p)
     p.o_jobs = take(sizeof(SampleJob) * (size_t)B);
     p.o_sums = take(sizeof(float) * 2 * (size_t)B * sample_chunks(V));
   }
+  p.o_sync = take(sizeof(int32_t) * (size_t)(B + 1));  // [0] call-wide arrivals, [1 + b] per request
   if (mode == SV_MODE_SCHEDULED) {
     p.s1 = choose(p.rows_d > 0 ? p.rows_d : 1, V, d, EPI_LOGITS);
     p.o_parts_d = take(sizeof(StatPart) * (size_t)(p.rows_d > 0 ? p.rows_d : 1) * p.s1.nslots);
@@ -151,12 +154,16 @@ bool aligned16(const void *q) { return ((uintptr_t)q & 15u) == 0; }
 template <typename T>
 T *at(void *ws, size_t off) { return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off); }
 
-#define SV_CHECK(expr)                       \
-  do {                                      \
-    if ((expr) != hipSuccess) {             \
-      (void)hipGetLastError();              \
-      return SV_EHIP;                       \
-    }                                       \
+thread_local const char *g_last_hip_error = "no error";
+
+#define SV_CHECK(expr)                                  \
+  do {                                                  \
+    const hipError_t e_ = (expr);                       \
+    if (e_ != hipSuccess) {                             \
+      g_last_hip_error = hipGetErrorString(e_);         \
+      (void)hipGetLastError();                          \
+      return SV_EHIP;                                   \
+    }                                                   \
   } while (0)
 
 hipError_t run_gemm(const Gemm &g, GemmArgs a, int epi, hipStream_t st) {
@@ -256,6 +263,8 @@ SV_API int spec_verify_greedy(const sv_weights *w, const uint16_t *h, const int3
   g.parts = at<StatPart>(ws, p.o_parts); g.nslots = p.lm.nslots;
   g.invT = 1.f; g.want_s = out->diag ? 1 : 0;
   g.status_reset = reset;
+  int32_t *sync = at<int32_t>(ws, p.o_sync);
+  g.counter_reset = sync;
   SV_CHECK(run_gemm_timed(p.lm, g, EPI_LOGITS, out, st));
   AcceptArgs a = {};
   a.B = B; a.K = K; a.V = p.V; a.invT = 1.f;
@@ -263,8 +272,9 @@ SV_API int spec_verify_greedy(const sv_weights *w, const uint16_t *h, const int3
   a.logits_t = out->logits;
   a.draft = draft; a.accepted_len = out->accepted_len; a.emitted = out->emitted;
   a.dev_status = out->dev_status; a.diag = out->diag;
+  a.done_cnt = sync;
+  a.fin = FinalizeArgs{out->accepted_len, nullptr, B, K, out->tau, out->counters};
   SV_CHECK(launch_accept_greedy(a, st));
-  SV_CHECK(launch_finalize(out->accepted_len, nullptr, B, K, out->tau, out->counters, st));
   return SV_OK;
 }
 
@@ -306,9 +316,11 @@ SV_API int spec_verify_sample(const sv_weights *w, const uint16_t *h, const uint
   a.accepted_len = out->accepted_len; a.emitted = out->emitted;
   a.jobs = at<SampleJob>(ws, p.o_jobs);
   a.dev_status = out->dev_status; a.diag = out->diag;
+  int32_t *sync = at<int32_t>(ws, p.o_sync);
+  a.done_cnt = sync; a.job_cnt = sync + 1;
   SV_CHECK(launch_accept_sample(a, st));
-  SV_CHECK(launch_sample(a.jobs, B, p.V, invT, at<float>(ws, p.o_sums), out->emitted, st));
-  SV_CHECK(launch_finalize(out->accepted_len, nullptr, B, K, out->tau, out->counters, st));
+  const FinalizeArgs fin{out->accepted_len, nullptr, B, K, out->tau, out->counters};
+  SV_CHECK(launch_sample(a.jobs, B, p.V, invT, at<float>(ws, p.o_sums), out->emitted, sync + 1, sync, fin, st));
   return SV_OK;
 }
 
@@ -385,9 +397,11 @@ SV_API int spec_verify_scheduled(const sv_weights *w, const uint16_t *h, const u
   a.accepted_len = out->accepted_len; a.emitted = out->emitted;
   a.jobs = at<SampleJob>(ws, p.o_jobs);
   a.dev_status = out->dev_status; a.diag = out->diag;
+  int32_t *sync = at<int32_t>(ws, p.o_sync);
+  a.done_cnt = sync; a.job_cnt = sync + 1;
   SV_CHECK(launch_accept_sample(a, st));
-  SV_CHECK(launch_sample(a.jobs, B, p.V, invT, at<float>(ws, p.o_sums), out->emitted, st));
-  SV_CHECK(launch_finalize(out->accepted_len, vlen, B, Kmax, out->tau, out->counters, st));
+  const FinalizeArgs fin{out->accepted_len, vlen, B, Kmax, out->tau, out->counters};
+  SV_CHECK(launch_sample(a.jobs, B, p.V, invT, at<float>(ws, p.o_sums), out->emitted, sync + 1, sync, fin, st));
   if (out->logits) SV_CHECK(launch_scatter_logits(logits_t, out->logits, rowmap, mtot, p.budget, p.V, st));
   if (out->hidden && p.d_ff > 0)
     SV_CHECK(launch_scatter_hidden(at<uint16_t>(ws, p.o_y), out->hidden, rowmap, mtot, p.budget, p.d, st));
@@ -415,11 +429,17 @@ SV_API int spec_draft_propose(const sv_weights *w, const uint16_t *h_draft, cons
   g.invT = invT; g.want_s = samp ? 1 : 0;
   SV_CHECK(run_gemm(p.lm, g, EPI_LOGITS, st));
   SampleJob *jobs = at<SampleJob>(ws, p.o_jobs);
+  int32_t *sync = at<int32_t>(ws, p.o_sync);
   SV_CHECK(launch_propose_finish(g.parts, p.lm.nslots, rows, invT, T, logits, p.V, coins, jobs, draft_out, conf_out,
-                                 nullptr, st));
-  if (samp) SV_CHECK(launch_sample(jobs, rows, p.V, invT, at<float>(ws, p.o_sums), draft_out, st));
+                                 nullptr, sync + 1, st));
+  if (samp) {
+    const FinalizeArgs none{nullptr, nullptr, 0, 0, nullptr, nullptr};
+    SV_CHECK(launch_sample(jobs, rows, p.V, invT, at<float>(ws, p.o_sums), draft_out, sync + 1, sync, none, st));
+  }
   return SV_OK;
 }
+
+SV_API const char *sv_last_hip_error(void) { return g_last_hip_error; }
 
 SV_API const char *sv_version(void) { return "specverify 0.1.0 (gfx950)"; }
 

@@ -58,8 +58,10 @@ struct GemmArgs {
   long ldr;
   // EPI_RAW (split-K partials [splits][M][Ncols])
   float *partial;
-  // zeroed by thread 0 of block 0 before anything else (device status of the call)
+  // zeroed by thread 0 of block 0 before anything else (device status, arrival counter)
   int32_t *status_reset;
+  int32_t *counter_reset;
+  int buf_cols;  // set by the streaming launcher: columns of the per-workgroup output buffer
 };
 
 // Sampling job: draw v from w_v = max(0, exp(z1_v*invT - lse1) - [z2 ? exp(z2_v*invT - lse2) : 0])
@@ -84,6 +86,15 @@ hipError_t launch_gemm_tiled(const GemmArgs &a, int epi, int bm, int bn, int spl
 int tiled_slots(int N, int bn);
 hipError_t launch_splitk_reduce(const GemmArgs &a, int epi, int splits, int bn, hipStream_t st);
 
+// End-of-call bookkeeping (tau and counters), run by the last block of the last kernel.
+struct FinalizeArgs {
+  const int32_t *acc;   // accepted lengths [B]; null = skip
+  const int32_t *vlen;  // verified drafts per request [B] (scheduled), else null (K each)
+  int B, K;
+  float *tau;
+  int64_t *counters;
+};
+
 struct AcceptArgs {
   int B, K, V;  // K = Kmax in scheduled mode
   float invT;
@@ -102,16 +113,17 @@ struct AcceptArgs {
   SampleJob *jobs;  // one per request (sample / scheduled)
   int32_t *dev_status;
   float *diag;  // may be null
+  int32_t *job_cnt;   // sampling arrival counters [B] (zeroed here)
+  int32_t *done_cnt;  // call-wide arrival counter (zeroed here in sampled modes; greedy: zeroed earlier)
+  FinalizeArgs fin;   // greedy: bookkeeping by the last block
 };
 hipError_t launch_accept_sample(const AcceptArgs &a, hipStream_t st);
 hipError_t launch_accept_greedy(const AcceptArgs &a, hipStream_t st);
 
 int sample_chunks(int V);
 hipError_t launch_sample(const SampleJob *jobs, int njobs, int V, float invT, float *chunk_sums,
-                         int32_t *out, hipStream_t st);
-
-hipError_t launch_finalize(const int32_t *accepted_len, const int32_t *verify_len, int B, int K,
-                           float *tau, int64_t *counters, hipStream_t st);
+                         int32_t *out, int32_t *job_cnt, int32_t *done_cnt, const FinalizeArgs &fin,
+                         hipStream_t st);
 
 hipError_t launch_init(int32_t *zero_i32, size_t n_i32, int32_t *dev_status, hipStream_t st);
 
@@ -142,6 +154,6 @@ hipError_t launch_scatter_hidden(const uint16_t *packed, uint16_t *dst, const in
 hipError_t launch_propose_finish(const StatPart *parts, int nslots, int rows, float invT, float T,
                                  const float *logits, int V, const float *coins, SampleJob *jobs,
                                  int32_t *draft_out, float *conf_out, int32_t *dev_status,
-                                 hipStream_t st);
+                                 int32_t *job_cnt, hipStream_t st);
 
 }  // namespace sv

@@ -16,6 +16,7 @@ namespace sv {
 namespace {
 
 constexpr int NT = 256;  // threads per block for the small kernels
+constexpr int PER = 8;   // tokens per thread in the final scan of a sampling chunk (chunk <= NT * PER)
 
 __device__ void set_status(int32_t *st, int code) {
   if (st) atomicCAS(st, 0, code);
@@ -36,8 +37,93 @@ __global__ void k_init(int32_t *z, long n, int32_t *dev_status) {
   if (dev_status && blockIdx.x == 0 && threadIdx.x == 0) *dev_status = 0;
 }
 
+// ---- block-wide helpers (fixed reduction order: results do not depend on timing)
+__device__ float block_sum(float v, float *red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[w];
+  return t;
+}
+
+__device__ int block_min_int(int v, int *red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  int t = red[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) t = min(t, red[w]);
+  return t;
+}
+
+// Inclusive prefix sum over the block in thread order: shuffle scan inside each wave,
+// then the wave totals (fixed order).  buf needs one float per wave.
+__device__ float block_incl_scan(float v, float *buf) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float x = __shfl_up(v, off);
+    if (lane >= off) v += x;
+  }
+  __syncthreads();
+  if (lane == 63) buf[wave] = v;
+  __syncthreads();
+  float base = 0.f;
+  for (int w = 0; w < wave; ++w) base += buf[w];
+  return base + v;
+}
+
+// End-of-call bookkeeping: tau = mean(A_b + 1) over valid requests and the counters.
+__device__ void finalize_block(const FinalizeArgs &f) {
+  __shared__ long long red[4][16];
+  long long sa = 0, sd = 0, se = 0, nv = 0;
+  for (int b = threadIdx.x; b < f.B; b += blockDim.x) {
+    const int A = f.acc[b];
+    if (A < 0) continue;
+    sa += A;
+    sd += f.vlen ? f.vlen[b] : f.K;
+    se += A + 1;
+    nv += 1;
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    sa += __shfl_xor(sa, off);
+    sd += __shfl_xor(sd, off);
+    se += __shfl_xor(se, off);
+    nv += __shfl_xor(nv, off);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) { red[0][wave] = sa; red[1][wave] = sd; red[2][wave] = se; red[3][wave] = nv; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long ta = 0, td = 0, te = 0, valid = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) { ta += red[0][w]; td += red[1][w]; te += red[2][w]; valid += red[3][w]; }
+    *f.tau = valid ? (float)((double)te / (double)valid) : 0.f;
+    if (f.counters) { f.counters[0] = ta; f.counters[1] = td; f.counters[2] = te; }
+  }
+}
+
+// Is this block the last one to arrive at `counter` (of `total`)?  Release before, acquire after.
+__device__ bool arrive_last(int32_t *counter, int total, int *flag) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const int old = atomicAdd(counter, 1);
+    *flag = (old == total - 1);
+  }
+  __syncthreads();
+  const bool last = *flag != 0;
+  if (last) __threadfence();
+  return last;
+}
+
 // One block per request.  Row statistics are merged by one wave per row.
-__global__ __launch_bounds__(NT) void k_accept_sample(const AcceptArgs a) {
+__global__ __launch_bounds__(1024) void k_accept_sample(const AcceptArgs a) {
   extern __shared__ float sm[];
   const int b = blockIdx.x;
   const int Kmax = a.K;
@@ -48,12 +134,17 @@ __global__ __launch_bounds__(NT) void k_accept_sample(const AcceptArgs a) {
   float *lse_t = sm;                  // [Kmax+1]
   float *lse_d = sm + (Kmax + 1);     // [Kmax]
   __shared__ int bad;
-  if (threadIdx.x == 0) bad = 0;
+  if (threadIdx.x == 0) {
+    bad = 0;
+    a.job_cnt[b] = 0;  // arrival counters of the sampling kernel that follows
+    if (b == 0) *a.done_cnt = 0;
+  }
   __syncthreads();
+  const int nw = blockDim.x >> 6;
 
   // row statistics: target rows 0..Kb, draft rows 0..Kb-1
   const int nrows = 2 * Kb + 1;
-  for (int r = wave; r < nrows; r += NT / 64) {
+  for (int r = wave; r < nrows; r += nw) {
     const bool is_t = r <= Kb;
     const int j = is_t ? r : r - Kb - 1;
     const StatPart *pp = is_t ? a.parts_t + (trow0 + j) * a.nslots_t : a.parts_d + (drow0 + j) * a.nslots_d;
@@ -66,7 +157,7 @@ __global__ __launch_bounds__(NT) void k_accept_sample(const AcceptArgs a) {
         const long drow = is_t ? (long)b * (Kmax + 1) + j : (long)a.B * (Kmax + 1) + drow0 + j;
         float *dg = a.diag + drow * SV_DIAG_COLS;
         dg[0] = lse; dg[1] = (float)st.i1; dg[2] = st.b1 - st.b2; dg[3] = st.b1;
-        dg[4] = NAN; dg[5] = NAN; dg[6] = is_t ? NAN : __expf(st.b1 * a.invT - lse); dg[7] = 0.f;
+        dg[4] = NAN; dg[5] = NAN; dg[6] = is_t ? NAN : 1.f / st.s; dg[7] = 0.f;
       }
     }
   }
@@ -139,16 +230,17 @@ __global__ __launch_bounds__(NT) void k_accept_sample(const AcceptArgs a) {
   }
 }
 
-__global__ __launch_bounds__(NT) void k_accept_greedy(const AcceptArgs a) {
+__global__ __launch_bounds__(1024) void k_accept_greedy(const AcceptArgs a) {
   extern __shared__ float sm[];
   int *amax = reinterpret_cast<int *>(sm);  // [K+1]
   const int b = blockIdx.x, K = a.K;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const long trow0 = (long)b * (K + 1);
-  __shared__ int bad;
+  __shared__ int bad, flag;
   if (threadIdx.x == 0) bad = 0;
   __syncthreads();
-  for (int j = wave; j <= K; j += NT / 64) {
+  const int nw = blockDim.x >> 6;
+  for (int j = wave; j <= K; j += nw) {
     const StatPart st = wave_merge_row(a.parts_t + (trow0 + j) * a.nslots_t, a.nslots_t, 1.f, a.diag != nullptr);
     if (lane == 0) {
       amax[j] = st.i1;
@@ -194,11 +286,13 @@ __global__ __launch_bounds__(NT) void k_accept_greedy(const AcceptArgs a) {
       a.emitted[(long)b * (K + 1) + j] = v;
     }
   }
+  if (a.fin.acc && arrive_last(a.done_cnt, a.B, &flag)) finalize_block(a.fin);
 }
 
-// ---- inverse-CDF sampling over V, split in chunks: pass 1 sums each chunk,
-// pass 2 locates the chunk and the token.  Weights are recomputed in both passes
-// from the fp32 logits, in ascending token order.
+// ---- inverse-CDF sampling over V, split in chunks.  Every block sums the weights of
+// its chunk; the last block of a job locates the chunk and then the token with block
+// prefix scans; the last job block overall runs the end-of-call bookkeeping.
+// Weights are recomputed from the fp32 logits in ascending token order.
 __device__ __forceinline__ float job_weight(const SampleJob &jb, int v, float invT, bool resid) {
   const float p = __expf(jb.z1[v] * invT - jb.lse1);
   if (!resid) return p;
@@ -206,137 +300,87 @@ __device__ __forceinline__ float job_weight(const SampleJob &jb, int v, float in
   return fmaxf(p - q, 0.f);
 }
 
-__device__ float block_sum(float v, float *red) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float t = 0.f;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[w];
-  return t;
-}
-
-__global__ __launch_bounds__(NT) void k_sample_chunks(const SampleJob *jobs, int V, int chunk, float invT,
-                                                      float *sums) {
+__global__ __launch_bounds__(NT) void k_sample(const SampleJob *jobs, int njobs, int V, int chunk, float invT,
+                                               float *sums, int32_t *out, int32_t *job_cnt, int32_t *done_cnt,
+                                               FinalizeArgs fin) {
   __shared__ float red[NT / 64];
-  const SampleJob jb = jobs[blockIdx.y];
-  const int c = blockIdx.x, C = gridDim.x;
-  const int v0 = c * chunk, v1 = min(V, v0 + chunk);
-  float sr = 0.f, sp = 0.f;
-  if (jb.out_index >= 0) {
-    for (int v = v0 + threadIdx.x; v < v1; v += NT) {
-      const float p = __expf(jb.z1[v] * invT - jb.lse1);
-      sp += p;
-      if (jb.z2) sr += fmaxf(p - __expf(jb.z2[v] * invT - jb.lse2), 0.f);
+  __shared__ int redi[NT / 64];
+  __shared__ float buf[NT / 64];
+  __shared__ float buf2[NT];
+  __shared__ int flag;
+  const int job = blockIdx.y, c = blockIdx.x, C = gridDim.x, t = threadIdx.x;
+  const SampleJob jb = jobs[job];
+  {
+    const int v0 = c * chunk, v1 = min(V, v0 + chunk);
+    float sr = 0.f, sp = 0.f;
+    if (jb.out_index >= 0) {
+      for (int v = v0 + t; v < v1; v += NT) {
+        const float p = __expf(jb.z1[v] * invT - jb.lse1);
+        sp += p;
+        if (jb.z2) sr += fmaxf(p - __expf(jb.z2[v] * invT - jb.lse2), 0.f);
+      }
+    }
+    const float tr = block_sum(sr, red);
+    const float tp = block_sum(sp, red);
+    if (t == 0) {
+      sums[((long)job * C + c) * 2 + 0] = tr;
+      sums[((long)job * C + c) * 2 + 1] = tp;
     }
   }
-  const float tr = block_sum(sr, red);
-  const float tp = block_sum(sp, red);
-  if (threadIdx.x == 0) {
-    sums[((long)blockIdx.y * C + c) * 2 + 0] = tr;
-    sums[((long)blockIdx.y * C + c) * 2 + 1] = tp;
-  }
-}
+  if (!arrive_last(job_cnt + job, C, &flag)) return;
 
-__global__ __launch_bounds__(NT) void k_sample_pick(const SampleJob *jobs, int V, int chunk, int C, float invT,
-                                                    const float *sums, int32_t *out) {
-  __shared__ float red[NT / 64];
-  __shared__ float wsum[NT];
-  __shared__ int s_chunk;
-  __shared__ float s_base, s_target;
-  __shared__ int s_resid;
-  const SampleJob jb = jobs[blockIdx.x];
-  if (jb.out_index < 0) return;
-  const float *cs = sums + (long)blockIdx.x * C * 2;
-  if (threadIdx.x == 0) {
-    // totals in a fixed (ascending chunk) order
-    float tr = 0.f, tp = 0.f;
-    for (int c = 0; c < C; ++c) { tr += cs[2 * c]; tp += cs[2 * c + 1]; }
-    const int resid = (jb.z2 != nullptr && tr > 0.f) ? 1 : 0;
+  if (jb.out_index >= 0) {
+    const float wr = t < C ? sums[((long)job * C + t) * 2 + 0] : 0.f;
+    const float wp = t < C ? sums[((long)job * C + t) * 2 + 1] : 0.f;
+    const float tr = block_sum(wr, red);
+    const float tp = block_sum(wp, red);
+    const bool resid = jb.z2 != nullptr && tr > 0.f;
     const float total = resid ? tr : tp;
     const float target = jb.u * total;
-    float run = 0.f;
-    int pick = -1;
-    int last_nz = 0;
-    for (int c = 0; c < C; ++c) {
-      const float w = cs[2 * c + (resid ? 0 : 1)];
-      if (w > 0.f) last_nz = c;
-      if (pick < 0 && run + w > target) { pick = c; break; }
-      run += w;
+    const float w = resid ? wr : wp;
+    const float incl = block_incl_scan(w, buf);
+    int pick = block_min_int((t < C && incl > target) ? t : 0x7fffffff, redi);
+    if (pick == 0x7fffffff) {  // rounding put the target at the very end: last non-empty chunk
+      pick = -block_min_int((t < C && w > 0.f) ? -t : 1, redi);
+      if (pick < 0) pick = 0;
     }
-    if (pick < 0) {  // rounding put the target past the last chunk: take the last non-empty one
-      pick = last_nz;
-      run = 0.f;
-      for (int c = 0; c < pick; ++c) run += cs[2 * c + (resid ? 0 : 1)];
+    buf2[t] = incl - w;  // exclusive prefix of the chunk sums
+    __syncthreads();
+    const float base = buf2[pick];
+    const int v0 = pick * chunk, v1 = min(V, v0 + chunk);
+    // each thread owns a contiguous run of at most PER tokens, weights kept in registers
+    const int per = (chunk + NT - 1) / NT;
+    const int a0 = v0 + t * per;
+    float wv[PER];
+    float mine = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      wv[i] = (i < per && a0 + i < v1) ? job_weight(jb, a0 + i, invT, resid) : 0.f;
+      mine += wv[i];
     }
-    s_chunk = pick; s_base = run; s_target = target; s_resid = resid;
-  }
-  __syncthreads();
-  const int c = s_chunk;
-  const bool resid = s_resid != 0;
-  const int v0 = c * chunk, v1 = min(V, v0 + chunk);
-  // each thread owns a contiguous run of the chunk
-  const int per = (chunk + NT - 1) / NT;
-  const int a0 = v0 + threadIdx.x * per, a1 = min(v1, a0 + per);
-  float mine = 0.f;
-  for (int v = a0; v < a1; ++v) mine += job_weight(jb, v, invT, resid);
-  wsum[threadIdx.x] = mine;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float run = s_base;
-    int pick_t = -1, last_t = -1;
-    for (int t = 0; t < NT; ++t) {
-      if (wsum[t] > 0.f) last_t = t;
-      if (pick_t < 0 && run + wsum[t] > s_target) { pick_t = t; break; }
-      run += wsum[t];
+    const float incl2 = block_incl_scan(mine, buf);
+    int tp2 = block_min_int((mine > 0.f && base + incl2 > target) ? t : 0x7fffffff, redi);
+    if (tp2 == 0x7fffffff) {
+      tp2 = -block_min_int(mine > 0.f ? -t : 1, redi);
+      if (tp2 < 0) tp2 = 0;
     }
-    if (pick_t < 0) pick_t = last_t;
-    if (pick_t < 0) pick_t = 0;
-    // rescan the picked thread's run sequentially
-    float r2 = s_base;
-    for (int t = 0; t < pick_t; ++t) r2 += wsum[t];
-    const int b0 = v0 + pick_t * per, b1 = min(v1, b0 + per);
-    int v_pick = -1, v_last = -1;
-    for (int v = b0; v < b1; ++v) {
-      const float w = job_weight(jb, v, invT, resid);
-      if (w > 0.f) v_last = v;
-      if (r2 + w > s_target) { v_pick = v; break; }
-      r2 += w;
+    if (t == tp2) {
+      float run = base + incl2 - mine;
+      int v_pick = -1, v_last = -1;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        if (v_pick >= 0) break;
+        if (wv[i] > 0.f) {
+          v_last = a0 + i;
+          if (run + wv[i] > target) v_pick = a0 + i;
+        }
+        run += wv[i];
+      }
+      if (v_pick < 0) v_pick = v_last >= 0 ? v_last : min(max(a0, 0), V - 1);
+      out[jb.out_index] = v_pick;
     }
-    if (v_pick < 0) v_pick = v_last >= 0 ? v_last : b0;
-    out[jb.out_index] = v_pick;
   }
-}
-
-__global__ __launch_bounds__(1024) void k_finalize(const int32_t *acc, const int32_t *vlen, int B, int K,
-                                                   float *tau, int64_t *counters) {
-  __shared__ long long red[4][16];
-  long long sa = 0, sd = 0, se = 0, nv = 0;
-  for (int b = threadIdx.x; b < B; b += blockDim.x) {
-    const int A = acc[b];
-    if (A < 0) continue;
-    sa += A;
-    sd += vlen ? vlen[b] : K;
-    se += A + 1;
-    nv += 1;
-  }
-  for (int off = 32; off >= 1; off >>= 1) {
-    sa += __shfl_xor(sa, off);
-    sd += __shfl_xor(sd, off);
-    se += __shfl_xor(se, off);
-    nv += __shfl_xor(nv, off);
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) { red[0][wave] = sa; red[1][wave] = sd; red[2][wave] = se; red[3][wave] = nv; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    long long ta = 0, td = 0, te = 0, valid = 0;
-    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) { ta += red[0][w]; td += red[1][w]; te += red[2][w]; valid += red[3][w]; }
-    *tau = valid ? (float)((double)te / (double)valid) : 0.f;
-    if (counters) { counters[0] = ta; counters[1] = td; counters[2] = te; }
-  }
+  if (fin.acc && arrive_last(done_cnt, njobs, &flag)) finalize_block(fin);
 }
 
 // Confidence of each draft row: conf = max_v q(v) = 1 / sum_v exp((z_v - max z)/T).  One wave per row.
@@ -467,13 +511,14 @@ __global__ void k_scatter_u16(const uint16_t *packed, uint16_t *dst, const int32
 __global__ __launch_bounds__(NT) void k_propose_finish(const StatPart *parts, int nslots, int rows, float invT,
                                                        float T, const float *logits, int V, const float *coins,
                                                        SampleJob *jobs, int32_t *draft_out, float *conf_out,
-                                                       int32_t *dev_status) {
+                                                       int32_t *dev_status, int32_t *job_cnt) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = blockIdx.x * (NT / 64) + wave;
   if (r >= rows) return;
   const bool samp = T > 0.f;
   const StatPart st = wave_merge_row(parts + (long)r * nslots, nslots, samp ? invT : 1.f, samp);
   if (lane != 0) return;
+  job_cnt[r] = 0;
   const float lse = st.b1 * invT + __logf(st.s);
   const bool fin = isfinite(st.b1) && (!samp || isfinite(lse));
   if (!fin) set_status(dev_status, SV_DEV_NONFINITE);
@@ -507,37 +552,32 @@ hipError_t launch_init(int32_t *zero_i32, size_t n_i32, int32_t *dev_status, hip
 
 hipError_t launch_accept_sample(const AcceptArgs &a, hipStream_t st) {
   const size_t shm = sizeof(float) * (2 * a.K + 2);
-  hipLaunchKernelGGL(k_accept_sample, dim3(a.B), dim3(NT), shm, st, a);
+  const int nw = min(16, max(1, 2 * a.K + 1));
+  hipLaunchKernelGGL(k_accept_sample, dim3(a.B), dim3(64 * nw), shm, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_accept_greedy(const AcceptArgs &a, hipStream_t st) {
   const size_t shm = sizeof(int) * (a.K + 2);
-  hipLaunchKernelGGL(k_accept_greedy, dim3(a.B), dim3(NT), shm, st, a);
+  const int nw = min(16, max(1, a.K + 1));
+  hipLaunchKernelGGL(k_accept_greedy, dim3(a.B), dim3(64 * nw), shm, st, a);
   return hipGetLastError();
 }
 
 int sample_chunks(int V) {
-  int c = (V + 2047) / 2048;
-  if (c > 256) c = 256;
+  // chunks of at most NT * PER tokens; at most NT chunks (one per thread of the pick)
+  int c = (V + NT * PER - 1) / (NT * PER);
   if (c < 1) c = 1;
   return c;
 }
 
 hipError_t launch_sample(const SampleJob *jobs, int njobs, int V, float invT, float *chunk_sums, int32_t *out,
-                         hipStream_t st) {
+                         int32_t *job_cnt, int32_t *done_cnt, const FinalizeArgs &fin, hipStream_t st) {
   if (njobs <= 0) return hipSuccess;
   const int C = sample_chunks(V);
   const int chunk = (V + C - 1) / C;
-  hipLaunchKernelGGL(k_sample_chunks, dim3(C, njobs), dim3(NT), 0, st, jobs, V, chunk, invT, chunk_sums);
-  hipLaunchKernelGGL(k_sample_pick, dim3(njobs), dim3(NT), 0, st, jobs, V, chunk, C, invT,
-                     (const float *)chunk_sums, out);
-  return hipGetLastError();
-}
-
-hipError_t launch_finalize(const int32_t *accepted_len, const int32_t *verify_len, int B, int K, float *tau,
-                           int64_t *counters, hipStream_t st) {
-  hipLaunchKernelGGL(k_finalize, dim3(1), dim3(1024), 0, st, accepted_len, verify_len, B, K, tau, counters);
+  hipLaunchKernelGGL(k_sample, dim3(C, njobs), dim3(NT), 0, st, jobs, njobs, V, chunk, invT, chunk_sums, out, job_cnt,
+                     done_cnt, fin);
   return hipGetLastError();
 }
 
@@ -571,10 +611,10 @@ hipError_t launch_scatter_hidden(const uint16_t *packed, uint16_t *dst, const in
 
 hipError_t launch_propose_finish(const StatPart *parts, int nslots, int rows, float invT, float T,
                                  const float *logits, int V, const float *coins, SampleJob *jobs, int32_t *draft_out,
-                                 float *conf_out, int32_t *dev_status, hipStream_t st) {
+                                 float *conf_out, int32_t *dev_status, int32_t *job_cnt, hipStream_t st) {
   const int blocks = (rows + (NT / 64) - 1) / (NT / 64);
   hipLaunchKernelGGL(k_propose_finish, dim3(blocks), dim3(NT), 0, st, parts, nslots, rows, invT, T, logits, V,
-                     coins, jobs, draft_out, conf_out, dev_status);
+                     coins, jobs, draft_out, conf_out, dev_status, job_cnt);
   return hipGetLastError();
 }
 

@@ -90,7 +90,7 @@ typedef struct sv_weights {
   const uint16_t *w_lm;   /* [V, d] shared LM head */
   int32_t d;              /* hidden size, multiple of 64 */
   int32_t d_ff;           /* MLP width, multiple of 64, or 0 */
-  int32_t V;              /* vocabulary, 1 <= V < 2^24 */
+  int32_t V;              /* vocabulary, 1 <= V <= 524288 */
 } sv_weights;
 
 typedef struct sv_outputs {
@@ -156,9 +156,11 @@ int spec_draft_propose(const sv_weights *w, const uint16_t *h_draft, const float
                        int rows, void *ws, size_t ws_bytes, int32_t *draft_out, float *conf_out,
                        void *stream);
 
-/* Library version string and a text for an SV_E* code. */
+/* Library version string, a text for an SV_E* code, and the HIP error text behind
+ * the last SV_EHIP returned on the calling thread. */
 const char *sv_version(void);
 const char *sv_strerror(int code);
+const char *sv_last_hip_error(void);
 
 #ifdef __cplusplus
 }

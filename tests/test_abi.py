@@ -73,7 +73,7 @@ def test_workspace_sizes(lib):
 
 
 @pytest.mark.parametrize("bad", [
-    dict(d=100), dict(d=0), dict(d_ff=100), dict(V=0), dict(V=1 << 24), dict(mlp=False, d_ff=12288),
+    dict(d=100), dict(d=0), dict(d_ff=100), dict(V=0), dict(V=(1 << 19) + 1), dict(mlp=False, d_ff=12288),
 ])
 def test_workspace_rejects_bad_shapes(lib, bad):
     kw = dict(d=4096, d_ff=12288, V=151936, mlp=True)
