@@ -18,6 +18,8 @@
 //  * the 8 partial accumulators of a tile are summed in a fixed order through LDS
 //    (deterministic), then the epilogue runs: fp32 logits + running per-row
 //    statistics, SwiGLU with paired gate/up rows, or residual add, bf16 output.
+#include <type_traits>
+
 #include "sv_device.h"
 
 namespace sv {
@@ -48,7 +50,8 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
   extern __shared__ float obuf[];
 
   if (a.status_reset && blockIdx.x == 0 && threadIdx.x == 0) *a.status_reset = 0;
-  if (a.counter_reset && blockIdx.x == 0 && threadIdx.x == 0) *a.counter_reset = 0;
+  if (a.counter_reset && blockIdx.x == 0 && blockIdx.z == 0)
+    for (int i = threadIdx.x; i < max(1, a.counter_reset_n); i += blockDim.x) a.counter_reset[i] = 0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int M = a.M_dev ? min(a.M, *a.M_dev) : a.M;
   const int N = a.N;
@@ -110,10 +113,13 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
 
   f32x4 acc[NACC];
   int parity = 0;
-  for (int stp = 0; stp < nsteps; ++stp) {
-    const int tile = t_begin + stp / nch, c = stp % nch;
-    // the last step re-loads its own operands: harmless, and keeps the loop free of branches
-    const int nstp = min(stp + 1, nsteps - 1);
+  // One step: the MFMAs of the current operands, each slot refilled right after use
+  // with the next step's operands.  The last step is peeled (PF = false) so it issues
+  // no prefetch at all and the loop body stays free of branches around loads.
+  auto mma_step = [&](int stp, auto pf) {
+    constexpr bool PF = decltype(pf)::value;
+    const int c = stp % nch;
+    const int nstp = stp + 1;
     const int ntile = t_begin + nstp / nch, nc = nstp % nch;
     if (c == 0) {
 #pragma unroll
@@ -131,15 +137,22 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
           acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][s], Wr[s], acc[mb], 0, 0, 0);
         }
       }
-      Wr[s] = as_bf16x8(ld16(wptr(a.w, ntile, nc, s)));
-      if constexpr (PAIR) Ur[s] = as_bf16x8(ld16(wptr(a.w2, ntile, nc, s)));
-      if constexpr (RELOAD_A) {
+      if constexpr (PF) {
+        Wr[s] = as_bf16x8(ld16(wptr(a.w, ntile, nc, s)));
+        if constexpr (PAIR) Ur[s] = as_bf16x8(ld16(wptr(a.w2, ntile, nc, s)));
+        if constexpr (RELOAD_A) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) A[mb][s] = load_a(nc, s, mb);
+          for (int mb = 0; mb < MB; ++mb) A[mb][s] = load_a(nc, s, mb);
+        }
       }
       // keep "use slot s, refill slot s" in program order so loads stay spread over the step
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  for (int stp = 0; stp < nsteps; ++stp) {
+    const int tile = t_begin + stp / nch, c = stp % nch;
+    if (stp + 1 < nsteps) mma_step(stp, std::true_type{});
+    else mma_step(stp, std::false_type{});
     if (c != nch - 1) continue;
 
     // ---- deterministic cross-wave reduction of the tile through LDS

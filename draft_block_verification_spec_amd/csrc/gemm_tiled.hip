@@ -31,7 +31,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   uint16_t(*Bs)[BN * LDK] = reinterpret_cast<uint16_t(*)[BN * LDK]>(smem + 2 * BM * LDK);
 
   if (a.status_reset && blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0) *a.status_reset = 0;
-  if (a.counter_reset && blockIdx.x == 0 && threadIdx.x == 0) *a.counter_reset = 0;
+  if (a.counter_reset && blockIdx.x == 0 && blockIdx.z == 0)
+    for (int i = threadIdx.x; i < max(1, a.counter_reset_n); i += blockDim.x) a.counter_reset[i] = 0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   int M = a.M;

@@ -29,6 +29,9 @@ int num_cus() {
 namespace {
 
 constexpr size_t ALIGN = 256;
+// Up to this many (request, position) candidates the sampled modes draw every possible
+// final token speculatively and decide acceptance in the same kernel (latency path).
+constexpr int SMALL_TAIL_JOBS = 32;
 size_t up(size_t x) { return (x + ALIGN - 1) & ~(ALIGN - 1); }
 
 struct Gemm {
@@ -71,7 +74,8 @@ struct Plan {
   Gemm gu, dn, lm, s1;
   size_t o_a = 0, o_y = 0, o_part = 0, o_parts = 0, o_parts_d = 0, o_logits = 0, o_logits_d = 0,
          o_jobs = 0, o_sums = 0, o_conf = 0, o_vlen = 0, o_rowoff = 0, o_rowmap = 0, o_mtot = 0,
-         o_hp = 0, o_sync = 0, total = 0;
+         o_hp = 0, o_sync = 0, o_cand = 0, o_lse = 0, total = 0;
+  bool small_tail = false;  // speculative per-position sampling + acceptance in one kernel
 };
 
 bool valid_weights(const sv_weights *w) {
@@ -128,12 +132,19 @@ bool make_plan(int mode, int B, int K, const sv_weights *w, int budget, Plan &p)
   if (part_floats) p.o_part = take(sizeof(float) * part_floats);
   p.lm = choose(p.M_lm, V, d, EPI_LOGITS);
   p.o_parts = take(sizeof(StatPart) * (size_t)p.M_lm * p.lm.nslots);
+  const int NJ = B * (K + 1);
   if (mode != SV_MODE_GREEDY) {
+    p.small_tail = NJ <= SMALL_TAIL_JOBS;
     p.o_logits = take(sizeof(float) * (size_t)p.M_lm * V);
     p.o_jobs = take(sizeof(SampleJob) * (size_t)B);
-    p.o_sums = take(sizeof(float) * 2 * (size_t)B * sample_chunks(V));
+    p.o_sums = take(sizeof(float) * 2 * (size_t)(p.small_tail ? NJ : B) * sample_chunks(V));
+    if (p.small_tail) {
+      p.o_cand = take(sizeof(StatPart) * 2 * (size_t)NJ);  // per-candidate row statistics
+      p.o_lse = take(sizeof(float) * 2 * (size_t)NJ);
+    }
   }
-  p.o_sync = take(sizeof(int32_t) * (size_t)(B + 1));  // [0] call-wide arrivals, [1 + b] per request
+  // arrival counters: [0] call-wide, [1 + i] per request (or per candidate job)
+  p.o_sync = take(sizeof(int32_t) * (size_t)(1 + (p.small_tail ? NJ : B)));
   if (mode == SV_MODE_SCHEDULED) {
     p.s1 = choose(p.rows_d > 0 ? p.rows_d : 1, V, d, EPI_LOGITS);
     p.o_parts_d = take(sizeof(StatPart) * (size_t)(p.rows_d > 0 ? p.rows_d : 1) * p.s1.nslots);
@@ -306,6 +317,7 @@ SV_API int spec_verify_sample(const sv_weights *w, const uint16_t *h, const uint
   g.parts = at<StatPart>(ws, p.o_parts); g.nslots = p.lm.nslots;
   g.invT = invT; g.want_s = 1;
   g.status_reset = reset;
+  int32_t *sync = at<int32_t>(ws, p.o_sync);
   SV_CHECK(run_gemm_timed(p.lm, g, EPI_LOGITS, out, st));
   AcceptArgs a = {};
   a.B = B; a.K = K; a.V = p.V; a.invT = invT;
@@ -316,10 +328,14 @@ SV_API int spec_verify_sample(const sv_weights *w, const uint16_t *h, const uint
   a.accepted_len = out->accepted_len; a.emitted = out->emitted;
   a.jobs = at<SampleJob>(ws, p.o_jobs);
   a.dev_status = out->dev_status; a.diag = out->diag;
-  int32_t *sync = at<int32_t>(ws, p.o_sync);
   a.done_cnt = sync; a.job_cnt = sync + 1;
-  SV_CHECK(launch_accept_sample(a, st));
   const FinalizeArgs fin{out->accepted_len, nullptr, B, K, out->tau, out->counters};
+  if (p.small_tail) {
+    SV_CHECK(launch_tail_small(a, at<float>(ws, p.o_sums), at<float>(ws, p.o_lse), at<StatPart>(ws, p.o_cand), fin,
+                               st));
+    return SV_OK;
+  }
+  SV_CHECK(launch_accept_sample(a, st));
   SV_CHECK(launch_sample(a.jobs, B, p.V, invT, at<float>(ws, p.o_sums), out->emitted, sync + 1, sync, fin, st));
   return SV_OK;
 }
@@ -386,6 +402,7 @@ SV_API int spec_verify_scheduled(const sv_weights *w, const uint16_t *h, const u
   g.logits = logits_t; g.ldl = p.V;
   g.parts = at<StatPart>(ws, p.o_parts); g.nslots = p.lm.nslots;
   g.invT = invT; g.want_s = 1;
+  int32_t *sync = at<int32_t>(ws, p.o_sync);
   SV_CHECK(run_gemm(p.lm, g, EPI_LOGITS, st));
   // S6-S9
   AcceptArgs a = {};
@@ -397,11 +414,15 @@ SV_API int spec_verify_scheduled(const sv_weights *w, const uint16_t *h, const u
   a.accepted_len = out->accepted_len; a.emitted = out->emitted;
   a.jobs = at<SampleJob>(ws, p.o_jobs);
   a.dev_status = out->dev_status; a.diag = out->diag;
-  int32_t *sync = at<int32_t>(ws, p.o_sync);
   a.done_cnt = sync; a.job_cnt = sync + 1;
-  SV_CHECK(launch_accept_sample(a, st));
   const FinalizeArgs fin{out->accepted_len, vlen, B, Kmax, out->tau, out->counters};
-  SV_CHECK(launch_sample(a.jobs, B, p.V, invT, at<float>(ws, p.o_sums), out->emitted, sync + 1, sync, fin, st));
+  if (p.small_tail) {
+    SV_CHECK(launch_tail_small(a, at<float>(ws, p.o_sums), at<float>(ws, p.o_lse), at<StatPart>(ws, p.o_cand), fin,
+                               st));
+  } else {
+    SV_CHECK(launch_accept_sample(a, st));
+    SV_CHECK(launch_sample(a.jobs, B, p.V, invT, at<float>(ws, p.o_sums), out->emitted, sync + 1, sync, fin, st));
+  }
   if (out->logits) SV_CHECK(launch_scatter_logits(logits_t, out->logits, rowmap, mtot, p.budget, p.V, st));
   if (out->hidden && p.d_ff > 0)
     SV_CHECK(launch_scatter_hidden(at<uint16_t>(ws, p.o_y), out->hidden, rowmap, mtot, p.budget, p.d, st));

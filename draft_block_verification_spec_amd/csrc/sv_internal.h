@@ -60,7 +60,8 @@ struct GemmArgs {
   float *partial;
   // zeroed by thread 0 of block 0 before anything else (device status, arrival counter)
   int32_t *status_reset;
-  int32_t *counter_reset;
+  int32_t *counter_reset;  // counter_reset[0 .. counter_reset_n) are zeroed (n >= 1 when set)
+  int counter_reset_n;
   int buf_cols;  // set by the streaming launcher: columns of the per-workgroup output buffer
 };
 
@@ -121,6 +122,11 @@ hipError_t launch_accept_sample(const AcceptArgs &a, hipStream_t st);
 hipError_t launch_accept_greedy(const AcceptArgs &a, hipStream_t st);
 
 int sample_chunks(int V);
+// Small batches: every candidate final token is drawn speculatively (one block row per
+// (request, position)), then the acceptance scan keeps the one at the first rejection.
+// sums [B*(K+1)*C*2], lse_buf [2*B*(K+1)], rowst [2*B*(K+1)].
+hipError_t launch_tail_small(const AcceptArgs &a, float *sums, float *lse_buf, StatPart *rowst,
+                             const FinalizeArgs &fin, hipStream_t st);
 hipError_t launch_sample(const SampleJob *jobs, int njobs, int V, float invT, float *chunk_sums,
                          int32_t *out, int32_t *job_cnt, int32_t *done_cnt, const FinalizeArgs &fin,
                          hipStream_t st);
