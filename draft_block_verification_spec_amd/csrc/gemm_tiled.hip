@@ -2,38 +2,80 @@
 //
 // Once B*(K+1) rows share each weight read the verification pass stops being
 // bound by HBM and becomes compute-bound (Wildberries page, "A bit of theory",
-// Statement 3: under load the step time grows with B*(K+1)).  This kernel tiles
-// BM x BN outputs per 256-thread workgroup (2 x 2 waves), stages 64-wide k slices
-// of both operands through double-buffered LDS (rows padded by 16 bytes so the
-// 128-bit operand reads are bank-conflict free) and issues
-// v_mfma_f32_32x32x16_bf16 on 32x32 blocks.  Workgroups are mapped XCD-major so
-// the row tiles that share a weight tile run on one XCD and share its L2.
-// Split-K writes fp32 partials that a second kernel reduces in a fixed order.
+// Statement 3: under load the step time grows with B*(K+1)).  Each 256-thread
+// workgroup (2 x 2 waves) owns a BM x BN output tile and walks k in 64-wide
+// slices.  Both operand slices travel from global memory straight into LDS with
+// global_load_lds_dwordx4 (no staging registers), NS slices deep, so the loads of
+// future slices run under the MFMAs of the current one.  Inside a row the sixteen-
+// byte chunks are XOR-swizzled so the 128-bit operand reads of
+// v_mfma_f32_32x32x16_bf16 hit distinct banks.  The LDS reads of the next k step,
+// and at slice boundaries the global->LDS loads of a future slice, are interleaved
+// one per MFMA.  Workgroups are mapped XCD-major so the row tiles that share a
+// weight tile run on one XCD and share its L2.  Split-K writes fp32 partials that a
+// second kernel reduces in a fixed order.
 #include "sv_device.h"
 
 namespace sv {
 
 namespace {
 
-constexpr int BK = 64;
-constexpr int LDK = BK + 8;
+typedef __attribute__((address_space(3))) void *lds_ptr;
+
+constexpr int BK = 64;         // k-slice depth
+constexpr int RB = BK * 2;     // bytes per tile row of a slice
+constexpr int CPR = BK / 8;    // 16-byte chunks per row
+constexpr int RPI = 64 / CPR;  // rows covered by one wave-wide 1 KB load
+
+// Row r's logical chunk c sits at chunk c ^ swz(r): sixteen consecutive rows read at
+// one logical chunk then cover all 64 banks once.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & (CPR - 1); }
+
+// 16 bytes per lane from global memory into LDS: lane l writes bytes
+// [16 l, 16 l + 16) after the wave-uniform LDS address.
+__device__ __forceinline__ void dma16(const void *g, void *lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr)lds, 16, 0, 0);
+}
+
+// Read one accumulator out of its AGPR where it is used, so the compiler does not
+// copy every accumulator to VGPRs at once after the main loop.
+__device__ __forceinline__ float agpr_read(float x) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(x));
+  return v;
+}
+
+// s_waitcnt vmcnt(N) alone (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+template <int BM, int BN>
+constexpr int stages() { return 2; }
+template <int BM, int BN>
+constexpr int waves_per_eu() { return BM * BN >= 256 * 256 ? 1 : 2; }
 
 // PAIR: the weight rows of a tile are [32 gate | 32 up] groups of the same outputs.
 template <int BM, int BN, int EPI, bool PAIR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_tiled(const GemmArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_eu<BM, BN>(), waves_per_eu<BM, BN>())))
+void k_tiled(const GemmArgs a) {
+  constexpr int NS = stages<BM, BN>();
+  constexpr int SA = BM * RB, SB = BN * RB, SS = SA + SB;  // bytes of one slice
+  constexpr int IA = BM / RPI / 4, IB = BN / RPI / 4;      // 1 KB loads per wave per slice
   constexpr int WTM = BM / 2, WTN = BN / 2, TM = WTM / 32, TN = WTN / 32;
-  constexpr int ACH = BM * 8 / 256, BCH = BN * 8 / 256;
-  static_assert(ACH >= 1 && BCH >= 1, "tile too small");
+  constexpr int KS = BK / 16;
+  static_assert(IA >= 1 && IB >= 1, "tile too small");
+  static_assert(KS % 2 == 0, "fragment sets alternate within a slice");
   static_assert(!PAIR || (WTN % 64) == 0, "paired tiles need gate/up block pairs");
-  // operand tiles, double-buffered; reused by the statistics epilogue after the main loop
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDK];
-  uint16_t(*As)[BM * LDK] = reinterpret_cast<uint16_t(*)[BM * LDK]>(smem);
-  uint16_t(*Bs)[BN * LDK] = reinterpret_cast<uint16_t(*)[BN * LDK]>(smem + 2 * BM * LDK);
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * SS];
 
   if (a.status_reset && blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0) *a.status_reset = 0;
   if (a.counter_reset && blockIdx.x == 0 && blockIdx.z == 0)
     for (int i = threadIdx.x; i < max(1, a.counter_reset_n); i += blockDim.x) a.counter_reset[i] = 0;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   int M = a.M;
   if (a.M_dev) M = min(M, *a.M_dev);
@@ -53,49 +95,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int kt1 = min(nkt_total, kt0 + per);
   const int nkt = kt1 > kt0 ? kt1 - kt0 : 0;
 
-  // ---- global -> register staging.  Rows past M (or N) read a clamped valid row;
-  // their results are never stored, and the loads stay free of branches.
-  const uint16_t *arow[ACH];
-  const uint16_t *brow[BCH];
+  // Per-lane global sources of the slice loads.  Load j of this wave fills LDS bytes
+  // [(wave + 4 j) KB, +1 KB) of the operand: rows (wave + 4 j) * RPI + lane / CPR, at
+  // swizzled chunk lane % CPR.  Rows past M (or N) read a clamped valid row; their
+  // results are never stored.
+  const uint16_t *ga[IA];
+  const uint16_t *gb[IB];
   const int mlast = max(M, 1) - 1;
 #pragma unroll
-  for (int i = 0; i < ACH; ++i) {
-    const int q = tid + i * 256, r = q >> 3;
+  for (int j = 0; j < IA; ++j) {
+    const int r = (wave + 4 * j) * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ swz(r);
     const int m = min(m0 + r, mlast);
-    arow[i] = (m < a.m1 ? a.x1 + (long)m * a.ldx1 : a.x2 + (long)(m - a.m1) * a.ldx2) + (q & 7) * 8;
+    ga[j] = (m < a.m1 ? a.x1 + (long)m * a.ldx1 : a.x2 + (long)(m - a.m1) * a.ldx2) + c * 8;
   }
 #pragma unroll
-  for (int i = 0; i < BCH; ++i) {
-    const int q = tid + i * 256, r = q >> 3;
+  for (int j = 0; j < IB; ++j) {
+    const int r = (wave + 4 * j) * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ swz(r);
     if constexpr (PAIR) {
-      // tile columns: 64-wide groups of [32 gate rows | 32 up rows] of the same outputs
       const int p = r >> 6, half = (r >> 5) & 1, rr = r & 31;
       const int n = min((n0 >> 1) + p * 32 + rr, a.N - 1);
-      brow[i] = (half ? a.w2 : a.w) + (long)n * a.K + (q & 7) * 8;
+      gb[j] = (half ? a.w2 : a.w) + (long)n * a.K + c * 8;
     } else {
       const int n = min(n0 + r, a.N - 1);
-      brow[i] = a.w + (long)n * a.K + (q & 7) * 8;
+      gb[j] = a.w + (long)n * a.K + c * 8;
     }
   }
-  u32x4 ra[ACH], rb[BCH];
-  auto gload = [&](int kt) {
-    const long ko = (long)kt * BK;
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) ra[i] = ld16(arow[i] + ko);
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) rb[i] = ld_nt(brow[i] + ko);
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-      const int q = tid + i * 256;
-      *reinterpret_cast<u32x4 *>(&As[buf][(q >> 3) * LDK + (q & 7) * 8]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-      const int q = tid + i * 256;
-      *reinterpret_cast<u32x4 *>(&Bs[buf][(q >> 3) * LDK + (q & 7) * 8]) = rb[i];
-    }
+  // element offset of slice t of this split; past the end it re-reads the last slice
+  auto kofs = [&](int t) -> long { return (long)(kt0 + min(t, nkt - 1)) * BK; };
+  auto issue_one = [&](long ko, uint32_t soff, int g) {
+    uint8_t *sb = smem + soff;
+    if (g < IA) dma16(ga[g] + ko, sb + (wave + 4 * g) * 1024);
+    else dma16(gb[g - IA] + ko, sb + SA + (wave + 4 * (g - IA)) * 1024);
   };
 
   f32x16 acc[TM][TN];
@@ -106,47 +138,71 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  if (nkt > 0) {
-    gload(kt0);
-    sstore(0);
-    __syncthreads();
-  }
-  const int l32 = lane & 31, khalf = (lane >> 5) * 8;
-  for (int t = 0; t < nkt; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < nkt) gload(kt0 + t + 1);
-    // operand fragments are double-buffered in registers: the LDS reads of step
-    // kk+1 are issued before the MFMAs of step kk
-    bf16x8 af[2][TM], bfr[2][TN];
-    auto lfrag = [&](int set, int kk) {
+  const int l32 = lane & 31, hi = lane >> 5;
+  // lane l reads row l%32 of a 32-row block at logical chunk 2 kk + l/32 of k step kk
+  int off[KS];
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[set][i] = *reinterpret_cast<const bf16x8 *>(&As[buf][(wm * WTM + i * 32 + l32) * LDK + kk * 16 + khalf]);
+  for (int kk = 0; kk < KS; ++kk) off[kk] = l32 * RB + (((kk * 2 + hi) ^ swz(l32)) << 4);
+  bf16x8 af[2][TM], bfr[2][TN];
+  auto lfrag_one = [&](int set, uint32_t soff, int kk, int g) {
+    const uint8_t *sb = smem + soff;
+    if (g < TM) af[set][g] = *reinterpret_cast<const bf16x8 *>(sb + (wm * WTM + g * 32) * RB + off[kk]);
+    else bfr[set][g - TM] = *reinterpret_cast<const bf16x8 *>(sb + SA + (wn * WTN + (g - TM) * 32) * RB + off[kk]);
+  };
+  // One k step: TM*TN MFMAs on fragment set `cur`; after MFMA q comes the LDS read of
+  // fragment q of the next step and, at a slice boundary, global->LDS load q.
+  auto step = [&](int cur, uint32_t rsoff, int rkk, bool ld, long ko, uint32_t lsoff) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[set][j] = *reinterpret_cast<const bf16x8 *>(&Bs[buf][(wn * WTN + j * 32 + l32) * LDK + kk * 16 + khalf]);
-    };
-    lfrag(0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int cur = kk & 1;
-      if (kk + 1 < BK / 16) lfrag(cur ^ 1, kk + 1);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
+    for (int q = 0; q < TM * TN; ++q) {
+      const int i = q / TN, j = q % TN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
+      if (ld && q < IA + IB) issue_one(ko, lsoff, q);
+      if (q < TM + TN) lfrag_one(cur ^ 1, rsoff, rkk, q);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (t + 1 < nkt) sstore(buf ^ 1);
-    __syncthreads();
+    if (ld) {  // loads left over when a slice needs more loads than the step has MFMAs
+#pragma unroll
+      for (int g = TM * TN; g < IA + IB; ++g) issue_one(ko, lsoff, g);
+    }
+#pragma unroll
+    for (int g = TM * TN; g < TM + TN; ++g) lfrag_one(cur ^ 1, rsoff, rkk, g);
+  };
+
+  if (nkt > 0) {
+    // prologue: slices 0 .. NS-1 in flight, wait for slice 0
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+#pragma unroll
+      for (int g = 0; g < IA + IB; ++g) issue_one(kofs(s), s * SS, g);
+    }
+    vm_wait<(NS - 1) * (IA + IB)>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int g = 0; g < TM + TN; ++g) lfrag_one(0, 0, 0, g);
+
+    uint32_t scur = 0;
+    for (int t = 0; t < nkt; ++t) {
+      const uint32_t snext = scur + SS == NS * SS ? 0 : scur + SS;
+#pragma unroll
+      for (int kk = 0; kk + 1 < KS; ++kk) step(kk & 1, scur, kk + 1, false, 0, 0);
+      // Slice boundary: every wave has finished reading slice t (its LDS reads are
+      // complete), slice t+1 has landed.  Refill slice t's buffer with slice t+NS and
+      // start reading slice t+1.  After the last slice this reads a stale buffer that
+      // no MFMA consumes.
+      lgkm_wait0();
+      vm_wait<(NS - 2) * (IA + IB)>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      step((KS - 1) & 1, snext, 0, true, kofs(t + NS), scur);
+      scur = snext;
+    }
+    // no load may still be writing LDS when the workgroup leaves
+    vm_wait<0>();
   }
 
   // ---- epilogue.  Lane l of block (i, j) holds column l%32 and, for register r,
   // row (r/4)*8 + (l/32)*4 + r%4 of the 32x32 block.
-  const int rsub = (lane >> 5) * 4;
+  const int rsub = hi * 4;
   if constexpr (EPI == EPI_RAW) {
     float *P = a.partial + (long)z * a.M * Ncols;
 #pragma unroll
@@ -172,7 +228,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
           if (m < M) {
-            const float gv = acc[i][2 * jp][r], uv = acc[i][2 * jp + 1][r];
+            const float gv = agpr_read(acc[i][2 * jp][r]), uv = agpr_read(acc[i][2 * jp + 1][r]);
             const float sg = gv / (1.f + __expf(-gv));
             a.out[(long)m * a.ldo + n] = f32_to_bf16(sg * uv);
           }
@@ -190,47 +246,93 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           const int m = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + rsub + (r & 3);
           if (m < M) {
             const float hv = bf16_to_f32(a.resid[(long)m * a.ldr + n]);
-            a.out[(long)m * a.ldo + n] = f32_to_bf16(hv + acc[i][j][r]);
+            a.out[(long)m * a.ldo + n] = f32_to_bf16(hv + agpr_read(acc[i][j][r]));
           }
         }
       }
   } else {  // EPI_LOGITS
-    // Logits go out straight from the accumulators (32 consecutive columns per
-    // register).  For the row statistics each wave stages one 32-row group of its
-    // tile in LDS at a time (row stride padded to 65 floats), then lane l scans row
-    // l%32 over half l/32 of the wave's columns in increasing order and the two
-    // halves are merged with one shuffle.
+    // Logits go out straight from the accumulators.  Row statistics are reduced in
+    // registers: each lane folds its TN columns of a row (in increasing column
+    // order), then a reduce-scatter over the 32 lanes that share a row group halves
+    // the rows per lane at each step, until lanes 2r and 2r+1 hold row r's
+    // statistics over all of the wave's columns.
     const bool ws = a.want_s != 0;
+    const float invT = a.invT;
     const int slot = tni * 2 + wn;
-    constexpr int SROW = WTN + 1;
-    static_assert(4 * 32 * SROW * 4 <= 2 * (BM + BN) * LDK * 2, "staging area too small");
-    __syncthreads();
-    float *stage = reinterpret_cast<float *>(smem) + wave * (32 * SROW);
+    const int nb = n0 + wn * WTN + l32;
+    if (a.logits) {
+      // row bases are wave-uniform; the lane part (row half, column) is an offset
+      const long lane_off = (long)rsub * a.ldl + nb;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WTN + j * 32 + l32;
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int rr = (r >> 2) * 8 + rsub + (r & 3);
-          const int m = m0 + wm * WTM + i * 32 + rr;
-          stage[rr * SROW + j * 32 + l32] = acc[i][j][r];
-          if (a.logits && m < M && n < a.N) a.logits[(long)m * a.ldl + n] = acc[i][j][r];
+          const int mrow = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + (r & 3);
+          float *rowbase = a.logits + (long)mrow * a.ldl;
+          if (mrow + rsub < M) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              if (nb + j * 32 < a.N) rowbase[lane_off + j * 32] = acc[i][j][r];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      auto fold = [&](int r) {
+        float zv[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) zv[j] = (nb + j * 32 < a.N) ? agpr_read(acc[i][j][r]) : -INFINITY;
+        float b1 = zv[0];
+        int j1 = 0;
+#pragma unroll
+        for (int j = 1; j < TN; ++j)
+          if (zv[j] > b1) {
+            b1 = zv[j];
+            j1 = j;
+          }
+        float b2 = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) b2 = fmaxf(b2, j == j1 ? -INFINITY : zv[j]);
+        float sum = 0.f;
+        if (ws && b1 > -INFINITY) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) sum += __expf((zv[j] - b1) * invT);
+        }
+        StatPart q;
+        q.b1 = b1;
+        q.b2 = b2;
+        q.s = sum;
+        q.i1 = b1 > -INFINITY ? nb + j1 * 32 : 0x7fffffff;
+        return q;
+      };
+      // first level straight from the folds: lanes with bit 4 set keep rows 8..15
+      StatPart p[8];
+      {
+        const bool up = (lane & 16) != 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const StatPart lo = fold(k), hi8 = fold(8 + k);
+          const StatPart keep = up ? hi8 : lo, send = up ? lo : hi8;
+          p[k] = stat_merge(keep, stat_shfl_xor(send, 16), invT, ws);
         }
       }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are done
-      const int rr = l32, half = lane >> 5;
-      const int m = m0 + wm * WTM + i * 32 + rr;
-      StatPart st = stat_empty();
-      const int c0 = half * (WTN / 2);
-      for (int c = 0; c < WTN / 2; ++c) {
-        const int n = n0 + wn * WTN + c0 + c;
-        if (n < a.N) stat_push(st, stage[rr * SROW + c0 + c], n, a.invT, ws);
+#pragma unroll
+      for (int lvl = 1; lvl < 4; ++lvl) {
+        const int half = 8 >> lvl, mask = 16 >> lvl;
+        const bool up = (lane & mask) != 0;
+#pragma unroll
+        for (int k = 0; k < half; ++k) {
+          const StatPart keep = up ? p[half + k] : p[k];
+          const StatPart send = up ? p[k] : p[half + k];
+          p[k] = stat_merge(keep, stat_shfl_xor(send, mask), invT, ws);
+        }
       }
-      st = stat_merge(st, stat_shfl_xor(st, 32), a.invT, ws);
-      if (half == 0 && m < M) a.parts[(long)m * a.nslots + slot] = st;
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next group
+      const StatPart st = stat_merge(p[0], stat_shfl_xor(p[0], 1), invT, ws);
+      const int rr = l32 >> 1;
+      const int m = m0 + wm * WTM + i * 32 + (rr >> 2) * 8 + rsub + (rr & 3);
+      if ((lane & 1) == 0 && m < M) a.parts[(long)m * a.nslots + slot] = st;
     }
   }
 }
