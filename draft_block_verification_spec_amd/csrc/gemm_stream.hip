@@ -11,10 +11,15 @@
 //  * the 8 waves split the reduction: wave w covers 16 MFMA k-steps (512 values)
 //    of every 4096-wide chunk of K, so each wave keeps its slice of X (the MFMA A
 //    operand, 16 rows per block) in VGPRs for the whole sweep when K <= 4096;
-//  * W tiles feed the B operand of v_mfma_f32_16x16x32_bf16 straight from global
-//    memory (lane l reads row l%16, 8 consecutive k at 8*(l/16)); each of the 16
-//    loads of a step is re-issued for the next step as soon as its MFMA has been
-//    issued, so about 16 KiB per wave stay in flight;
+//  * W tiles feed the B operand of v_mfma_f32_16x16x32_bf16.  HBM streams fastest
+//    when every row is read in runs of 256 bytes or more, while the MFMA wants each
+//    lane on its own row (16 rows x 64 bytes per load).  So when K is a whole number
+//    of 4096-value chunks each wave load reads 4 rows x 256 contiguous bytes, and a
+//    private 4 KiB LDS slot per wave turns 4 such loads (16 rows x 128 values) into
+//    the fragments of 4 k-steps: one 128-bit LDS write and one read per lane and
+//    load, XOR-swizzled so both are free of bank conflicts, no barriers.  Each of
+//    the 16 loads of a step is re-issued for the next step as soon as its data is in
+//    LDS, so about 16 KiB per wave stay in flight;
 //  * the 8 partial accumulators of a tile are summed in a fixed order through LDS
 //    (deterministic), then the epilogue runs: fp32 logits + running per-row
 //    statistics, SwiGLU with paired gate/up rows, or residual add, bf16 output.
@@ -43,7 +48,15 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
   constexpr bool RELOAD_A = KM != 1;  // activations change with the chunk
   constexpr bool PAIR = (EPI == EPI_SWIGLU);
   constexpr int NACC = PAIR ? 2 * MB : MB;
+  constexpr int NW = PAIR ? 2 : 1;  // weight streams
+  // The LM head reads far more weight bytes than the caches hold: nontemporal loads
+  // keep it from evicting anything (measured faster); the smaller MLP weights use
+  // ordinary loads (measured faster there).
+  constexpr bool NT = EPI == EPI_LOGITS;
+  auto ldw = [](const uint16_t *p) -> bf16x8 { return as_bf16x8(NT ? ld_nt(p) : ld16(p)); };
   __shared__ float red[2][WAVES * NACC * 4 * 64];
+  // per-wave reshaping slots (whole-chunk K only): [wave][stream][16 rows x 256 bytes]
+  __shared__ __attribute__((aligned(16))) uint8_t tbuf[FULL ? WAVES * NW * 4096 : 16];
   // Outputs of the workgroup's whole column range are kept in LDS and written once at
   // the end (when a.buf_cols > 0): stores inside the streaming loop would share the
   // vector-memory counter with the weight loads and stall them.
@@ -85,10 +98,27 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
       return zero8;
     }
   };
+  // Weight load s of a step.  Whole chunks: group g = s/4 holds values [128 g, 128 g + 128)
+  // of the wave's 512 in every row, load s%4 of the group rows 4 (s%4) + l/16, 16 bytes at
+  // 16 (l%16) of the 256-byte run.  General K: the MFMA layout straight from memory.
   auto wptr = [&](const uint16_t *base, int tile, int chunk, int s) -> const uint16_t * {
-    const int ks = min(kstep(chunk, s), nks - 1);
-    const int n = min(tile * 16 + r16, N - 1);
-    return base + (long)n * K + ks * 32 + kq;
+    if constexpr (FULL) {
+      const int n = min(tile * 16 + 4 * (s & 3) + (lane >> 4), N - 1);
+      return base + (long)n * K + chunk * (CHUNK_KS * 32) + wave * (STEPS * 32) + (s >> 2) * 128 + r16 * 8;
+    } else {
+      const int ks = min(kstep(chunk, s), nks - 1);
+      const int n = min(tile * 16 + r16, N - 1);
+      return base + (long)n * K + ks * 32 + kq;
+    }
+  };
+  // LDS reshaping (whole chunks): row r's 16-byte chunk c of a group sits at chunk c ^ r.
+  uint8_t *tw = tbuf + (FULL ? wave * NW * 4096 : 0);
+  auto put4 = [&](uint8_t *slot, int i, bf16x8 v) {  // load i of a group, this lane's 16 bytes
+    const int r = 4 * i + (lane >> 4);
+    *reinterpret_cast<bf16x8 *>(slot + r * 256 + ((r16 ^ r) << 4)) = v;
+  };
+  auto frag = [&](const uint8_t *slot, int j) -> bf16x8 {  // B operand of k-step j of a group
+    return *reinterpret_cast<const bf16x8 *>(slot + r16 * 256 + ((((4 * j) + (lane >> 4)) ^ r16) << 4));
   };
 
   // statistics of the row this thread reduces (EPI_LOGITS)
@@ -106,8 +136,8 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
       for (int mb = 0; mb < MB; ++mb) A[mb][s] = load_a(0, s, mb);
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
-      Wr[s] = as_bf16x8(ld16(wptr(a.w, t_begin, 0, s)));
-      if constexpr (PAIR) Ur[s] = as_bf16x8(ld16(wptr(a.w2, t_begin, 0, s)));
+      Wr[s] = ldw(wptr(a.w, t_begin, 0, s));
+      if constexpr (PAIR) Ur[s] = ldw(wptr(a.w2, t_begin, 0, s));
     }
   }
 
@@ -125,6 +155,44 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
 #pragma unroll
       for (int q = 0; q < NACC; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    if constexpr (FULL) {
+#pragma unroll
+      for (int g = 0; g < STEPS / 4; ++g) {
+        // the group's 4 loads (per stream) into this wave's slot, then refill them
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          put4(tw, i, Wr[4 * g + i]);
+          if constexpr (PAIR) put4(tw + 4096, i, Ur[4 * g + i]);
+        }
+        if constexpr (PF) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            Wr[4 * g + i] = ldw(wptr(a.w, ntile, nc, 4 * g + i));
+            if constexpr (PAIR) Ur[4 * g + i] = ldw(wptr(a.w2, ntile, nc, 4 * g + i));
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int ks = 4 * g + j;
+          const bf16x8 bw = frag(tw, j);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            if constexpr (PAIR) {
+              const bf16x8 bu = frag(tw + 4096, j);
+              acc[2 * mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][ks], bw, acc[2 * mb], 0, 0, 0);
+              acc[2 * mb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][ks], bu, acc[2 * mb + 1], 0, 0, 0);
+            } else {
+              acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][ks], bw, acc[mb], 0, 0, 0);
+            }
+          }
+          if constexpr (PF && RELOAD_A) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) A[mb][ks] = load_a(nc, ks, mb);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
 #pragma unroll
@@ -138,8 +206,8 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
         }
       }
       if constexpr (PF) {
-        Wr[s] = as_bf16x8(ld16(wptr(a.w, ntile, nc, s)));
-        if constexpr (PAIR) Ur[s] = as_bf16x8(ld16(wptr(a.w2, ntile, nc, s)));
+        Wr[s] = ldw(wptr(a.w, ntile, nc, s));
+        if constexpr (PAIR) Ur[s] = ldw(wptr(a.w2, ntile, nc, s));
         if constexpr (RELOAD_A) {
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) A[mb][s] = load_a(nc, s, mb);
@@ -147,6 +215,7 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
       }
       // keep "use slot s, refill slot s" in program order so loads stay spread over the step
       __builtin_amdgcn_sched_barrier(0);
+    }
     }
   };
   for (int stp = 0; stp < nsteps; ++stp) {
@@ -231,22 +300,35 @@ int stream_grid(const GemmArgs &a, int epi) {
   return ntiles < num_cus() ? ntiles : num_cus();
 }
 
-// Output buffer per workgroup: up to 32 rows x its column range (fp32 logits or bf16).
+// Output buffer per workgroup: up to 32 rows x its column range (fp32 logits or bf16),
+// in the LDS left over by the kernel's static buffers (160 KiB per workgroup on gfx950).
+constexpr size_t LDS_PER_CU = 160 * 1024;
 constexpr size_t OBUF_MAX = 96 * 1024;
 
 template <int MB, int EPI, int KM>
+constexpr size_t stream_static_lds() {
+  constexpr size_t nacc = EPI == EPI_SWIGLU ? 2 * MB : MB;
+  constexpr size_t red = 2 * WAVES * nacc * 4 * 64 * sizeof(float);
+  constexpr size_t tb = KM != 0 ? (size_t)WAVES * (EPI == EPI_SWIGLU ? 2 : 1) * 4096 : 16;
+  return red + tb;
+}
+
+template <int MB, int EPI, int KM>
 hipError_t launch_one(GemmArgs a, int grid, hipStream_t st) {
+  constexpr size_t dyn_max = LDS_PER_CU - stream_static_lds<MB, EPI, KM>() < OBUF_MAX
+                                 ? LDS_PER_CU - stream_static_lds<MB, EPI, KM>()
+                                 : OBUF_MAX;
   const int ntiles = (a.N + 15) / 16;
   const int cols = 16 * ((ntiles + grid - 1) / grid);
   const size_t esz = EPI == EPI_LOGITS ? 4 : 2;
   size_t shm = (size_t)MB * 16 * cols * esz;
   a.buf_cols = 0;
-  if (shm <= OBUF_MAX && (EPI != EPI_LOGITS || a.logits)) {
+  if (shm <= dyn_max && (EPI != EPI_LOGITS || a.logits)) {
     a.buf_cols = cols;
     static bool attr_set = false;  // one instantiation per (MB, EPI, KM)
     if (!attr_set) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_stream<MB, EPI, KM>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)OBUF_MAX);
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_max);
       if (e != hipSuccess) return e;
       attr_set = true;
     }

@@ -53,11 +53,16 @@ Gemm choose(int M, int N, int K, int epi) {
   }
   g.stream = false;
   g.bm = M <= 64 ? 64 : (M <= 128 ? 128 : 256);
-  g.bn = M > 256 ? 256 : 128;
+  g.bn = (epi == EPI_LOGITS && M > 256) ? 256 : 128;
+  // SwiGLU pairs fill the chip better with 128-row tiles, two workgroups per CU
+  if (epi == EPI_SWIGLU && M > 128) g.bm = 128;
   const int Ncols = epi == EPI_SWIGLU ? 2 * N : N;
   const long tiles = (long)((M + g.bm - 1) / g.bm) * ((Ncols + g.bn - 1) / g.bn);
-  if (epi != EPI_LOGITS && tiles < 2L * num_cus()) {
-    const int want = (int)((2L * num_cus() + tiles - 1) / tiles);
+  // resident workgroups per CU, set by the LDS of the two-slice pipeline
+  const int per_cu = g.bm * g.bn >= 256 * 128 ? 1 : (g.bm == 128 ? 2 : 3);
+  const long slots = (long)per_cu * num_cus();
+  if (epi != EPI_LOGITS && tiles < slots) {
+    const int want = (int)((slots + tiles - 1) / tiles);
     int maxs = (K / 64) / 4;
     if (maxs < 1) maxs = 1;
     g.splits = want < maxs ? want : maxs;
