@@ -79,7 +79,7 @@ struct Plan {
   Gemm gu, dn, lm, s1;
   size_t o_a = 0, o_y = 0, o_part = 0, o_parts = 0, o_parts_d = 0, o_logits = 0, o_logits_d = 0,
          o_jobs = 0, o_sums = 0, o_conf = 0, o_vlen = 0, o_rowoff = 0, o_rowmap = 0, o_mtot = 0,
-         o_hp = 0, o_sync = 0, o_cand = 0, o_lse = 0, total = 0;
+         o_hp = 0, o_sync = 0, o_lse = 0, total = 0;
   bool small_tail = false;  // speculative per-position sampling + acceptance in one kernel
 };
 
@@ -143,10 +143,7 @@ bool make_plan(int mode, int B, int K, const sv_weights *w, int budget, Plan &p)
     p.o_logits = take(sizeof(float) * (size_t)p.M_lm * V);
     p.o_jobs = take(sizeof(SampleJob) * (size_t)B);
     p.o_sums = take(sizeof(float) * 2 * (size_t)(p.small_tail ? NJ : B) * sample_chunks(V));
-    if (p.small_tail) {
-      p.o_cand = take(sizeof(StatPart) * 2 * (size_t)NJ);  // per-candidate row statistics
-      p.o_lse = take(sizeof(float) * 2 * (size_t)NJ);
-    }
+    if (p.small_tail) p.o_lse = take(sizeof(float) * 3 * (size_t)NJ);  // normalisers + flags
   }
   // arrival counters: [0] call-wide, [1 + i] per request (or per candidate job)
   p.o_sync = take(sizeof(int32_t) * (size_t)(1 + (p.small_tail ? NJ : B)));
@@ -336,8 +333,7 @@ SV_API int spec_verify_sample(const sv_weights *w, const uint16_t *h, const uint
   a.done_cnt = sync; a.job_cnt = sync + 1;
   const FinalizeArgs fin{out->accepted_len, nullptr, B, K, out->tau, out->counters};
   if (p.small_tail) {
-    SV_CHECK(launch_tail_small(a, at<float>(ws, p.o_sums), at<float>(ws, p.o_lse), at<StatPart>(ws, p.o_cand), fin,
-                               st));
+    SV_CHECK(launch_tail_small(a, at<float>(ws, p.o_sums), at<float>(ws, p.o_lse), fin, st));
     return SV_OK;
   }
   SV_CHECK(launch_accept_sample(a, st));
@@ -422,8 +418,7 @@ SV_API int spec_verify_scheduled(const sv_weights *w, const uint16_t *h, const u
   a.done_cnt = sync; a.job_cnt = sync + 1;
   const FinalizeArgs fin{out->accepted_len, vlen, B, Kmax, out->tau, out->counters};
   if (p.small_tail) {
-    SV_CHECK(launch_tail_small(a, at<float>(ws, p.o_sums), at<float>(ws, p.o_lse), at<StatPart>(ws, p.o_cand), fin,
-                               st));
+    SV_CHECK(launch_tail_small(a, at<float>(ws, p.o_sums), at<float>(ws, p.o_lse), fin, st));
   } else {
     SV_CHECK(launch_accept_sample(a, st));
     SV_CHECK(launch_sample(a.jobs, B, p.V, invT, at<float>(ws, p.o_sums), out->emitted, sync + 1, sync, fin, st));

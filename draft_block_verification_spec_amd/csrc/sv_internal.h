@@ -122,11 +122,12 @@ hipError_t launch_accept_sample(const AcceptArgs &a, hipStream_t st);
 hipError_t launch_accept_greedy(const AcceptArgs &a, hipStream_t st);
 
 int sample_chunks(int V);
-// Small batches: every candidate final token is drawn speculatively (one block row per
-// (request, position)), then the acceptance scan keeps the one at the first rejection.
-// sums [B*(K+1)*C*2], lse_buf [2*B*(K+1)], rowst [2*B*(K+1)].
-hipError_t launch_tail_small(const AcceptArgs &a, float *sums, float *lse_buf, StatPart *rowst,
-                             const FinalizeArgs &fin, hipStream_t st);
+// Small batches: the draw for every candidate first-rejection position is prepared at
+// once, then the acceptance scan keeps the one at the first rejection.
+// sums [B*(K+1)*C*2], lse_buf [3*B*(K+1)] (two normalisers per candidate, then an int
+// acceptance flag per candidate).
+hipError_t launch_tail_small(const AcceptArgs &a, float *sums, float *lse_buf, const FinalizeArgs &fin,
+                             hipStream_t st);
 hipError_t launch_sample(const SampleJob *jobs, int njobs, int V, float invT, float *chunk_sums,
                          int32_t *out, int32_t *job_cnt, int32_t *done_cnt, const FinalizeArgs &fin,
                          hipStream_t st);

@@ -400,263 +400,299 @@ __device__ StatPart block_merge_row(const StatPart *parts, int nslots, float inv
 }
 
 // ---- small-batch tail.  For every request b and every possible first rejection
-// point j = 0..K_b a block row draws, with the request's final coin, the token that
-// would be emitted there: from the normalised max(0, p_j - q_j) (p_j if that is all
-// zero) for j < K_b, from p_{K_b} for j = K_b.  That is the same draw as after the
-// acceptance scan, made for every j at once so the scan and the sampling do not
-// wait on each other.  Two kernels, no inter-block signalling: tail1 merges the row
-// statistics and sums each chunk's weights; tail2 (one block per candidate) locates
-// its token, runs the acceptance scan of its request and, if it is the candidate at
-// the first rejection, writes the request's outputs.
-__global__ __launch_bounds__(NT) void k_tail1(const AcceptArgs a, int chunk, float *sums, float *lse_buf,
-                                              StatPart *rowst) {
-  __shared__ float red[NT / 64];
+// point j = 0..K_b the token that would be emitted there is drawn with the request's
+// final coin: from the normalised max(0, p_j - q_j) (p_j if that is all zero) for
+// j < K_b, from p_{K_b} for j = K_b.  That is the same draw as after the acceptance
+// scan, prepared for every j at once so the scan and the sampling do not wait on each
+// other.  Two kernels, no inter-block signalling (a device-scope release per block
+// costs more than the kernel boundary it would save):
+//  * tail1, blocks (chunk group, candidate): merges the row statistics of the
+//    candidate's rows and sums the sampling weights over SUBS chunks of V; the first
+//    chunk group also decides acceptance of draft token j and writes the row
+//    diagnostics;
+//  * tail2, one block per request: the acceptance scan over the flags, then the draw
+//    of the candidate at the first rejection from its chunk sums and chunk; block 0
+//    also does the call-wide bookkeeping.
+constexpr int SUBS = 4;  // sampling chunks per tail1 block
+// acceptance flag bits
+constexpr int FLAG_ACCEPT = 1, FLAG_BAD_TOKEN = 2, FLAG_NONFINITE = 4;
+
+// Acceptance scan of one request over the flags (one wave): A = first rejected position
+// (K_b if none); bad = union of the problem bits of positions 0..K_b.
+__device__ void scan_flags(const int32_t *fl, int Kb, int &A, int &bad) {
+  const int lane = threadIdx.x & 63;
+  A = Kb;
+  bool rej = false;
+  int badm = 0;
+  for (int base = 0; base <= Kb; base += 64) {
+    const int jj = base + lane;
+    const int f = jj <= Kb ? fl[jj] : FLAG_ACCEPT;
+    badm |= f & (FLAG_BAD_TOKEN | FLAG_NONFINITE);
+    const unsigned long long rm = __ballot(jj < Kb && !(f & FLAG_ACCEPT));
+    if (!rej && rm) {
+      A = base + __ffsll((long long)rm) - 1;
+      rej = true;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) badm |= __shfl_xor(badm, off);
+  bad = badm;
+}
+
+// VEC: V and the chunk length are multiples of 4, so each thread reads 16-byte pieces.
+template <bool VEC>
+__global__ __launch_bounds__(NT) void k_tail1(const AcceptArgs a, int chunk, int C, float *sums, float *lse_buf) {
+  __shared__ float red[NT / 64][2 * SUBS];
   __shared__ StatPart reds[NT / 64];
   const int Kmax = a.K, NJ = a.B * (Kmax + 1);
-  const int job = blockIdx.y, c = blockIdx.x, C = gridDim.x, t = threadIdx.x;
+  int32_t *flags = reinterpret_cast<int32_t *>(lse_buf + 2 * NJ);
+  const int job = blockIdx.y, cb = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int b = job / (Kmax + 1), j = job % (Kmax + 1);
   const int Kb = a.verify_len ? a.verify_len[b] : Kmax;
   if (j > Kb) return;
   const long trow0 = a.row_off ? a.row_off[b] : (long)b * (Kmax + 1);
   const long drow0 = (long)b * Kmax;
   const bool resid_row = j < Kb;
-  const StatPart st_t = block_merge_row(a.parts_t + (trow0 + j) * a.nslots_t, a.nslots_t, a.invT, true, reds);
-  StatPart st_d = stat_empty();
-  if (resid_row) st_d = block_merge_row(a.parts_d + (drow0 + j) * a.nslots_d, a.nslots_d, a.invT, true, reds);
-  const float lse1 = st_t.b1 * a.invT + __logf(st_t.s);
-  const float lse2 = resid_row ? st_d.b1 * a.invT + __logf(st_d.s) : 0.f;
-  const float *z1 = a.logits_t + (trow0 + j) * (long)a.V;
-  const float *z2 = resid_row ? a.logits_d + (drow0 + j) * (long)a.V : nullptr;
-  const int v0 = c * chunk, v1 = min(a.V, v0 + chunk);
-  float sr = 0.f, sp = 0.f;
-  for (int v = v0 + t; v < v1; v += NT) {
-    const float p = __expf(z1[v] * a.invT - lse1);
-    sp += p;
-    if (z2) sr += fmaxf(p - __expf(z2[v] * a.invT - lse2), 0.f);
-  }
-  const float tr = block_sum(sr, red);
-  const float tp = block_sum(sp, red);
-  if (t == 0) {
-    sums[((long)job * C + c) * 2 + 0] = tr;
-    sums[((long)job * C + c) * 2 + 1] = tp;
-    if (c == 0) {
+  const float invT = a.invT;
+  {
+    const float *z1 = a.logits_t + (trow0 + j) * (long)a.V;
+    const float *z2 = resid_row ? a.logits_d + (drow0 + j) * (long)a.V : nullptr;
+    // this thread's logits of the block's chunks (chunk <= NT * PER), loaded before the
+    // row statistics are merged so the memory round trips overlap
+    auto tok = [&](int q, int i) {
+      const int v0 = (cb * SUBS + q) * chunk;
+      return VEC ? v0 + (i >> 2) * (4 * NT) + 4 * t + (i & 3) : v0 + t + i * NT;
+    };
+    float zt[SUBS][PER], zd[SUBS][PER];
+#pragma unroll
+    for (int q = 0; q < SUBS; ++q) {
+      const int v1 = min(a.V, (cb * SUBS + q) * chunk + chunk);
+      if constexpr (VEC) {
+#pragma unroll
+        for (int i = 0; i < PER; i += 4) {
+          const int v = tok(q, i);
+          const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+          const f32x4 x = v < v1 ? *reinterpret_cast<const f32x4 *>(z1 + v) : zero4;
+          const f32x4 y = (z2 && v < v1) ? *reinterpret_cast<const f32x4 *>(z2 + v) : zero4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            zt[q][i + e] = x[e];
+            zd[q][i + e] = y[e];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const int v = tok(q, i);
+          zt[q][i] = v < v1 ? z1[v] : 0.f;
+          zd[q][i] = (z2 && v < v1) ? z2[v] : 0.f;
+        }
+      }
+    }
+    const StatPart st_t = block_merge_row(a.parts_t + (trow0 + j) * a.nslots_t, a.nslots_t, invT, true, reds);
+    StatPart st_d = stat_empty();
+    if (resid_row) st_d = block_merge_row(a.parts_d + (drow0 + j) * a.nslots_d, a.nslots_d, invT, true, reds);
+    const float lse1 = st_t.b1 * invT + __logf(st_t.s);
+    const float lse2 = resid_row ? st_d.b1 * invT + __logf(st_d.s) : 0.f;
+    // per chunk: sum of max(0, p - q) and of p over this thread's tokens (token order)
+    float part[2 * SUBS];
+#pragma unroll
+    for (int q = 0; q < SUBS; ++q) {
+      const int v1 = min(a.V, (cb * SUBS + q) * chunk + chunk);
+      float sr = 0.f, sp = 0.f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        if (tok(q, i) < v1) {
+          const float p = __expf(zt[q][i] * invT - lse1);
+          sp += p;
+          if (z2) sr += fmaxf(p - __expf(zd[q][i] * invT - lse2), 0.f);
+        }
+      }
+      part[2 * q] = sr;
+      part[2 * q + 1] = sp;
+    }
+    // block sums of the 2*SUBS values: wave butterflies, then waves in a fixed order
+#pragma unroll
+    for (int k = 0; k < 2 * SUBS; ++k) {
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) part[k] += __shfl_xor(part[k], off);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int k = 0; k < 2 * SUBS; ++k) red[wave][k] = part[k];
+    }
+    __syncthreads();
+    if (t < 2 * SUBS) {
+      const int c = cb * SUBS + (t >> 1);
+      float tot = 0.f;
+      for (int w = 0; w < NT / 64; ++w) tot += red[w][t];
+      if (c < C) sums[((long)job * C + c) * 2 + (t & 1)] = tot;
+    }
+    if (cb == 0 && t == 0) {
+      // first chunk group: normalisers, acceptance of draft token j, diagnostics
       lse_buf[job] = lse1;
       lse_buf[NJ + job] = lse2;
-      rowst[2 * job] = st_t;
-      rowst[2 * job + 1] = st_d;
+      int flag = 0;
+      if (!isfinite(lse1) || (resid_row && !isfinite(lse2))) flag |= FLAG_NONFINITE;
+      if (resid_row) {
+        const int x = a.draft[drow0 + j];
+        if (x < 0 || x >= a.V) {
+          flag |= FLAG_BAD_TOKEN;
+        } else {
+          const float zx = z1[x], zdx = z2[x];
+          const float lpt = zx * invT - lse1;
+          const float lqd = zdx * invT - lse2;
+          const float ratio = __expf(lpt - lqd);
+          if (a.u[(long)b * (Kmax + 1) + j] < ratio) flag |= FLAG_ACCEPT;
+          if (a.diag) {
+            float *dt = a.diag + ((long)b * (Kmax + 1) + j) * SV_DIAG_COLS;
+            dt[4] = zx; dt[5] = __expf(lpt); dt[6] = ratio;
+            float *dd = a.diag + ((long)a.B * (Kmax + 1) + drow0 + j) * SV_DIAG_COLS;
+            dd[4] = zdx; dd[5] = __expf(lqd);
+          }
+        }
+      }
+      flags[job] = flag;
+      if (a.diag) {
+        float *dg = a.diag + ((long)b * (Kmax + 1) + j) * SV_DIAG_COLS;
+        dg[0] = lse1; dg[1] = (float)st_t.i1; dg[2] = st_t.b1 - st_t.b2; dg[3] = st_t.b1; dg[7] = 0.f;
+        if (resid_row) {
+          float *dd = a.diag + ((long)a.B * (Kmax + 1) + drow0 + j) * SV_DIAG_COLS;
+          dd[0] = lse2; dd[1] = (float)st_d.i1; dd[2] = st_d.b1 - st_d.b2; dd[3] = st_d.b1;
+          dd[6] = 1.f / st_d.s; dd[7] = 0.f;
+        }
+      }
     }
   }
 }
 
 __global__ __launch_bounds__(NT) void k_tail2(const AcceptArgs a, int chunk, int C, const float *sums,
-                                              const float *lse_buf, const StatPart *rowst, FinalizeArgs fin) {
-  __shared__ float red[NT / 64];
+                                              const float *lse_buf, FinalizeArgs fin) {
+  __shared__ float redf[NT / 64];
   __shared__ int redi[NT / 64];
   __shared__ float buf[NT / 64];
   __shared__ float buf2[NT];
-  __shared__ int s_A, s_good;
+  __shared__ int s_flag;
   const int Kmax = a.K, NJ = a.B * (Kmax + 1);
-  const int job = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int b = job / (Kmax + 1), j = job % (Kmax + 1);
+  const int32_t *flags = reinterpret_cast<const int32_t *>(lse_buf + 2 * NJ);
+  const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int Kb = a.verify_len ? a.verify_len[b] : Kmax;
-  const float invT = a.invT;
-  // bookkeeping over all requests (block 0): acceptance of every request, tau, counters
-  if (job == 0 && fin.acc) {
-    __shared__ unsigned long long tot[4];  // integer sums: order-independent
-    if (t == 0) { tot[0] = tot[1] = tot[2] = tot[3] = 0; }
-    __syncthreads();
-    for (int bb = wave; bb < a.B; bb += NT / 64) {
-      const int Kbb = a.verify_len ? a.verify_len[bb] : Kmax;
-      const long tr0 = a.row_off ? a.row_off[bb] : (long)bb * (Kmax + 1);
-      const long dr0 = (long)bb * Kmax;
-      const int jb0 = bb * (Kmax + 1);
-      bool ok = true, rej = false;
-      int A = 0;
-      for (int base = 0; base <= Kbb; base += 64) {
-        const int jj = base + lane;
-        bool acc = false;
-        if (jj <= Kbb && (!isfinite(lse_buf[jb0 + jj]) || (jj < Kbb && !isfinite(lse_buf[NJ + jb0 + jj])))) ok = false;
-        if (jj < Kbb) {
-          const int x = a.draft[dr0 + jj];
-          if (x < 0 || x >= a.V) {
-            ok = false;
-          } else {
-            const float lpt = a.logits_t[(tr0 + jj) * (long)a.V + x] * invT - lse_buf[jb0 + jj];
-            const float lqd = a.logits_d[(dr0 + jj) * (long)a.V + x] * invT - lse_buf[NJ + jb0 + jj];
-            acc = a.u[(long)bb * (Kmax + 1) + jj] < __expf(lpt - lqd);
-          }
-        }
-        if (!rej && base < Kbb) {
-          const int live_n = Kbb - base;
-          const unsigned long long live = live_n >= 64 ? ~0ull : ((1ull << live_n) - 1ull);
-          const unsigned long long rejm = __ballot(!acc) & live;
-          if (rejm) { A = base + __ffsll((long long)rejm) - 1; rej = true; }
-          else A = min(Kbb, base + 64);
-        }
-      }
-      const bool good_b = !__any(!ok);
-      if (lane == 0 && good_b) {
-        atomicAdd(&tot[0], (unsigned long long)A);
-        atomicAdd(&tot[1], (unsigned long long)Kbb);
-        atomicAdd(&tot[2], (unsigned long long)(A + 1));
-        atomicAdd(&tot[3], 1ull);
-      }
-    }
-    __syncthreads();
-    if (t == 0) {
-      *fin.tau = tot[3] ? (float)((double)tot[2] / (double)tot[3]) : 0.f;
-      if (fin.counters) {
-        fin.counters[0] = (int64_t)tot[0];
-        fin.counters[1] = (int64_t)tot[1];
-        fin.counters[2] = (int64_t)tot[2];
-      }
-    }
-    __syncthreads();
-  }
-  if (j > Kb) return;
   const long trow0 = a.row_off ? a.row_off[b] : (long)b * (Kmax + 1);
   const long drow0 = (long)b * Kmax;
+  const float invT = a.invT;
   const int jb0 = b * (Kmax + 1);
-  // ---- acceptance scan of this request (wave 0), shared with the block
   if (wave == 0) {
-    bool ok = true, rej = false;
-    int A = 0;
-    for (int base = 0; base <= Kb; base += 64) {
-      const int jj = base + lane;
-      bool acc = false;
-      if (jj <= Kb && (!isfinite(lse_buf[jb0 + jj]) || (jj < Kb && !isfinite(lse_buf[NJ + jb0 + jj])))) ok = false;
-      if (jj < Kb) {
-        const int x = a.draft[drow0 + jj];
-        if (x < 0 || x >= a.V) {
-          ok = false;
-          set_status(a.dev_status, SV_DEV_BAD_TOKEN);
-        } else {
-          const float zt = a.logits_t[(trow0 + jj) * (long)a.V + x];
-          const float zd = a.logits_d[(drow0 + jj) * (long)a.V + x];
-          const float lpt = zt * invT - lse_buf[jb0 + jj];
-          const float lqd = zd * invT - lse_buf[NJ + jb0 + jj];
-          const float ratio = __expf(lpt - lqd);
-          acc = a.u[(long)b * (Kmax + 1) + jj] < ratio;
-          if (a.diag && j == 0) {
-            float *dt = a.diag + ((long)b * (Kmax + 1) + jj) * SV_DIAG_COLS;
-            dt[4] = zt; dt[5] = __expf(lpt); dt[6] = ratio;
-            float *dd = a.diag + ((long)a.B * (Kmax + 1) + drow0 + jj) * SV_DIAG_COLS;
-            dd[4] = zd; dd[5] = __expf(lqd);
-          }
-        }
-      }
-      if (!rej && base < Kb) {
-        const int live_n = Kb - base;
-        const unsigned long long live = live_n >= 64 ? ~0ull : ((1ull << live_n) - 1ull);
-        const unsigned long long rejm = __ballot(!acc) & live;
-        if (rejm) { A = base + __ffsll((long long)rejm) - 1; rej = true; }
-        else A = min(Kb, base + 64);
-      }
-    }
-    const bool good = !__any(!ok);
-    if (lane == 0) {
-      s_A = A;
-      s_good = good;
-      if (!good) {
-        bool nonfin = false;
-        for (int jj = 0; jj <= Kb; ++jj)
-          if (!isfinite(lse_buf[jb0 + jj]) || (jj < Kb && !isfinite(lse_buf[NJ + jb0 + jj]))) nonfin = true;
-        if (nonfin) set_status(a.dev_status, SV_DEV_NONFINITE);
-      }
-    }
-  }
-  // per-row statistics for the diagnostics (the j == 0 block of each request)
-  if (a.diag && j == 0 && t <= Kb) {
-    const StatPart st = rowst[2 * (jb0 + t)];
-    float *dg = a.diag + ((long)b * (Kmax + 1) + t) * SV_DIAG_COLS;
-    dg[0] = lse_buf[jb0 + t]; dg[1] = (float)st.i1; dg[2] = st.b1 - st.b2; dg[3] = st.b1; dg[7] = 0.f;
-    if (t < Kb) {
-      const StatPart sd = rowst[2 * (jb0 + t) + 1];
-      float *dd = a.diag + ((long)a.B * (Kmax + 1) + drow0 + t) * SV_DIAG_COLS;
-      dd[0] = lse_buf[NJ + jb0 + t]; dd[1] = (float)sd.i1; dd[2] = sd.b1 - sd.b2; dd[3] = sd.b1;
-      dd[6] = 1.f / sd.s; dd[7] = 0.f;
+    int A, bad;
+    scan_flags(flags + jb0, Kb, A, bad);
+    if (t == 0) {
+      if (bad & FLAG_BAD_TOKEN) set_status(a.dev_status, SV_DEV_BAD_TOKEN);
+      if (bad & FLAG_NONFINITE) set_status(a.dev_status, SV_DEV_NONFINITE);
+      s_flag = bad ? -1 : A;
     }
   }
   __syncthreads();
-  const int A = s_A;
-  const bool good = s_good != 0;
-  if (!good) {
-    if (j == 0) {
-      for (int jj = t; jj <= Kmax; jj += NT) a.emitted[(long)b * (Kmax + 1) + jj] = -1;
-      if (t == 0) a.accepted_len[b] = -1;
+  const int A = s_flag;
+  if (A < 0) {
+    for (int jj = t; jj <= Kmax; jj += NT) a.emitted[(long)b * (Kmax + 1) + jj] = -1;
+    if (t == 0) a.accepted_len[b] = -1;
+  } else {
+    // ---- draw the token of the candidate at the first rejection
+    const int cj = jb0 + A;
+    const bool resid_cand = A < Kb;
+    const float lse1 = lse_buf[cj], lse2 = lse_buf[NJ + cj];
+    const float *z1 = a.logits_t + (trow0 + A) * (long)a.V;
+    const float *z2 = resid_cand ? a.logits_d + (drow0 + A) * (long)a.V : nullptr;
+    const float coin = a.u[(long)b * (Kmax + 1) + Kmax];
+    const float wr = t < C ? sums[((long)cj * C + t) * 2 + 0] : 0.f;
+    const float wp = t < C ? sums[((long)cj * C + t) * 2 + 1] : 0.f;
+    const float tr = block_sum(wr, redf);
+    const float tp = block_sum(wp, redf);
+    const bool resid = z2 != nullptr && tr > 0.f;
+    const float total = resid ? tr : tp;
+    const float target = coin * total;
+    const float w = resid ? wr : wp;
+    const float incl = block_incl_scan(w, buf);
+    int pick = block_min_int((t < C && incl > target) ? t : 0x7fffffff, redi);
+    if (pick == 0x7fffffff) {
+      pick = -block_min_int((t < C && w > 0.f) ? -t : 1, redi);
+      if (pick < 0) pick = 0;
     }
-    return;
-  }
-  if (j != A) return;  // only the candidate at the first rejection matters
-  // ---- locate this candidate's token
-  const bool resid_row = j < Kb;
-  const float lse1 = lse_buf[job], lse2 = lse_buf[NJ + job];
-  const float *z1 = a.logits_t + (trow0 + j) * (long)a.V;
-  const float *z2 = resid_row ? a.logits_d + (drow0 + j) * (long)a.V : nullptr;
-  const float coin = a.u[(long)b * (Kmax + 1) + Kmax];
-  const float wr = t < C ? sums[((long)job * C + t) * 2 + 0] : 0.f;
-  const float wp = t < C ? sums[((long)job * C + t) * 2 + 1] : 0.f;
-  const float tr = block_sum(wr, red);
-  const float tp = block_sum(wp, red);
-  const bool resid = z2 != nullptr && tr > 0.f;
-  const float total = resid ? tr : tp;
-  const float target = coin * total;
-  const float w = resid ? wr : wp;
-  const float incl = block_incl_scan(w, buf);
-  int pick = block_min_int((t < C && incl > target) ? t : 0x7fffffff, redi);
-  if (pick == 0x7fffffff) {
-    pick = -block_min_int((t < C && w > 0.f) ? -t : 1, redi);
-    if (pick < 0) pick = 0;
-  }
-  buf2[t] = incl - w;
-  __syncthreads();
-  const float base = buf2[pick];
-  const int v0 = pick * chunk, v1 = min(a.V, v0 + chunk);
-  const int per = (chunk + NT - 1) / NT;
-  const int a0 = v0 + t * per;
-  float wv[PER];
-  float mine = 0.f;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    float x = 0.f;
-    if (i < per && a0 + i < v1) {
-      const float p = __expf(z1[a0 + i] * invT - lse1);
-      x = resid ? fmaxf(p - __expf(z2[a0 + i] * invT - lse2), 0.f) : p;
-    }
-    wv[i] = x;
-    mine += x;
-  }
-  const float incl2 = block_incl_scan(mine, buf);
-  int tp2 = block_min_int((mine > 0.f && base + incl2 > target) ? t : 0x7fffffff, redi);
-  if (tp2 == 0x7fffffff) {
-    tp2 = -block_min_int(mine > 0.f ? -t : 1, redi);
-    if (tp2 < 0) tp2 = 0;
-  }
-  int v_pick = -1;
-  if (t == tp2) {
-    float run = base + incl2 - mine;
-    int v_last = -1;
+    buf2[t] = incl - w;
+    __syncthreads();
+    const float base = buf2[pick];
+    const int v0 = pick * chunk, v1 = min(a.V, v0 + chunk);
+    const int per = (chunk + NT - 1) / NT;
+    const int a0 = v0 + t * per;
+    float wv[PER];
+    float mine = 0.f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      if (v_pick >= 0) break;
-      if (wv[i] > 0.f) {
-        v_last = a0 + i;
-        if (run + wv[i] > target) v_pick = a0 + i;
+      float x = 0.f;
+      if (i < per && a0 + i < v1) {
+        const float p = __expf(z1[a0 + i] * invT - lse1);
+        x = resid ? fmaxf(p - __expf(z2[a0 + i] * invT - lse2), 0.f) : p;
       }
-      run += wv[i];
+      wv[i] = x;
+      mine += x;
     }
-    if (v_pick < 0) v_pick = v_last >= 0 ? v_last : min(max(a0, 0), a.V - 1);
-    buf2[0] = __int_as_float(v_pick);
+    const float incl2 = block_incl_scan(mine, buf);
+    int tp2 = block_min_int((mine > 0.f && base + incl2 > target) ? t : 0x7fffffff, redi);
+    if (tp2 == 0x7fffffff) {
+      tp2 = -block_min_int(mine > 0.f ? -t : 1, redi);
+      if (tp2 < 0) tp2 = 0;
+    }
+    int v_pick = -1;
+    if (t == tp2) {
+      float run = base + incl2 - mine;
+      int v_last = -1;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        if (v_pick >= 0) break;
+        if (wv[i] > 0.f) {
+          v_last = a0 + i;
+          if (run + wv[i] > target) v_pick = a0 + i;
+        }
+        run += wv[i];
+      }
+      if (v_pick < 0) v_pick = v_last >= 0 ? v_last : min(max(a0, 0), a.V - 1);
+      buf2[0] = __int_as_float(v_pick);
+    }
+    __syncthreads();
+    v_pick = __float_as_int(buf2[0]);
+    for (int jj = t; jj <= Kmax; jj += NT) {
+      int v = -1;
+      if (jj < A) v = a.draft[drow0 + jj];
+      if (jj == A) v = v_pick;
+      a.emitted[(long)b * (Kmax + 1) + jj] = v;
+    }
+    if (t == 0) a.accepted_len[b] = A;
+  }
+  if (b != 0 || !fin.acc) return;
+  // ---- block 0: acceptance of every request, tau, counters
+  __syncthreads();
+  __shared__ unsigned long long tot[4];  // integer sums: order-independent
+  if (t == 0) { tot[0] = tot[1] = tot[2] = tot[3] = 0; }
+  __syncthreads();
+  for (int bb = wave; bb < a.B; bb += NT / 64) {
+    const int Kbb = a.verify_len ? a.verify_len[bb] : Kmax;
+    int Ab, bad;
+    scan_flags(flags + bb * (Kmax + 1), Kbb, Ab, bad);
+    if (lane == 0 && !bad) {
+      atomicAdd(&tot[0], (unsigned long long)Ab);
+      atomicAdd(&tot[1], (unsigned long long)Kbb);
+      atomicAdd(&tot[2], (unsigned long long)(Ab + 1));
+      atomicAdd(&tot[3], 1ull);
+    }
   }
   __syncthreads();
-  v_pick = __float_as_int(buf2[0]);
-  for (int jj = t; jj <= Kmax; jj += NT) {
-    int v = -1;
-    if (jj < A) v = a.draft[drow0 + jj];
-    if (jj == A) v = v_pick;
-    a.emitted[(long)b * (Kmax + 1) + jj] = v;
+  if (t == 0) {
+    *fin.tau = tot[3] ? (float)((double)tot[2] / (double)tot[3]) : 0.f;
+    if (fin.counters) {
+      fin.counters[0] = (int64_t)tot[0];
+      fin.counters[1] = (int64_t)tot[1];
+      fin.counters[2] = (int64_t)tot[2];
+    }
   }
-  if (t == 0) a.accepted_len[b] = A;
 }
 
 // Confidence of each draft row: conf = max_v q(v) = 1 / sum_v exp((z_v - max z)/T).  One wave per row.
@@ -857,14 +893,19 @@ hipError_t launch_sample(const SampleJob *jobs, int njobs, int V, float invT, fl
   return hipGetLastError();
 }
 
-hipError_t launch_tail_small(const AcceptArgs &a, float *sums, float *lse_buf, StatPart *rowst,
-                             const FinalizeArgs &fin, hipStream_t st) {
+hipError_t launch_tail_small(const AcceptArgs &a, float *sums, float *lse_buf, const FinalizeArgs &fin,
+                             hipStream_t st) {
   const int C = sample_chunks(a.V);
-  const int chunk = (a.V + C - 1) / C;
+  // chunks of a multiple of 64 tokens (at most NT * PER): 16-byte aligned when V % 4 == 0
+  const int chunk = (((a.V + C - 1) / C) + 63) / 64 * 64;
   const int NJ = a.B * (a.K + 1);
-  hipLaunchKernelGGL(k_tail1, dim3(C, NJ), dim3(NT), 0, st, a, chunk, sums, lse_buf, rowst);
-  hipLaunchKernelGGL(k_tail2, dim3(NJ), dim3(NT), 0, st, a, chunk, C, (const float *)sums, (const float *)lse_buf,
-                     (const StatPart *)rowst, fin);
+  const dim3 grid((C + SUBS - 1) / SUBS, NJ);
+  if (a.V % 4 == 0)
+    hipLaunchKernelGGL(k_tail1<true>, grid, dim3(NT), 0, st, a, chunk, C, sums, lse_buf);
+  else
+    hipLaunchKernelGGL(k_tail1<false>, grid, dim3(NT), 0, st, a, chunk, C, sums, lse_buf);
+  hipLaunchKernelGGL(k_tail2, dim3(a.B), dim3(NT), 0, st, a, chunk, C, (const float *)sums, (const float *)lse_buf,
+                     fin);
   return hipGetLastError();
 }
 
