@@ -81,19 +81,29 @@ void k_tiled(const GemmArgs a) {
   if (a.M_dev) M = min(M, *a.M_dev);
   const int Ncols = PAIR ? 2 * a.N : a.N;  // columns of the weight-row space
   const int tiles_m = (a.M + BM - 1) / BM;
-  const int G = gridDim.x;
-  int lin = blockIdx.x;
-  if ((G & 7) == 0) lin = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-  const int tmi = lin % tiles_m, tni = lin / tiles_m;
-  const int m0 = tmi * BM, n0 = tni * BN;
-  if (m0 >= M) return;
-
+  const int total = tiles_m * ((Ncols + BN - 1) / BN);
   const int splits = gridDim.z, z = blockIdx.z;
   const int nkt_total = a.K / BK;
   const int per = (nkt_total + splits - 1) / splits;
   const int kt0 = z * per;
   const int kt1 = min(nkt_total, kt0 + per);
   const int nkt = kt1 > kt0 ? kt1 - kt0 : 0;
+  // Tiles: workgroup w takes tiles r*G + slot(w), r = 0, 1, ... (one round when the grid
+  // covers every tile).  With G a multiple of 8, workgroup w runs on XCD w % 8 and
+  // slot(w) = (w % 8) * G/8 + w / 8, so consecutive tiles - the row tiles of one weight
+  // tile - run on one XCD at the same time and read that weight tile through its L2.
+  // A persistent grid (one workgroup per CU slot) keeps those row tiles in step round
+  // after round; the hardware dispatcher would start them at scattered times.
+  const int G = gridDim.x;
+  const int slot = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  for (int lin = slot; lin < total; lin += G) {
+  const int tmi = lin % tiles_m, tni = lin / tiles_m;
+  const int m0 = tmi * BM, n0 = tni * BN;
+  if (m0 >= M) continue;
+  if (lin != slot) {  // every wave's reads of the previous tile's slices are done
+    lgkm_wait0();
+    __builtin_amdgcn_s_barrier();
+  }
 
   // Per-lane global sources of the slice loads.  Load j of this wave fills LDS bytes
   // [(wave + 4 j) KB, +1 KB) of the operand: rows (wave + 4 j) * RPI + lane / CPR, at
@@ -258,7 +268,7 @@ void k_tiled(const GemmArgs a) {
     // statistics over all of the wave's columns.
     const bool ws = a.want_s != 0;
     const float invT = a.invT;
-    const int slot = tni * 2 + wn;
+    const int pslot = tni * 2 + wn;
     const int nb = n0 + wn * WTN + l32;
     if (a.logits) {
       // row bases are wave-uniform; the lane part (row half, column) is an offset
@@ -332,9 +342,10 @@ void k_tiled(const GemmArgs a) {
       const StatPart st = stat_merge(p[0], stat_shfl_xor(p[0], 1), invT, ws);
       const int rr = l32 >> 1;
       const int m = m0 + wm * WTM + i * 32 + (rr >> 2) * 8 + rsub + (rr & 3);
-      if ((lane & 1) == 0 && m < M) a.parts[(long)m * a.nslots + slot] = st;
+      if ((lane & 1) == 0 && m < M) a.parts[(long)m * a.nslots + pslot] = st;
     }
   }
+  }  // tiles
 }
 
 // Fixed-order reduction of split-K partials followed by the elementwise epilogue.
@@ -367,11 +378,24 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const GemmArgs a, int spl
   }
 }
 
+// Workgroups of one tile shape resident per CU: bounded by the LDS of the slice pipeline
+// (160 KiB per CU) and by the waves per SIMD the kernel is compiled for.
+template <int BM, int BN>
+constexpr int per_cu() {
+  constexpr int lds = stages<BM, BN>() * (BM + BN) * RB;
+  constexpr int by_lds = (160 * 1024) / lds;
+  return by_lds < waves_per_eu<BM, BN>() ? by_lds : waves_per_eu<BM, BN>();
+}
+
 template <int BM, int BN>
 hipError_t launch_bm_bn(const GemmArgs &a, int epi, int splits, hipStream_t st) {
   const int Ncols = (epi == EPI_SWIGLU) ? 2 * a.N : a.N;
   const int tiles = ((a.M + BM - 1) / BM) * ((Ncols + BN - 1) / BN);
-  dim3 grd(tiles, 1, splits), blk(256);
+  // more tiles than resident slots: a persistent grid of one workgroup per slot
+  int gx = tiles;
+  const int slots = (per_cu<BM, BN>() * num_cus()) & ~7;
+  if (splits == 1 && slots > 0 && tiles > slots) gx = slots;
+  dim3 grd(gx, 1, splits), blk(256);
   if (splits > 1) {
     if (epi == EPI_SWIGLU) hipLaunchKernelGGL((k_tiled<BM, BN, EPI_RAW, true>), grd, blk, 0, st, a);
     else hipLaunchKernelGGL((k_tiled<BM, BN, EPI_RAW, false>), grd, blk, 0, st, a);
