@@ -7,8 +7,9 @@ target and draft rows, statistics, acceptance, residual/bonus sampling, tau) on 
 batch of synthetic inputs already resident in HBM.  The headline workload is the
 16-token block (B=1, K=15, d=4096, d_ff=12288, V=151936, T=1 sampled); `value` is
 verified positions per second (B*(K+1) target rows per step).  Rank 0 prints one
-JSON line.  Extra points (greedy at B=1, greedy at B=128) are reported under
-"extra" with their own roofline.
+JSON line.  Extra points (greedy at B=1; the greedy batch sweep at B=8, 32, 128; the
+confidence-scheduled step, literal and budget-binding; the wide model) are reported
+under "extra", each with its own roofline and the spread of single-step times.
 """
 from __future__ import annotations
 
@@ -77,11 +78,15 @@ def main():
     t0 = time.time()
     data = wl.generate(wk)
     log(f"generated {wk.name} inputs in {time.time() - t0:.1f}s")
-    w = bd.Weights(to_bf16(data["w_lm"]), to_bf16(data["w_gate"]) if wk.d_ff else None,
-                   to_bf16(data["w_up"]) if wk.d_ff else None, to_bf16(data["w_down"]) if wk.d_ff else None)
+    def weights(datac, wkc):
+        return bd.Weights(to_bf16(datac["w_lm"]), to_bf16(datac["w_gate"]) if wkc.d_ff else None,
+                          to_bf16(datac["w_up"]) if wkc.d_ff else None, to_bf16(datac["w_down"]) if wkc.d_ff else None)
 
-    def prepare(wkc, datac, modec):
+    w = w_main = weights(data, wk)
+
+    def prepare(wkc, datac, modec, wts=None):
         """Device inputs, drafts from the library's own drafter step, outputs, workspace."""
+        w = wts if wts is not None else w_main
         h = to_bf16(datac["h"])
         hd = to_bf16(datac["h_draft"])
         u = to_f32(datac["coins"])
@@ -130,7 +135,16 @@ def main():
         out.ev_lm = None
         lm_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
         ms_instr = e2.elapsed_time(e3) / steps
-        return ms, lm_ms, ms_instr
+        # and once more with an event between consecutive steps: the spread of single steps
+        sev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        sev[0].record()
+        for i in range(steps):
+            call()
+            sev[i + 1].record()
+        torch.cuda.synchronize()
+        per = np.array([sev[i].elapsed_time(sev[i + 1]) for i in range(steps)])
+        spread = {"median": float(np.median(per)), "min": float(per.min()), "max": float(per.max())}
+        return ms, lm_ms, ms_instr, spread
 
     if args.copy_calibration:
         src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
@@ -140,7 +154,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     call, out = prepare(wk, data, mode)
-    ms, lm_ms, ms_instr = timed(call, out, args.steps, args.warmup)
+    ms, lm_ms, ms_instr, spread = timed(call, out, args.steps, args.warmup)
     st = int(out.dev_status.item())
     if st != 0:
         raise SystemExit(f"device status {st}")
@@ -174,7 +188,7 @@ def main():
                    "mode": mode},
         "accepted_tokens_per_sec": tok_s, "accepted_drafts_per_sec": float(counters[0]) / (ms * 1e-3),
         "tau": tau, "step_hbm_fraction": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "ms_per_step_with_lm_events": ms_instr, "roofline": roof,
+        "ms_per_step_with_lm_events": ms_instr, "step_ms_spread": spread, "roofline": roof,
     }
     if mode == "scheduled":
         result["config"]["budget"] = wk.budget
@@ -187,9 +201,9 @@ def main():
         extra = []
         # greedy on the same block
         call_g, out_g = prepare(wk, data, "greedy")
-        msg, lmg, _ = timed(call_g, out_g, args.steps, args.warmup)
+        msg, lmg, _, sp_g = timed(call_g, out_g, args.steps, args.warmup)
         b_lm = 2.0 * V * d + 2.0 * B * (K + 1) * d
-        extra.append({"workload": f"block16 greedy: B=1 K=15", "ms_per_step": msg,
+        extra.append({"workload": f"block16 greedy: B=1 K=15", "ms_per_step": msg, "step_ms_spread": sp_g,
                       "positions_per_sec": B * (K + 1) / (msg * 1e-3),
                       "accepted_tokens_per_sec": float(out_g.counters.cpu().numpy()[2]) / (msg * 1e-3),
                       "tau": float(out_g.tau.item()),
@@ -198,25 +212,76 @@ def main():
                                    "kernel": "LM-head GEMM", "launch_ms": lmg},
                       "step_hbm_fraction": step_bytes / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS})
         log(f"block16/greedy: {msg:.3f} ms/step")
-        # B = 128, K = 7 greedy: the compute-bound end of the batch sweep (same weight shapes)
-        wk2 = wl.SWEEP.with_batch(128)
-        d2 = wl.generate(wk2, weights=False)
-        call2, out2 = prepare(wk2, d2, "greedy")
-        ms2, lm2, _ = timed(call2, out2, max(5, args.steps // 2), max(2, args.warmup // 2))
-        M2 = wk2.B * (wk2.K + 1)
-        flops = 2.0 * M2 * 3 * d * d_ff + 2.0 * M2 * d * V
-        lm_fl = 2.0 * M2 * d * V
-        extra.append({"workload": "sweep greedy: B=128 K=7 (same shapes)", "ms_per_step": ms2,
-                      "positions_per_sec": M2 / (ms2 * 1e-3),
-                      "accepted_tokens_per_sec": float(out2.counters.cpu().numpy()[2]) / (ms2 * 1e-3),
-                      "tau": float(out2.tau.item()),
-                      "step_tflops": flops / (ms2 * 1e-3) / 1e12,
-                      "step_mfma_fraction": flops / (ms2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                      "roofline": {"bound": "mfma", "achieved": lm_fl / (lm2 * 1e-3) / 1e12,
-                                   "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                   "frac": lm_fl / (lm2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                                   "kernel": "LM-head GEMM", "launch_ms": lm2}})
-        log(f"sweep B=128 greedy: {ms2:.3f} ms/step, {flops / (ms2 * 1e-3) / 1e12:.0f} TFLOP/s")
+        del call_g, out_g
+        # the batch sweep (K = 7 greedy, same weight shapes): B = 8, 32 HBM-bound, B = 128 MFMA-bound
+        for Bs in (8, 32, 128):
+            wk2 = wl.SWEEP.with_batch(Bs)
+            d2 = wl.generate(wk2, weights=False)
+            call2, out2 = prepare(wk2, d2, "greedy")
+            ms2, lm2, _, sp2 = timed(call2, out2, max(5, args.steps // 2), max(2, args.warmup // 2))
+            M2 = wk2.B * (wk2.K + 1)
+            flops = 2.0 * M2 * 3 * d * d_ff + 2.0 * M2 * d * V
+            lm_fl, lm_b = 2.0 * M2 * d * V, 2.0 * V * d + 2.0 * M2 * d
+            pt = {"workload": f"sweep greedy: B={Bs} K=7 (same shapes)", "ms_per_step": ms2, "step_ms_spread": sp2,
+                  "positions_per_sec": M2 / (ms2 * 1e-3),
+                  "accepted_tokens_per_sec": float(out2.counters.cpu().numpy()[2]) / (ms2 * 1e-3),
+                  "tau": float(out2.tau.item()),
+                  "step_tflops": flops / (ms2 * 1e-3) / 1e12,
+                  "step_mfma_fraction": flops / (ms2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                  "step_hbm_fraction": step_bytes / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            if lm_fl / lm_b >= 315:
+                pt["roofline"] = {"bound": "mfma", "achieved": lm_fl / (lm2 * 1e-3) / 1e12,
+                                  "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": lm_fl / (lm2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                                  "kernel": "LM-head GEMM", "launch_ms": lm2}
+            else:
+                pt["roofline"] = {"bound": "hbm", "achieved": lm_b / (lm2 * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": lm_b / (lm2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                  "kernel": "LM-head GEMM", "launch_ms": lm2}
+            extra.append(pt)
+            log(f"sweep B={Bs} greedy: {ms2:.3f} ms/step, {flops / (ms2 * 1e-3) / 1e12:.0f} TFLOP/s")
+            del call2, out2, d2
+        # the confidence-scheduled step: literal configuration and the budget-binding stress variant
+        for wk3 in (wl.SCHED, wl.SCHED_STRESS):
+            d3 = wl.generate(wk3, weights=False)
+            call3, out3 = prepare(wk3, d3, "scheduled")
+            ms3, lm3, _, sp3 = timed(call3, out3, max(5, args.steps // 2), max(2, args.warmup // 2))
+            vl3 = out3.verify_len.cpu().numpy()
+            M3 = int((vl3 + 1).sum())
+            rows_d = wk3.B * wk3.K
+            s1_fl = 2.0 * rows_d * d * V
+            extra.append({"workload": f"{wk3.name} scheduled: B={wk3.B} Kmax={wk3.K} budget={wk3.budget} "
+                                      f"threshold={wk3.threshold} T={wk3.T}",
+                          "ms_per_step": ms3, "step_ms_spread": sp3, "verified_rows": M3,
+                          "positions_per_sec": M3 / (ms3 * 1e-3),
+                          "accepted_tokens_per_sec": float(out3.counters.cpu().numpy()[2]) / (ms3 * 1e-3),
+                          "tau": float(out3.tau.item()),
+                          "roofline": {"bound": "mfma", "achieved": s1_fl / (lm3 * 1e-3) / 1e12,
+                                       "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": s1_fl / (lm3 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                                       "kernel": f"draft-confidence LM-head pass over {rows_d} rows",
+                                       "launch_ms": lm3}})
+            log(f"{wk3.name}: {ms3:.3f} ms/step, {M3} verified rows")
+            del call3, out3, d3
+        # the wide model (d = 8192, d_ff = 28672, V = 128256), B = 32, K = 4, T = 0.7, sampled
+        wk4 = wl.WIDE
+        d4 = wl.generate(wk4)
+        w4 = weights(d4, wk4)
+        call4, out4 = prepare(wk4, d4, "sample", w4)
+        ms4, lm4, _, sp4 = timed(call4, out4, max(5, args.steps // 2), max(2, args.warmup // 2))
+        M4t, M4 = wk4.B * (wk4.K + 1), wk4.B * (2 * wk4.K + 1)
+        b4 = 2.0 * wk4.V * wk4.d + 2.0 * M4 * wk4.d
+        extra.append({"workload": f"wide sample: B={wk4.B} K={wk4.K} d={wk4.d} d_ff={wk4.d_ff} V={wk4.V} T={wk4.T}",
+                      "ms_per_step": ms4, "step_ms_spread": sp4,
+                      "positions_per_sec": M4t / (ms4 * 1e-3),
+                      "accepted_tokens_per_sec": float(out4.counters.cpu().numpy()[2]) / (ms4 * 1e-3),
+                      "tau": float(out4.tau.item()),
+                      "step_hbm_fraction": float(wk4.weight_bytes()) / (ms4 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "roofline": {"bound": "hbm", "achieved": b4 / (lm4 * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                                   "unit": "GB/s", "frac": b4 / (lm4 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                   "kernel": f"LM-head GEMM over {M4} rows", "launch_ms": lm4}})
+        log(f"wide: {ms4:.3f} ms/step")
+        del call4, out4, w4, d4
         result["extra"] = extra
 
     if not args.no_cpu:
