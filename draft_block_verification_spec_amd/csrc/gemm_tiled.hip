@@ -21,14 +21,15 @@ namespace {
 
 typedef __attribute__((address_space(3))) void *lds_ptr;
 
-constexpr int BK = 64;         // k-slice depth
-constexpr int RB = BK * 2;     // bytes per tile row of a slice
-constexpr int CPR = BK / 8;    // 16-byte chunks per row
-constexpr int RPI = 64 / CPR;  // rows covered by one wave-wide 1 KB load
-
-// Row r's logical chunk c sits at chunk c ^ swz(r): sixteen consecutive rows read at
-// one logical chunk then cover all 64 banks once.
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & (CPR - 1); }
+// Slice geometry for a k-slice depth BK: RB bytes per tile row, CPR 16-byte chunks per
+// row, RPI rows covered by one wave-wide 1 KB load.
+template <int BK>
+struct Slice {
+  static constexpr int RB = BK * 2, CPR = BK / 8, RPI = 64 / CPR;
+  // Row r's logical chunk c sits at chunk c ^ swz(r): with 64 banks of 4 bytes, 16
+  // consecutive rows read at one logical chunk then hit 16 distinct 16-byte bank groups.
+  static __device__ __forceinline__ int swz(int r) { return (r / (16 / CPR)) & (CPR - 1); }
+};
 
 // 16 bytes per lane from global memory into LDS: lane l writes bytes
 // [16 l, 16 l + 16) after the wave-uniform LDS address.
@@ -53,20 +54,19 @@ __device__ __forceinline__ void vm_wait() {
 __device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 template <int BM, int BN>
-constexpr int stages() { return 2; }
-template <int BM, int BN>
 constexpr int waves_per_eu() { return BM * BN >= 256 * 256 ? 1 : 2; }
 
 // PAIR: the weight rows of a tile are [32 gate | 32 up] groups of the same outputs.
-template <int BM, int BN, int EPI, bool PAIR>
+template <int BM, int BN, int BK, int NS, int EPI, bool PAIR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_eu<BM, BN>(), waves_per_eu<BM, BN>())))
 void k_tiled(const GemmArgs a) {
-  constexpr int NS = stages<BM, BN>();
+  constexpr int RB = Slice<BK>::RB, CPR = Slice<BK>::CPR, RPI = Slice<BK>::RPI;
   constexpr int SA = BM * RB, SB = BN * RB, SS = SA + SB;  // bytes of one slice
   constexpr int IA = BM / RPI / 4, IB = BN / RPI / 4;      // 1 KB loads per wave per slice
   constexpr int WTM = BM / 2, WTN = BN / 2, TM = WTM / 32, TN = WTN / 32;
   constexpr int KS = BK / 16;
   static_assert(IA >= 1 && IB >= 1, "tile too small");
+  static_assert(NS >= 2 && (NS - 1) * (IA + IB) < 64, "slice pipeline depth");
   static_assert(KS % 2 == 0, "fragment sets alternate within a slice");
   static_assert(!PAIR || (WTN % 64) == 0, "paired tiles need gate/up block pairs");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * SS];
@@ -115,14 +115,14 @@ void k_tiled(const GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < IA; ++j) {
     const int r = (wave + 4 * j) * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ swz(r);
+    const int c = (lane % CPR) ^ Slice<BK>::swz(r);
     const int m = min(m0 + r, mlast);
     ga[j] = (m < a.m1 ? a.x1 + (long)m * a.ldx1 : a.x2 + (long)(m - a.m1) * a.ldx2) + c * 8;
   }
 #pragma unroll
   for (int j = 0; j < IB; ++j) {
     const int r = (wave + 4 * j) * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ swz(r);
+    const int c = (lane % CPR) ^ Slice<BK>::swz(r);
     if constexpr (PAIR) {
       const int p = r >> 6, half = (r >> 5) & 1, rr = r & 31;
       const int n = min((n0 >> 1) + p * 32 + rr, a.N - 1);
@@ -152,7 +152,7 @@ void k_tiled(const GemmArgs a) {
   // lane l reads row l%32 of a 32-row block at logical chunk 2 kk + l/32 of k step kk
   int off[KS];
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) off[kk] = l32 * RB + (((kk * 2 + hi) ^ swz(l32)) << 4);
+  for (int kk = 0; kk < KS; ++kk) off[kk] = l32 * RB + (((kk * 2 + hi) ^ Slice<BK>::swz(l32)) << 4);
   bf16x8 af[2][TM], bfr[2][TN];
   auto lfrag_one = [&](int set, uint32_t soff, int kk, int g) {
     const uint8_t *sb = smem + soff;
@@ -380,31 +380,31 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const GemmArgs a, int spl
 
 // Workgroups of one tile shape resident per CU: bounded by the LDS of the slice pipeline
 // (160 KiB per CU) and by the waves per SIMD the kernel is compiled for.
-template <int BM, int BN>
+template <int BM, int BN, int BK, int NS>
 constexpr int per_cu() {
-  constexpr int lds = stages<BM, BN>() * (BM + BN) * RB;
+  constexpr int lds = NS * (BM + BN) * BK * 2;
   constexpr int by_lds = (160 * 1024) / lds;
   return by_lds < waves_per_eu<BM, BN>() ? by_lds : waves_per_eu<BM, BN>();
 }
 
-template <int BM, int BN>
-hipError_t launch_bm_bn(const GemmArgs &a, int epi, int splits, hipStream_t st) {
+template <int BM, int BN, int BK, int NS>
+hipError_t launch_shape(const GemmArgs &a, int epi, int splits, hipStream_t st) {
   const int Ncols = (epi == EPI_SWIGLU) ? 2 * a.N : a.N;
   const int tiles = ((a.M + BM - 1) / BM) * ((Ncols + BN - 1) / BN);
   // more tiles than resident slots: a persistent grid of one workgroup per slot
   int gx = tiles;
-  const int slots = (per_cu<BM, BN>() * num_cus()) & ~7;
+  const int slots = (per_cu<BM, BN, BK, NS>() * num_cus()) & ~7;
   if (splits == 1 && slots > 0 && tiles > slots) gx = slots;
   dim3 grd(gx, 1, splits), blk(256);
   if (splits > 1) {
-    if (epi == EPI_SWIGLU) hipLaunchKernelGGL((k_tiled<BM, BN, EPI_RAW, true>), grd, blk, 0, st, a);
-    else hipLaunchKernelGGL((k_tiled<BM, BN, EPI_RAW, false>), grd, blk, 0, st, a);
+    if (epi == EPI_SWIGLU) hipLaunchKernelGGL((k_tiled<BM, BN, BK, NS, EPI_RAW, true>), grd, blk, 0, st, a);
+    else hipLaunchKernelGGL((k_tiled<BM, BN, BK, NS, EPI_RAW, false>), grd, blk, 0, st, a);
     return hipGetLastError();
   }
   switch (epi) {
-    case EPI_LOGITS: hipLaunchKernelGGL((k_tiled<BM, BN, EPI_LOGITS, false>), grd, blk, 0, st, a); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((k_tiled<BM, BN, EPI_SWIGLU, true>), grd, blk, 0, st, a); break;
-    case EPI_RESID: hipLaunchKernelGGL((k_tiled<BM, BN, EPI_RESID, false>), grd, blk, 0, st, a); break;
+    case EPI_LOGITS: hipLaunchKernelGGL((k_tiled<BM, BN, BK, NS, EPI_LOGITS, false>), grd, blk, 0, st, a); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((k_tiled<BM, BN, BK, NS, EPI_SWIGLU, true>), grd, blk, 0, st, a); break;
+    case EPI_RESID: hipLaunchKernelGGL((k_tiled<BM, BN, BK, NS, EPI_RESID, false>), grd, blk, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -414,15 +414,47 @@ hipError_t launch_bm_bn(const GemmArgs &a, int epi, int splits, hipStream_t st) 
 
 int tiled_slots(int N, int bn) { return ((N + bn - 1) / bn) * 2; }
 
-hipError_t launch_gemm_tiled(const GemmArgs &a, int epi, int bm, int bn, int splits, hipStream_t st) {
-  if (bn == 256 && bm == 256) return launch_bm_bn<256, 256>(a, epi, splits, st);
-  if (bn != 128) return hipErrorInvalidValue;
-  switch (bm) {
-    case 64: return launch_bm_bn<64, 128>(a, epi, splits, st);
-    case 128: return launch_bm_bn<128, 128>(a, epi, splits, st);
-    case 256: return launch_bm_bn<256, 128>(a, epi, splits, st);
-    default: return hipErrorInvalidValue;
+// Shapes measured best on MI355X for the row counts of the verification step (LM head,
+// gate/up, down at d = 4096 and 8192): the fewer the rows, the more of each slice is
+// weights, and the deeper the pipeline must be to keep HBM busy.
+TileShape tiled_shape(int M, int N, int K, int epi) {
+  (void)N;
+  const bool k128 = K % 128 == 0;
+  if (epi == EPI_SWIGLU) return M <= 128 ? TileShape{128, 128, 64, 4} : TileShape{256, 128, 64, 3};
+  if (epi == EPI_RESID) {
+    if (M <= 64) return k128 ? TileShape{64, 128, 128, 3} : TileShape{64, 128, 64, 2};
+    return M <= 256 ? TileShape{128, 256, 64, 3} : TileShape{256, 128, 64, 3};
   }
+  if (M <= 64) return k128 ? TileShape{64, 128, 128, 3} : TileShape{64, 128, 64, 2};
+  if (M <= 128) return TileShape{128, 128, 64, 4};
+  if (M <= 256) return TileShape{256, 128, 64, 3};
+  if (M <= 384) return TileShape{128, 256, 64, 3};
+  return TileShape{256, 256, 64, 2};
+}
+
+#define SV_TILE_SHAPES(X) \
+  X(64, 128, 64, 2)       \
+  X(64, 128, 128, 3)      \
+  X(128, 128, 64, 4)      \
+  X(256, 128, 64, 3)      \
+  X(128, 256, 64, 3)      \
+  X(256, 256, 64, 2)
+
+int tiled_per_cu(const TileShape &sh) {
+#define SV_PER_CU(BM, BN, BK, NS) \
+  if (sh.bm == BM && sh.bn == BN && sh.bk == BK && sh.ns == NS) return per_cu<BM, BN, BK, NS>();
+  SV_TILE_SHAPES(SV_PER_CU)
+#undef SV_PER_CU
+  return 0;
+}
+
+hipError_t launch_gemm_tiled(const GemmArgs &a, int epi, const TileShape &sh, int splits, hipStream_t st) {
+  if (a.K % sh.bk != 0) return hipErrorInvalidValue;
+#define SV_LAUNCH(BM, BN, BK, NS) \
+  if (sh.bm == BM && sh.bn == BN && sh.bk == BK && sh.ns == NS) return launch_shape<BM, BN, BK, NS>(a, epi, splits, st);
+  SV_TILE_SHAPES(SV_LAUNCH)
+#undef SV_LAUNCH
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_splitk_reduce(const GemmArgs &a, int epi, int splits, int bn, hipStream_t st) {

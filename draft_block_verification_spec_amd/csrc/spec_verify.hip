@@ -36,8 +36,9 @@ size_t up(size_t x) { return (x + ALIGN - 1) & ~(ALIGN - 1); }
 
 struct Gemm {
   bool stream = true;
-  int grid = 0;    // stream kernel
-  int bm = 0, bn = 128, splits = 1;  // tiled kernel
+  int grid = 0;                     // stream kernel
+  TileShape shape{128, 128, 64, 2};  // tiled kernel
+  int splits = 1;
   int nslots = 0;  // statistics slots per row (EPI_LOGITS)
   size_t partial_floats = 0;
 };
@@ -52,24 +53,21 @@ Gemm choose(int M, int N, int K, int epi) {
     return g;
   }
   g.stream = false;
-  g.bm = M <= 64 ? 64 : (M <= 128 ? 128 : 256);
-  g.bn = (epi == EPI_LOGITS && M > 256) ? 256 : 128;
-  // SwiGLU pairs fill the chip better with 128-row tiles, two workgroups per CU
-  if (epi == EPI_SWIGLU && M > 128) g.bm = 128;
+  g.shape = tiled_shape(M, N, K, epi);
   const int Ncols = epi == EPI_SWIGLU ? 2 * N : N;
-  const long tiles = (long)((M + g.bm - 1) / g.bm) * ((Ncols + g.bn - 1) / g.bn);
-  // resident workgroups per CU, set by the LDS of the two-slice pipeline
-  const int per_cu = g.bm * g.bn >= 256 * 128 ? 1 : (g.bm == 128 ? 2 : 3);
-  const long slots = (long)per_cu * num_cus();
-  if (epi != EPI_LOGITS && tiles < slots) {
+  const long tiles = (long)((M + g.shape.bm - 1) / g.shape.bm) * ((Ncols + g.shape.bn - 1) / g.shape.bn);
+  // the down projection (few output columns, long K) splits K until the tiles fill the
+  // resident workgroup slots; split SwiGLU and logits tiles measured slower
+  const long slots = (long)tiled_per_cu(g.shape) * num_cus();
+  if (epi == EPI_RESID && tiles < slots) {
     const int want = (int)((slots + tiles - 1) / tiles);
-    int maxs = (K / 64) / 4;
+    int maxs = (K / g.shape.bk) / 4;
+    if (maxs > 8) maxs = 8;
     if (maxs < 1) maxs = 1;
     g.splits = want < maxs ? want : maxs;
-    if (g.splits < 1) g.splits = 1;
   }
   if (g.splits > 1) g.partial_floats = (size_t)g.splits * M * Ncols;
-  if (epi == EPI_LOGITS) g.nslots = tiled_slots(N, g.bn);
+  if (epi == EPI_LOGITS) g.nslots = tiled_slots(N, g.shape.bn);
   return g;
 }
 
@@ -182,11 +180,11 @@ thread_local const char *g_last_hip_error = "no error";
 hipError_t run_gemm(const Gemm &g, GemmArgs a, int epi, hipStream_t st) {
   if (g.stream) return launch_gemm_stream(a, epi, g.grid, st);
   if (g.splits > 1) {
-    hipError_t e = launch_gemm_tiled(a, epi, g.bm, g.bn, g.splits, st);
+    hipError_t e = launch_gemm_tiled(a, epi, g.shape, g.splits, st);
     if (e != hipSuccess) return e;
-    return launch_splitk_reduce(a, epi, g.splits, g.bn, st);
+    return launch_splitk_reduce(a, epi, g.splits, g.shape.bn, st);
   }
-  return launch_gemm_tiled(a, epi, g.bm, g.bn, 1, st);
+  return launch_gemm_tiled(a, epi, g.shape, 1, st);
 }
 
 // The dominant GEMM of a call, bracketed by the caller's optional measurement events.

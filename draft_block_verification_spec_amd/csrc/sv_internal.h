@@ -83,7 +83,16 @@ hipError_t launch_gemm_stream(const GemmArgs &a, int epi, int grid, hipStream_t 
 int stream_grid(const GemmArgs &a, int epi);
 bool stream_ok(int M, int epi);
 
-hipError_t launch_gemm_tiled(const GemmArgs &a, int epi, int bm, int bn, int splits, hipStream_t st);
+// Tile shape of the LDS-tiled GEMM: BM x BN outputs per workgroup, k-slices of BK
+// values, NS slices in the LDS pipeline.
+struct TileShape {
+  int bm, bn, bk, ns;
+};
+// Shape chosen for an M x N x K product with epilogue epi (K must be a multiple of 64).
+TileShape tiled_shape(int M, int N, int K, int epi);
+// Workgroups of a shape resident per CU (LDS and waves per SIMD).
+int tiled_per_cu(const TileShape &sh);
+hipError_t launch_gemm_tiled(const GemmArgs &a, int epi, const TileShape &sh, int splits, hipStream_t st);
 int tiled_slots(int N, int bn);
 hipError_t launch_splitk_reduce(const GemmArgs &a, int epi, int splits, int bn, hipStream_t st);
 
