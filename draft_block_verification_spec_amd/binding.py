@@ -31,9 +31,14 @@ class SpecVerifyError(RuntimeError):
     pass
 
 
+SV_WEIGHTS_BF16, SV_WEIGHTS_FP8_E4M3 = 0, 1
+
+
 class SvWeights(ctypes.Structure):
     _fields_ = [("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
-                ("w_lm", ctypes.c_void_p), ("d", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("V", ctypes.c_int32)]
+                ("w_lm", ctypes.c_void_p), ("d", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("V", ctypes.c_int32),
+                ("wtype", ctypes.c_int32), ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p),
+                ("s_down", ctypes.c_void_p), ("s_lm", ctypes.c_void_p)]
 
 
 class SvOutputs(ctypes.Structure):
@@ -95,20 +100,36 @@ def _check_dev(t, dtype, name):
 
 @dataclass
 class Weights:
-    """Device weights (bf16, row-major [out, in]) and the C struct that points at them."""
+    """Device weights, row-major [out, in], and the C struct that points at them.
+
+    bf16 tensors, or (FP8) uint8 E4M3 codes with the fp32 scale of every output row in
+    ``s_lm``, ``s_gate``, ``s_up``, ``s_down``."""
 
     w_lm: torch.Tensor
     w_gate: torch.Tensor | None = None
     w_up: torch.Tensor | None = None
     w_down: torch.Tensor | None = None
+    s_lm: torch.Tensor | None = None
+    s_gate: torch.Tensor | None = None
+    s_up: torch.Tensor | None = None
+    s_down: torch.Tensor | None = None
     c: SvWeights = field(init=False)
 
     def __post_init__(self):
+        fp8 = self.w_lm.dtype == torch.uint8
         for n in ("w_lm", "w_gate", "w_up", "w_down"):
-            _check_dev(getattr(self, n), torch.bfloat16, n)
+            _check_dev(getattr(self, n), torch.uint8 if fp8 else torch.bfloat16, n)
+        if fp8:
+            for n in ("s_lm",) + (("s_gate", "s_up", "s_down") if self.w_gate is not None else ()):
+                if getattr(self, n) is None:
+                    raise SpecVerifyError(f"{n}: FP8 weights need their row scales")
+                _check_dev(getattr(self, n), torch.float32, n)
         V, d = self.w_lm.shape
         d_ff = 0 if self.w_gate is None else self.w_gate.shape[0]
-        self.c = SvWeights(_ptr(self.w_gate), _ptr(self.w_up), _ptr(self.w_down), _ptr(self.w_lm), d, d_ff, V)
+        self.c = SvWeights(_ptr(self.w_gate), _ptr(self.w_up), _ptr(self.w_down), _ptr(self.w_lm), d, d_ff, V,
+                           SV_WEIGHTS_FP8_E4M3 if fp8 else SV_WEIGHTS_BF16,
+                           _ptr(self.s_gate) if fp8 else None, _ptr(self.s_up) if fp8 else None,
+                           _ptr(self.s_down) if fp8 else None, _ptr(self.s_lm) if fp8 else None)
 
     @property
     def d(self):

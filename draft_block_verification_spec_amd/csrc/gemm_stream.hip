@@ -34,6 +34,7 @@ namespace {
 constexpr int STEPS = 16;     // MFMA k-steps (32 values) per wave per chunk
 constexpr int WAVES = 8;
 constexpr int CHUNK_KS = STEPS * WAVES;  // k-steps per chunk (4096 values)
+constexpr int F8_MAX_COLS = 2048;        // FP8: columns of one workgroup whose scales are staged
 
 // KM (K mode): 1 = K is one 4096-value chunk, 2 = K is several whole chunks, 0 = any
 // other K.  With whole chunks (FULL) every wave owns exactly STEPS
@@ -42,19 +43,28 @@ constexpr int CHUNK_KS = STEPS * WAVES;  // k-steps per chunk (4096 values)
 // the compiler keep the 16 loads of a step in flight with partial vmcnt waits.
 // Rows beyond M read a clamped row and their results are dropped; weight rows
 // beyond N likewise.  The general path masks the tail of K with zero operands.
-template <int MB, int EPI, int KM>
+template <int MB, int EPI, int KM, bool F8>
 __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
   constexpr bool FULL = KM != 0;
   constexpr bool RELOAD_A = KM != 1;  // activations change with the chunk
   constexpr bool PAIR = (EPI == EPI_SWIGLU);
   constexpr int NACC = PAIR ? 2 * MB : MB;
   constexpr int NW = PAIR ? 2 : 1;  // weight streams
+  // FP8 weights: one byte per value, so a 256-byte run of a row holds 8 k-steps and a
+  // step of 16 k-steps needs 8 loads (16 with bf16); the general path reads 8 bytes
+  // per lane and k-step.
+  constexpr int ES = F8 ? 1 : 2;                // bytes per weight value
+  constexpr int WL = (F8 && FULL) ? 8 : STEPS;  // weight loads per wave and step
+  constexpr int GK = F8 ? 8 : 4;                // k-steps per reshaping group
+  using WT = typename std::conditional<F8 && !FULL, u32x2, u32x4>::type;
   // Every weight byte is read exactly once per call: nontemporal loads (measured
   // faster for all three GEMMs of the step).
-  auto ldw = [](const uint16_t *p) -> bf16x8 { return as_bf16x8(ld_nt(p)); };
+  auto ldw = [](const uint8_t *p) -> WT { return __builtin_nontemporal_load(reinterpret_cast<const WT *>(p)); };
   __shared__ float red[2][WAVES * NACC * 4 * 64];
   // per-wave reshaping slots (whole-chunk K only): [wave][stream][16 rows x 256 bytes]
   __shared__ __attribute__((aligned(16))) uint8_t tbuf[FULL ? WAVES * NW * 4096 : 16];
+  // FP8: the row scales of the workgroup's column range, staged once
+  __shared__ float sscale[F8 ? NW * F8_MAX_COLS : 1];
   // Outputs of the workgroup's whole column range are kept in LDS and written once at
   // the end (when a.buf_cols > 0): stores inside the streaming loop would share the
   // vector-memory counter with the weight loads and stall them.
@@ -82,9 +92,11 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
   };
 
   bf16x8 A[MB][STEPS];
-  bf16x8 Wr[STEPS];
-  bf16x8 Ur[PAIR ? STEPS : 1];
+  WT Wr[WL];
+  WT Ur[PAIR ? WL : 1];
   const bf16x8 zero8 = {};
+  const uint8_t *wb = reinterpret_cast<const uint8_t *>(a.w);
+  const uint8_t *wb2 = reinterpret_cast<const uint8_t *>(a.w2);
 
   auto kstep = [&](int chunk, int s) { return chunk * CHUNK_KS + wave * STEPS + s; };
   auto load_a = [&](int chunk, int s, int mb) -> bf16x8 {
@@ -96,27 +108,48 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
       return zero8;
     }
   };
-  // Weight load s of a step.  Whole chunks: group g = s/4 holds values [128 g, 128 g + 128)
-  // of the wave's 512 in every row, load s%4 of the group rows 4 (s%4) + l/16, 16 bytes at
-  // 16 (l%16) of the 256-byte run.  General K: the MFMA layout straight from memory.
-  auto wptr = [&](const uint16_t *base, int tile, int chunk, int s) -> const uint16_t * {
+  // Weight load s of a step.  Whole chunks: group g holds GK k-steps (a 256-byte run of
+  // every row, 128 bf16 or 256 FP8 values) of the wave's 512 values; load s%4 of the
+  // group covers rows 4 (s%4) + l/16, 16 bytes at 16 (l%16) of the run.  General K: the
+  // MFMA layout straight from memory (row l%16, 8 values at 8 (l/16)).
+  auto wptr = [&](const uint8_t *base, int tile, int chunk, int s) -> const uint8_t * {
     if constexpr (FULL) {
       const int n = min(tile * 16 + 4 * (s & 3) + (lane >> 4), N - 1);
-      return base + (long)n * K + chunk * (CHUNK_KS * 32) + wave * (STEPS * 32) + (s >> 2) * 128 + r16 * 8;
+      return base + ((long)n * K + chunk * (CHUNK_KS * 32) + wave * (STEPS * 32)) * ES + (s >> 2) * 256 + r16 * 16;
     } else {
       const int ks = min(kstep(chunk, s), nks - 1);
       const int n = min(tile * 16 + r16, N - 1);
-      return base + (long)n * K + ks * 32 + kq;
+      return base + ((long)n * K + ks * 32 + kq) * ES;
     }
+  };
+  // 8 FP8 values (one per byte, in order) to the bf16 MFMA operand (exact).
+  auto f8_bf16 = [](u32x2 v) -> bf16x8 {
+    u32x4 r;
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true));
+    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false));
+    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true));
+    return as_bf16x8(r);
+  };
+  // B operand of a general-path load
+  auto wop = [&](const WT &v) -> bf16x8 {
+    if constexpr (F8 && !FULL) return f8_bf16(v);
+    else return as_bf16x8(v);
   };
   // LDS reshaping (whole chunks): row r's 16-byte chunk c of a group sits at chunk c ^ r.
   uint8_t *tw = tbuf + (FULL ? wave * NW * 4096 : 0);
-  auto put4 = [&](uint8_t *slot, int i, bf16x8 v) {  // load i of a group, this lane's 16 bytes
+  auto put4 = [&](uint8_t *slot, int i, const u32x4 &v) {  // load i of a group, this lane's 16 bytes
     const int r = 4 * i + (lane >> 4);
-    *reinterpret_cast<bf16x8 *>(slot + r * 256 + ((r16 ^ r) << 4)) = v;
+    *reinterpret_cast<u32x4 *>(slot + r * 256 + ((r16 ^ r) << 4)) = v;
   };
   auto frag = [&](const uint8_t *slot, int j) -> bf16x8 {  // B operand of k-step j of a group
-    return *reinterpret_cast<const bf16x8 *>(slot + r16 * 256 + ((((4 * j) + (lane >> 4)) ^ r16) << 4));
+    if constexpr (F8) {
+      const int q = lane >> 4;  // 8 bytes at 32 j + 8 q of row r16
+      return f8_bf16(*reinterpret_cast<const u32x2 *>(slot + r16 * 256 + ((((2 * j) + (q >> 1)) ^ r16) << 4) +
+                                                      (q & 1) * 8));
+    } else {
+      return *reinterpret_cast<const bf16x8 *>(slot + r16 * 256 + ((((4 * j) + (lane >> 4)) ^ r16) << 4));
+    }
   };
 
   // statistics of the row this thread reduces (EPI_LOGITS)
@@ -127,15 +160,23 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
   const int e_m = e_mb * 16 + 4 * (e_ln >> 4) + e_r;
   const int e_n16 = e_ln & 15;
 
+  if constexpr (F8) {
+    // row scales of this workgroup's columns (the launcher checks they fit)
+    const int n0 = t_begin * 16, cols = min(N, t_end * 16) - n0;
+    for (int i = threadIdx.x; i < cols; i += blockDim.x) {
+      sscale[i] = a.wscale[n0 + i];
+      if constexpr (PAIR) sscale[F8_MAX_COLS + i] = a.wscale2[n0 + i];
+    }
+  }
   if (nsteps > 0) {
 #pragma unroll
     for (int s = 0; s < STEPS; ++s)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) A[mb][s] = load_a(0, s, mb);
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-      Wr[s] = ldw(wptr(a.w, t_begin, 0, s));
-      if constexpr (PAIR) Ur[s] = ldw(wptr(a.w2, t_begin, 0, s));
+    for (int s = 0; s < WL; ++s) {
+      Wr[s] = ldw(wptr(wb, t_begin, 0, s));
+      if constexpr (PAIR) Ur[s] = ldw(wptr(wb2, t_begin, 0, s));
     }
   }
 
@@ -155,7 +196,7 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
     }
     if constexpr (FULL) {
 #pragma unroll
-      for (int g = 0; g < STEPS / 4; ++g) {
+      for (int g = 0; g < STEPS / GK; ++g) {
         // the group's 4 loads (per stream) into this wave's slot, then refill them
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -165,18 +206,19 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
         if constexpr (PF) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            Wr[4 * g + i] = ldw(wptr(a.w, ntile, nc, 4 * g + i));
-            if constexpr (PAIR) Ur[4 * g + i] = ldw(wptr(a.w2, ntile, nc, 4 * g + i));
+            Wr[4 * g + i] = ldw(wptr(wb, ntile, nc, 4 * g + i));
+            if constexpr (PAIR) Ur[4 * g + i] = ldw(wptr(wb2, ntile, nc, 4 * g + i));
           }
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int ks = 4 * g + j;
+        for (int j = 0; j < GK; ++j) {
+          const int ks = GK * g + j;
           const bf16x8 bw = frag(tw, j);
+          bf16x8 bu = bw;
+          if constexpr (PAIR) bu = frag(tw + 4096, j);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
             if constexpr (PAIR) {
-              const bf16x8 bu = frag(tw + 4096, j);
               acc[2 * mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][ks], bw, acc[2 * mb], 0, 0, 0);
               acc[2 * mb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][ks], bu, acc[2 * mb + 1], 0, 0, 0);
             } else {
@@ -196,16 +238,16 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         if constexpr (PAIR) {
-          acc[2 * mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][s], Wr[s], acc[2 * mb], 0, 0, 0);
+          acc[2 * mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][s], wop(Wr[s]), acc[2 * mb], 0, 0, 0);
           acc[2 * mb + 1] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][s], Ur[s], acc[2 * mb + 1], 0, 0, 0);
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][s], wop(Ur[s]), acc[2 * mb + 1], 0, 0, 0);
         } else {
-          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][s], Wr[s], acc[mb], 0, 0, 0);
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb][s], wop(Wr[s]), acc[mb], 0, 0, 0);
         }
       }
       if constexpr (PF) {
-        Wr[s] = ldw(wptr(a.w, ntile, nc, s));
-        if constexpr (PAIR) Ur[s] = ldw(wptr(a.w2, ntile, nc, s));
+        Wr[s] = ldw(wptr(wb, ntile, nc, s));
+        if constexpr (PAIR) Ur[s] = ldw(wptr(wb2, ntile, nc, s));
         if constexpr (RELOAD_A) {
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) A[mb][s] = load_a(nc, s, mb);
@@ -241,6 +283,10 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
       }
       if (m < M && n < N) {
         const int bc = n - t_begin * 16;  // column within the workgroup's range
+        if constexpr (F8) {
+          v0 *= sscale[bc];
+          if constexpr (PAIR) v1 *= sscale[F8_MAX_COLS + bc];
+        }
         if constexpr (EPI == EPI_LOGITS) {
           if (a.logits) {
             if (a.buf_cols) obuf[m * a.buf_cols + bc] = v0;
@@ -303,29 +349,31 @@ int stream_grid(const GemmArgs &a, int epi) {
 constexpr size_t LDS_PER_CU = 160 * 1024;
 constexpr size_t OBUF_MAX = 96 * 1024;
 
-template <int MB, int EPI, int KM>
+template <int MB, int EPI, int KM, bool F8>
 constexpr size_t stream_static_lds() {
   constexpr size_t nacc = EPI == EPI_SWIGLU ? 2 * MB : MB;
+  constexpr size_t nw = EPI == EPI_SWIGLU ? 2 : 1;
   constexpr size_t red = 2 * WAVES * nacc * 4 * 64 * sizeof(float);
-  constexpr size_t tb = KM != 0 ? (size_t)WAVES * (EPI == EPI_SWIGLU ? 2 : 1) * 4096 : 16;
-  return red + tb;
+  constexpr size_t tb = KM != 0 ? (size_t)WAVES * nw * 4096 : 16;
+  constexpr size_t sc = F8 ? nw * F8_MAX_COLS * sizeof(float) : sizeof(float);
+  return red + tb + sc;
 }
 
-template <int MB, int EPI, int KM>
+template <int MB, int EPI, int KM, bool F8>
 hipError_t launch_one(GemmArgs a, int grid, hipStream_t st) {
-  constexpr size_t dyn_max = LDS_PER_CU - stream_static_lds<MB, EPI, KM>() < OBUF_MAX
-                                 ? LDS_PER_CU - stream_static_lds<MB, EPI, KM>()
-                                 : OBUF_MAX;
+  constexpr size_t stat = stream_static_lds<MB, EPI, KM, F8>();
+  constexpr size_t dyn_max = LDS_PER_CU - stat < OBUF_MAX ? LDS_PER_CU - stat : OBUF_MAX;
   const int ntiles = (a.N + 15) / 16;
   const int cols = 16 * ((ntiles + grid - 1) / grid);
+  if (F8 && cols > F8_MAX_COLS) return hipErrorInvalidValue;
   const size_t esz = EPI == EPI_LOGITS ? 4 : 2;
   size_t shm = (size_t)MB * 16 * cols * esz;
   a.buf_cols = 0;
   if (shm <= dyn_max && (EPI != EPI_LOGITS || a.logits)) {
     a.buf_cols = cols;
-    static bool attr_set = false;  // one instantiation per (MB, EPI, KM)
+    static bool attr_set = false;  // one instantiation per (MB, EPI, KM, F8)
     if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_stream<MB, EPI, KM>),
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_stream<MB, EPI, KM, F8>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_max);
       if (e != hipSuccess) return e;
       attr_set = true;
@@ -333,29 +381,38 @@ hipError_t launch_one(GemmArgs a, int grid, hipStream_t st) {
   } else {
     shm = 0;
   }
-  hipLaunchKernelGGL((k_stream<MB, EPI, KM>), dim3(grid), dim3(512), shm, st, a);
+  hipLaunchKernelGGL((k_stream<MB, EPI, KM, F8>), dim3(grid), dim3(512), shm, st, a);
   return hipGetLastError();
 }
 
-template <int KM>
+template <int KM, bool F8>
 hipError_t launch_stream_t(const GemmArgs &a, int epi, int grid, hipStream_t st) {
   const bool two = a.M > 16;
   switch (epi) {
     case EPI_LOGITS:
-      return two ? launch_one<2, EPI_LOGITS, KM>(a, grid, st) : launch_one<1, EPI_LOGITS, KM>(a, grid, st);
+      return two ? launch_one<2, EPI_LOGITS, KM, F8>(a, grid, st) : launch_one<1, EPI_LOGITS, KM, F8>(a, grid, st);
     case EPI_SWIGLU:
-      return launch_one<1, EPI_SWIGLU, KM>(a, grid, st);
+      return launch_one<1, EPI_SWIGLU, KM, F8>(a, grid, st);
     case EPI_RESID:
-      return two ? launch_one<2, EPI_RESID, KM>(a, grid, st) : launch_one<1, EPI_RESID, KM>(a, grid, st);
+      return two ? launch_one<2, EPI_RESID, KM, F8>(a, grid, st) : launch_one<1, EPI_RESID, KM, F8>(a, grid, st);
     default:
       return hipErrorInvalidValue;
   }
 }
 
+template <bool F8>
+hipError_t launch_stream_q(const GemmArgs &a, int epi, int grid, hipStream_t st) {
+  if (a.K == CHUNK_KS * 32) return launch_stream_t<1, F8>(a, epi, grid, st);
+  if (a.K % (CHUNK_KS * 32) == 0) return launch_stream_t<2, F8>(a, epi, grid, st);
+  return launch_stream_t<0, F8>(a, epi, grid, st);
+}
+
 hipError_t launch_gemm_stream(const GemmArgs &a, int epi, int grid, hipStream_t st) {
-  if (a.K == CHUNK_KS * 32) return launch_stream_t<1>(a, epi, grid, st);
-  if (a.K % (CHUNK_KS * 32) == 0) return launch_stream_t<2>(a, epi, grid, st);
-  return launch_stream_t<0>(a, epi, grid, st);
+  if (a.wfp8) {
+    if (!a.wscale || (epi == EPI_SWIGLU && !a.wscale2)) return hipErrorInvalidValue;
+    return launch_stream_q<true>(a, epi, grid, st);
+  }
+  return launch_stream_q<false>(a, epi, grid, st);
 }
 
 }  // namespace sv

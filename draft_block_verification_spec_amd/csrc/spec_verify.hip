@@ -83,12 +83,25 @@ struct Plan {
 
 bool valid_weights(const sv_weights *w) {
   if (!w || !w->w_lm) return false;
+  if (w->wtype != SV_WEIGHTS_BF16 && w->wtype != SV_WEIGHTS_FP8_E4M3) return false;
+  if (w->wtype == SV_WEIGHTS_FP8_E4M3) {
+    if (!w->s_lm) return false;
+    if (w->d_ff > 0 && (!w->s_gate || !w->s_up || !w->s_down)) return false;
+  }
   if (w->d <= 0 || (w->d % 64) != 0) return false;
   if (w->V < 1 || w->V > (1 << 19)) return false;  // sampling keeps at most 256 chunks of 2048 tokens
   if (w->d_ff < 0 || (w->d_ff % 64) != 0) return false;
   const bool has = w->d_ff > 0;
   if (has != (w->w_gate != nullptr) || has != (w->w_up != nullptr) || has != (w->w_down != nullptr)) return false;
   return true;
+}
+
+// FP8 weights run on the weight-streaming kernel only, which stages the row scales of
+// a workgroup's whole column range (at most 2048 columns).
+bool fp8_ok(const Gemm &g, int N) {
+  if (!g.stream || g.grid < 1) return false;
+  const int ntiles = (N + 15) / 16;
+  return 16 * ((ntiles + g.grid - 1) / g.grid) <= 2048;
 }
 
 bool make_plan(int mode, int B, int K, const sv_weights *w, int budget, Plan &p) {
@@ -107,7 +120,7 @@ bool make_plan(int mode, int B, int K, const sv_weights *w, int budget, Plan &p)
     p.o_sums = take(sizeof(float) * 2 * (size_t)B * sample_chunks(V));
     p.o_sync = take(sizeof(int32_t) * (size_t)(B + 1));
     p.total = off;
-    return true;
+    return w->wtype != SV_WEIGHTS_FP8_E4M3 || fp8_ok(p.lm, V);
   }
   int M_mlp;
   if (mode == SV_MODE_SCHEDULED) {
@@ -157,6 +170,11 @@ bool make_plan(int mode, int B, int K, const sv_weights *w, int budget, Plan &p)
     p.o_hp = take(2 * (size_t)p.budget * d);
   }
   p.total = off;
+  if (w->wtype == SV_WEIGHTS_FP8_E4M3) {
+    if (!fp8_ok(p.lm, V)) return false;
+    if (w->d_ff > 0 && (!fp8_ok(p.gu, w->d_ff) || !fp8_ok(p.dn, d))) return false;
+    if (mode == SV_MODE_SCHEDULED && p.rows_d > 0 && !fp8_ok(p.s1, V)) return false;
+  }
   return true;
 }
 
@@ -206,13 +224,23 @@ GemmArgs base_args() {
 }
 
 // S3 + S4: a = bf16(silu(h W_gate^T) * (h W_up^T)), y = bf16(h + a W_down^T).
+// Weights of one product: bf16 bit patterns, or FP8 codes and their row scales.
+void set_w(GemmArgs &g, const void *wt, const float *sc, const void *wt2, const float *sc2, int32_t wtype) {
+  g.w = static_cast<const uint16_t *>(wt);
+  g.w2 = static_cast<const uint16_t *>(wt2);
+  g.wfp8 = wtype == SV_WEIGHTS_FP8_E4M3;
+  g.wscale = g.wfp8 ? sc : nullptr;
+  g.wscale2 = g.wfp8 ? sc2 : nullptr;
+}
+void set_lm(GemmArgs &g, const sv_weights *w) { set_w(g, w->w_lm, w->s_lm, nullptr, nullptr, w->wtype); }
+
 hipError_t run_mlp(const Plan &p, const sv_weights *w, const uint16_t *h, int M, const int *M_dev, uint16_t *y,
                    void *ws, int32_t *status_reset, hipStream_t st) {
   uint16_t *abuf = at<uint16_t>(ws, p.o_a);
   GemmArgs g = base_args();
   g.x1 = h; g.ldx1 = p.d; g.m1 = M; g.x2 = h; g.ldx2 = p.d;
   g.M = M; g.M_dev = M_dev; g.N = p.d_ff; g.K = p.d;
-  g.w = w->w_gate; g.w2 = w->w_up;
+  set_w(g, w->w_gate, w->s_gate, w->w_up, w->s_up, w->wtype);
   g.out = abuf; g.ldo = p.d_ff;
   g.partial = p.gu.splits > 1 ? at<float>(ws, p.o_part) : nullptr;
   g.status_reset = status_reset;
@@ -221,7 +249,7 @@ hipError_t run_mlp(const Plan &p, const sv_weights *w, const uint16_t *h, int M,
   GemmArgs dn = base_args();
   dn.x1 = abuf; dn.ldx1 = p.d_ff; dn.m1 = M; dn.x2 = abuf; dn.ldx2 = p.d_ff;
   dn.M = M; dn.M_dev = M_dev; dn.N = p.d; dn.K = p.d_ff;
-  dn.w = w->w_down;
+  set_w(dn, w->w_down, w->s_down, nullptr, nullptr, w->wtype);
   dn.out = y; dn.ldo = p.d; dn.resid = h; dn.ldr = p.d;
   dn.partial = p.dn.splits > 1 ? at<float>(ws, p.o_part) : nullptr;
   return run_gemm(p.dn, dn, EPI_RESID, st);
@@ -269,7 +297,7 @@ SV_API int spec_verify_greedy(const sv_weights *w, const uint16_t *h, const int3
   }
   GemmArgs g = base_args();
   g.x1 = y; g.ldx1 = p.d; g.m1 = p.M_t; g.x2 = y; g.ldx2 = p.d;
-  g.M = p.M_t; g.N = p.V; g.K = p.d; g.w = w->w_lm;
+  g.M = p.M_t; g.N = p.V; g.K = p.d; set_lm(g, w);
   g.logits = out->logits; g.ldl = p.V;
   g.parts = at<StatPart>(ws, p.o_parts); g.nslots = p.lm.nslots;
   g.invT = 1.f; g.want_s = out->diag ? 1 : 0;
@@ -312,7 +340,7 @@ SV_API int spec_verify_sample(const sv_weights *w, const uint16_t *h, const uint
   float *logits = out->logits ? out->logits : at<float>(ws, p.o_logits);
   GemmArgs g = base_args();
   g.x1 = y; g.ldx1 = p.d; g.m1 = p.M_t; g.x2 = K > 0 ? h_draft : y; g.ldx2 = p.d;
-  g.M = p.M_lm; g.N = p.V; g.K = p.d; g.w = w->w_lm;
+  g.M = p.M_lm; g.N = p.V; g.K = p.d; set_lm(g, w);
   g.logits = logits; g.ldl = p.V;
   g.parts = at<StatPart>(ws, p.o_parts); g.nslots = p.lm.nslots;
   g.invT = invT; g.want_s = 1;
@@ -367,7 +395,7 @@ SV_API int spec_verify_scheduled(const sv_weights *w, const uint16_t *h, const u
   if (rows_d > 0) {
     GemmArgs g = base_args();
     g.x1 = h_draft; g.ldx1 = p.d; g.m1 = rows_d; g.x2 = h_draft; g.ldx2 = p.d;
-    g.M = rows_d; g.N = p.V; g.K = p.d; g.w = w->w_lm;
+    g.M = rows_d; g.N = p.V; g.K = p.d; set_lm(g, w);
     g.logits = logits_d; g.ldl = p.V;
     g.parts = parts_d; g.nslots = p.s1.nslots;
     g.invT = invT; g.want_s = 1;
@@ -397,7 +425,7 @@ SV_API int spec_verify_scheduled(const sv_weights *w, const uint16_t *h, const u
   float *logits_t = at<float>(ws, p.o_logits);
   GemmArgs g = base_args();
   g.x1 = y; g.ldx1 = p.d; g.m1 = p.budget; g.x2 = y; g.ldx2 = p.d;
-  g.M = p.budget; g.M_dev = mtot; g.N = p.V; g.K = p.d; g.w = w->w_lm;
+  g.M = p.budget; g.M_dev = mtot; g.N = p.V; g.K = p.d; set_lm(g, w);
   g.logits = logits_t; g.ldl = p.V;
   g.parts = at<StatPart>(ws, p.o_parts); g.nslots = p.lm.nslots;
   g.invT = invT; g.want_s = 1;
@@ -442,7 +470,7 @@ SV_API int spec_draft_propose(const sv_weights *w, const uint16_t *h_draft, cons
   float *logits = at<float>(ws, p.o_logits);
   GemmArgs g = base_args();
   g.x1 = h_draft; g.ldx1 = p.d; g.m1 = rows; g.x2 = h_draft; g.ldx2 = p.d;
-  g.M = rows; g.N = p.V; g.K = p.d; g.w = w->w_lm;
+  g.M = rows; g.N = p.V; g.K = p.d; set_lm(g, w);
   g.logits = samp ? logits : nullptr; g.ldl = p.V;
   g.parts = at<StatPart>(ws, p.o_parts); g.nslots = p.lm.nslots;
   g.invT = invT; g.want_s = samp ? 1 : 0;

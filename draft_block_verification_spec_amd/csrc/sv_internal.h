@@ -15,6 +15,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Per-row partial statistics of a logit row over a subset of its columns:
 // b1 = max z, b2 = second largest z, i1 = lowest column index attaining b1,
@@ -63,6 +64,11 @@ struct GemmArgs {
   int32_t *counter_reset;  // counter_reset[0 .. counter_reset_n) are zeroed (n >= 1 when set)
   int counter_reset_n;
   int buf_cols;  // set by the streaming launcher: columns of the per-workgroup output buffer
+  // FP8 (E4M3) weights: w / w2 hold one code per element and every output row n is
+  // multiplied by wscale[n] (w) / wscale2[n] (w2); weight-streaming kernel only
+  int wfp8;
+  const float *wscale;
+  const float *wscale2;
 };
 
 // Sampling job: draw v from w_v = max(0, exp(z1_v*invT - lse1) - [z2 ? exp(z2_v*invT - lse2) : 0])

@@ -199,3 +199,24 @@ def generate(w: Workload, repeat: int = 0, *, weights: bool = True, keep_f32: bo
     out["sigma"] = sigma
     out["gain"] = gain
     return out
+
+
+def to_fp8(data: dict) -> dict:
+    """FP8 copy of a batch's weights: for every matrix (``lm``, ``gate``, ``up``,
+    ``down``) one fp32 scale per output row, ``s = max|w_row| / 448``, and the E4M3
+    codes of ``w / s`` (``q_*``, uint8, rounded to nearest even by torch's float8
+    conversion).  The bf16 weights are dropped; activations and coins are kept."""
+    import torch
+
+    out = {k: v for k, v in data.items() if not k.startswith("w_")}
+    for name in ("lm", "gate", "up", "down"):
+        bits = data.get("w_" + name)
+        if bits is None:
+            continue
+        w = torch.from_numpy(np.ascontiguousarray(bits).astype(np.int32) << 16).view(torch.float32)
+        amax = w.abs().amax(dim=1).clamp_min(torch.finfo(torch.float32).tiny)
+        scale = (amax / 448.0).to(torch.float32)
+        q = (w / scale[:, None]).to(torch.float8_e4m3fn)
+        out["q_" + name] = q.view(torch.uint8).numpy()
+        out["s_" + name] = scale.numpy()
+    return out

@@ -83,14 +83,28 @@ extern "C" {
  * [7] reserved (0) */
 #define SV_DIAG_COLS 8
 
+#define SV_WEIGHTS_BF16 0     /* bf16 weights (uint16 bit patterns) */
+#define SV_WEIGHTS_FP8_E4M3 1 /* 8-bit E4M3 codes (uint8) with one fp32 scale per output row */
+
+/* Weights, row-major [out, in].  FP8 weights (reading of the pages' FP8 serving: the
+ * OCP 8-bit E4M3 format, one fp32 scale per output row, bf16 activations) stand for
+ * decode(code) * scale[row] and are supported when every product of the call streams
+ * its weights (at most 16 target rows with an MLP, at most 32 rows through the LM
+ * head, e.g. one 16-token block); other calls return SV_EINVAL, and
+ * sv_workspace_bytes returns 0 for them. */
 typedef struct sv_weights {
-  const uint16_t *w_gate; /* [d_ff, d]; NULL iff d_ff == 0 */
-  const uint16_t *w_up;   /* [d_ff, d]; NULL iff d_ff == 0 */
-  const uint16_t *w_down; /* [d, d_ff]; NULL iff d_ff == 0 */
-  const uint16_t *w_lm;   /* [V, d] shared LM head */
-  int32_t d;              /* hidden size, multiple of 64 */
-  int32_t d_ff;           /* MLP width, multiple of 64, or 0 */
-  int32_t V;              /* vocabulary, 1 <= V <= 524288 */
+  const void *w_gate; /* [d_ff, d]; NULL iff d_ff == 0 */
+  const void *w_up;   /* [d_ff, d]; NULL iff d_ff == 0 */
+  const void *w_down; /* [d, d_ff]; NULL iff d_ff == 0 */
+  const void *w_lm;   /* [V, d] shared LM head */
+  int32_t d;          /* hidden size, multiple of 64 */
+  int32_t d_ff;       /* MLP width, multiple of 64, or 0 */
+  int32_t V;          /* vocabulary, 1 <= V <= 524288 */
+  int32_t wtype;      /* SV_WEIGHTS_*; 0 (bf16) when the struct is zero-initialised */
+  const float *s_gate; /* FP8: [d_ff] scales of w_gate rows (else ignored) */
+  const float *s_up;   /* FP8: [d_ff] */
+  const float *s_down; /* FP8: [d] */
+  const float *s_lm;   /* FP8: [V] */
 } sv_weights;
 
 typedef struct sv_outputs {

@@ -5,7 +5,7 @@ leg of the benchmark may import this package; the library never does, and the
 oracle never imports the library.  It shares no code with the GPU path.
 """
 from .verify import (  # noqa: F401
-    Weights, bf16_rne, from_bf16_bits, silu, target_hidden, lm_logits, softmax_t, row_stats,
+    Weights, bf16_rne, from_bf16_bits, from_e4m3_bits, silu, target_hidden, lm_logits, softmax_t, row_stats,
     inverse_cdf, accept_sample, accept_greedy, propose, survival_schedule,
     verify_greedy, verify_sample, verify_scheduled,
 )

@@ -36,6 +36,12 @@ R1 the verified tail is a residual SwiGLU MLP followed by the LM head, the LM
    probability, survival = running product, budget filled by descending
    floor(1024 * survival), then request, then position.
 
+R8 FP8 weights (the pages serve FP8 targets: [WB] production model and the
+   table of off-the-shelf drafters; [VLLM26] "Frequently asked questions";
+   [MISHA] "Why is generation slow?" on weight bytes per token) are read as the
+   OCP 8-bit E4M3 format with one fp32 scale per output channel (weight row);
+   activations stay bf16, so an FP8 weight matrix is exactly decode(q) * scale.
+
 Parity unpinned: the MLP weight scale and the 1/1024 key grid of the scheduler
 are readings, not values the pages fix.
 """
@@ -65,6 +71,22 @@ def bf16_rne(x) -> np.ndarray:
     return np.ldexp(np.rint(np.ldexp(f, 8)), e - 8)
 
 
+def from_e4m3_bits(codes) -> np.ndarray:
+    """Decode 8-bit E4M3 codes (uint8) exactly to float64 (reading R8).
+
+    Bit layout s eeee mmm with exponent bias 7: exponent field e > 0 gives
+    (-1)^s * (1 + m/8) * 2**(e - 7); e = 0 gives the subnormal (-1)^s * m/8 * 2**-6.
+    There is no infinity; s 1111 111 is NaN.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = (c >> 7) & 1
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(s == 1, -mag, mag)
+
+
 def silu(x) -> np.ndarray:
     """x * sigmoid(x) = x / (1 + exp(-x))."""
     x = np.asarray(x, dtype=np.float64)
@@ -76,7 +98,7 @@ def silu(x) -> np.ndarray:
 
 @dataclass
 class Weights:
-    """fp64 copies of the bf16 weights, row-major ``[out, in]``."""
+    """fp64 values of the weights (bf16, or FP8 times its row scales), row-major ``[out, in]``."""
 
     w_lm: np.ndarray                   # [V, d]
     w_gate: np.ndarray | None = None   # [d_ff, d]
@@ -90,6 +112,16 @@ class Weights:
                    None if g is None else from_bf16_bits(g),
                    None if g is None else from_bf16_bits(data["w_up"]),
                    None if g is None else from_bf16_bits(data["w_down"]))
+
+    @classmethod
+    def from_fp8(cls, data: dict) -> "Weights":
+        """FP8 weights (reading R8): W = decode(q_*) * s_*[:, None] for every matrix."""
+        def mat(name):
+            q = data.get("q_" + name)
+            if q is None:
+                return None
+            return from_e4m3_bits(q) * np.asarray(data["s_" + name], dtype=np.float64)[:, None]
+        return cls(mat("lm"), mat("gate"), mat("up"), mat("down"))
 
 
 def target_hidden(h, w: Weights) -> np.ndarray:

@@ -38,6 +38,18 @@ def dev_weights(data: dict, device="cuda") -> bd.Weights:
                       None if g is None else dev_bf16(data["w_down"], device))
 
 
+def dev_fp8_weights(data: dict, device="cuda") -> bd.Weights:
+    """FP8 codes (uint8) and fp32 row scales of ``workload.to_fp8`` on the device."""
+    def q(n):
+        a = data.get("q_" + n)
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+    def s(n):
+        a = data.get("s_" + n)
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+    return bd.Weights(q("lm"), q("gate"), q("up"), q("down"), s("lm"), s("gate"), s("up"), s("down"))
+
+
 def oracle_drafts(W: oracle.Weights, data: dict, T: float, rows=None) -> dict:
     """Draft tokens drawn by the oracle's drafter (x ~ q at T, or argmax when T == 0)."""
     hd = oracle.from_bf16_bits(data["h_draft"] if rows is None else data["h_draft"][rows])

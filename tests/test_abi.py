@@ -138,3 +138,30 @@ def test_entry_points_reject_small_workspace(lib):
     # misaligned workspace
     assert lib.spec_verify_greedy(ctypes.byref(w), P, P, 2, 7, (1 << 30) + 16, 1 << 40, ctypes.byref(o),
                                   None) == b.SV_EINVAL
+
+
+def _w8(**kw):
+    w = _w(**{k: v for k, v in kw.items() if k in ("d", "d_ff", "V", "mlp")})
+    w.wtype = b.SV_WEIGHTS_FP8_E4M3
+    z = 1 << 22
+    w.s_lm = 5 * z
+    if w.d_ff:
+        w.s_gate, w.s_up, w.s_down = 6 * z, 7 * z, 8 * z
+    for k, v in kw.items():
+        if k.startswith("s_") or k == "wtype":
+            setattr(w, k, v)
+    return w
+
+
+def test_fp8_weights_workspace_rules(lib):
+    # one 16-token block streams every product: supported
+    assert lib.sv_workspace_bytes(b.SV_MODE_SAMPLE, 1, 15, ctypes.byref(_w8())) > 0
+    assert lib.sv_workspace_bytes(b.SV_MODE_GREEDY, 1, 15, ctypes.byref(_w8())) > 0
+    assert lib.sv_workspace_bytes(b.SV_MODE_PROPOSE, 15, 0, ctypes.byref(_w8())) > 0
+    # batches past the streaming kernel's rows, missing scales, unknown weight types: rejected
+    assert lib.sv_workspace_bytes(b.SV_MODE_GREEDY, 8, 7, ctypes.byref(_w8())) == 0
+    assert lib.sv_workspace_bytes(b.SV_MODE_SAMPLE, 1, 15, ctypes.byref(_w8(s_lm=None))) == 0
+    assert lib.sv_workspace_bytes(b.SV_MODE_SAMPLE, 1, 15, ctypes.byref(_w8(s_down=None))) == 0
+    assert lib.sv_workspace_bytes(b.SV_MODE_SAMPLE, 1, 15, ctypes.byref(_w8(wtype=7))) == 0
+    # without an MLP only the LM-head scales are needed
+    assert lib.sv_workspace_bytes(b.SV_MODE_SAMPLE, 1, 15, ctypes.byref(_w8(mlp=False, d_ff=0))) > 0

@@ -1,0 +1,80 @@
+"""GPU parity with FP8 weights (reading R8: E4M3 codes, one fp32 scale per output row).
+
+The oracle decodes the same codes exactly and multiplies by the row scales
+(``oracle.Weights.from_fp8``); the library streams the codes, converts them to bf16
+MFMA operands and scales each output row after the reduction.  Shapes: the full
+16-token block (whole 4096-value chunks of K) and reduced shapes whose K is not a
+multiple of 4096 (the general streaming path), all within the rows the
+weight-streaming kernel takes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from draft_block_verification_spec_amd import binding as bd
+from draft_block_verification_spec_amd import workload as wl
+from tests import parity as pt
+from tests.test_gpu_parity import _run_greedy, _run_sample
+
+pytestmark = pytest.mark.gpu
+
+# reduced shapes with at most 16 target rows (MLP) and 32 LM-head rows
+SMALL8 = [wl.SMALL.with_batch(2), wl.SMALL_WIDE.with_batch(3), wl.TINY.with_batch(3)]
+
+
+@pytest.mark.parametrize("wk", SMALL8, ids=lambda w: f"{w.name}-B{w.B}")
+def test_fp8_sample_reduced(wk):
+    _run_sample(wk, fp8=True)
+
+
+@pytest.mark.parametrize("wk", SMALL8, ids=lambda w: f"{w.name}-B{w.B}")
+def test_fp8_greedy_reduced(wk):
+    _run_greedy(wk, fp8=True)
+
+
+@pytest.mark.parametrize("rep", [0, 1])
+def test_fp8_block16_sample(rep):
+    _run_sample(wl.BLOCK16, rep, fp8=True)
+
+
+def test_fp8_block16_greedy():
+    _run_greedy(wl.BLOCK16, fp8=True)
+
+
+def test_fp8_propose_matches_oracle_drafter():
+    """The drafter step with FP8 weights: argmax drafts and conf = 1 at T = 0; inverse-CDF
+    drafts and top-1 probabilities at the workload's temperature."""
+    wk = wl.BLOCK16
+    data = wl.to_fp8(wl.generate(wk))
+    W = oracle.Weights.from_fp8(data)
+    w = pt.dev_fp8_weights(data)
+    hd = pt.dev_bf16(data["h_draft"])
+    coins = torch.from_numpy(data["draft_coins"].astype(np.float32)).cuda()
+    for T in (wk.T, 0.0):
+        ref = pt.oracle_drafts(W, data, T)
+        x, conf = bd.spec_draft_propose(w, hd, coins, T)
+        torch.cuda.synchronize()
+        x = x.cpu().numpy()
+        conf = conf.cpu().numpy()
+        z = ref["logits"]
+        if T == 0.0:
+            sure = oracle.row_stats(z)["gap"] >= pt.GAP_BAND
+            np.testing.assert_array_equal(x[sure], ref["draft"][sure])
+            np.testing.assert_array_equal(conf, np.ones_like(conf))
+        else:
+            C = np.cumsum(oracle.softmax_t(z, T), axis=-1)
+            u = data["draft_coins"].astype(np.float64)
+            for idx in zip(*np.nonzero(x != ref["draft"])):
+                assert np.min(np.abs(C[idx] - u[idx])) < pt.CDF_BAND, f"draft token differs at {idx}"
+            np.testing.assert_allclose(conf, ref["conf"], atol=pt.PROB_TOL)
+
+
+def test_fp8_rejects_batches_past_the_streaming_kernel():
+    """FP8 weights on a batch whose products would not stream (64 target rows): invalid."""
+    wk = wl.SMALL.with_batch(8)
+    data = wl.to_fp8(wl.generate(wk))
+    w = pt.dev_fp8_weights(data)
+    draft = torch.zeros(wk.B, wk.K, dtype=torch.int32, device="cuda")
+    with pytest.raises(bd.SpecVerifyError):
+        bd.spec_verify_greedy(w, pt.dev_bf16(data["h"]), draft)

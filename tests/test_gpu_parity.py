@@ -29,22 +29,32 @@ def _check_hidden(out_hidden, ref_y, rows):
     ref = ref_y.reshape(rows, -1)
     diff = np.abs(got - ref)
     # A one-ulp flip of an intermediate `a` moves y by |W_down| * ulp(a) ~ 1e-4 before y's own
-    # rounding, so y may differ by one of its ulps plus that amount, and only rarely.
+    # rounding, so y may differ by one of its ulps plus that amount, and only rarely: the fp32
+    # sums over K terms carry a relative error of about sqrt(K) * 2**-24 (6.6e-6 at K = 12288),
+    # and a value within that distance of a bf16 rounding boundary (ulp 2**-8 relative) rounds
+    # the other way with probability ~ 2 * 6.6e-6 / 2**-8 = 3.4e-3.
     ulp = np.abs(ref) * 2.0 ** -7
     assert np.all(diff <= ulp * 1.01 + 1e-3), f"MLP output differs by {diff.max()}"
-    assert np.mean(diff > 0) < 2e-3, f"too many bf16 rounding flips: {np.mean(diff > 0)}"
+    assert np.mean(diff > 0) < 5e-3, f"too many bf16 rounding flips: {np.mean(diff > 0)}"
 
 
-def _run_sample(wk, rep=0, check_hidden=True):
+def _weights(wk, rep, fp8):
+    """Inputs, oracle weights and device weights (bf16, or FP8 codes + row scales)."""
     data = wl.generate(wk, rep)
-    W = oracle.Weights.from_bits(data)
+    if fp8:
+        data = wl.to_fp8(data)
+        return data, oracle.Weights.from_fp8(data), pt.dev_fp8_weights(data)
+    return data, oracle.Weights.from_bits(data), pt.dev_weights(data)
+
+
+def _run_sample(wk, rep=0, check_hidden=True, fp8=False):
+    data, W, w = _weights(wk, rep, fp8)
     T = wk.T
     draft = pt.oracle_drafts(W, data, T)["draft"]
     h64 = oracle.from_bf16_bits(data["h"])
     hd64 = oracle.from_bf16_bits(data["h_draft"])
     coins = data["coins"].astype(np.float64)
     ref = oracle.verify_sample(W, h64, hd64, draft, coins, T)
-    w = pt.dev_weights(data)
     out = bd.spec_verify_sample(w, pt.dev_bf16(data["h"]), pt.dev_bf16(data["h_draft"]), _i32(draft),
                                 _f32(data["coins"]), T, diag=True, logits=True, hidden=wk.d_ff > 0)
     torch.cuda.synchronize()
@@ -89,12 +99,10 @@ def test_sample_parity_tiny_steps():
     _run_sample(wl.TINY.with_batch(2000))
 
 
-def _run_greedy(wk, rep=0):
-    data = wl.generate(wk, rep)
-    W = oracle.Weights.from_bits(data)
+def _run_greedy(wk, rep=0, fp8=False):
+    data, W, w = _weights(wk, rep, fp8)
     draft = pt.oracle_drafts(W, data, 0.0)["draft"]
     ref = oracle.verify_greedy(W, oracle.from_bf16_bits(data["h"]), draft)
-    w = pt.dev_weights(data)
     out = bd.spec_verify_greedy(w, pt.dev_bf16(data["h"]), _i32(draft), diag=True, logits=True,
                                 hidden=wk.d_ff > 0)
     torch.cuda.synchronize()

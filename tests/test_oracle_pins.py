@@ -93,6 +93,36 @@ def test_from_bf16_bits_exact():
     assert got[4] == (2 - 2 ** -7) * 2.0 ** 127
 
 
+def test_e4m3_decode_matches_torch_float8():
+    """The FP8 decoder (reading R8) against torch's own float8_e4m3fn conversion, all codes."""
+    codes = np.arange(256, dtype=np.uint8)
+    mine = oracle.from_e4m3_bits(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    assert np.array_equal(mine[~np.isnan(mine)], ref[~np.isnan(ref)])
+
+
+def test_e4m3_closed_forms():
+    """Values fixed by the format: bias 7, 3 mantissa bits, subnormals m/8 * 2**-6, no infinities."""
+    d = oracle.from_e4m3_bits(np.array([0x38, 0x40, 0x7E, 0x01, 0x07, 0x08, 0xB8, 0x00, 0x80, 0x7F, 0xFF],
+                                       dtype=np.uint8))
+    assert d[0] == 1.0 and d[1] == 2.0 and d[2] == 448.0
+    assert d[3] == 2.0 ** -9 and d[4] == 7 * 2.0 ** -9 and d[5] == 2.0 ** -6
+    assert d[6] == -1.0 and d[7] == 0.0 and d[8] == 0.0 and np.signbit(d[8])
+    assert np.isnan(d[9]) and np.isnan(d[10])
+    pos = oracle.from_e4m3_bits(np.arange(0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)  # codes 0..126 are the finite non-negative values in order
+
+
+def test_fp8_weights_apply_row_scales():
+    """W = decode(q) * s[row]: a 2 x 2 hand example."""
+    data = {"q_lm": np.array([[0x38, 0x40], [0xB8, 0x01]], dtype=np.uint8),
+            "s_lm": np.array([2.0, 0.5], dtype=np.float32)}
+    W = oracle.Weights.from_fp8(data)
+    assert np.array_equal(W.w_lm, np.array([[2.0, 4.0], [-0.5, 2.0 ** -10]]))
+    assert W.w_gate is None
+
+
 def test_target_hidden_hand_example():
     # d = 2, d_ff = 1: g = 2, u = 3, silu(2) * 3 = 5.28478... -> bf16 5.28125; y = bf16(h + a W_down^T)
     w = oracle.Weights(w_lm=np.eye(2), w_gate=np.array([[1.0, 0.0]]), w_up=np.array([[0.0, 1.0]]),
