@@ -213,6 +213,30 @@ def main():
                       "step_hbm_fraction": step_bytes / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS})
         log(f"block16/greedy: {msg:.3f} ms/step")
         del call_g, out_g
+        # FP8 (E4M3) weights with per-row fp32 scales, same block: one byte per weight streamed
+        d8 = wl.to_fp8(data)
+        w8 = bd.Weights(*(torch.from_numpy(np.ascontiguousarray(d8["q_" + n])).to(dev) for n in ("lm", "gate", "up", "down")),
+                        *(to_f32(d8["s_" + n]) for n in ("lm", "gate", "up", "down")))
+        del d8
+        step8 = float(wk.weight_bytes()) / 2 + 4.0 * (V + 2 * d_ff + d)
+        for m8 in ("sample", "greedy"):
+            call8, out8 = prepare(wk, data, m8, w8)
+            ms8, lm8, _, sp8 = timed(call8, out8, args.steps, args.warmup)
+            rows8 = B * (K + 1) + (B * K if m8 == "sample" else 0)
+            b8 = 1.0 * V * d + 4.0 * V + 2.0 * rows8 * d
+            extra.append({"workload": f"block16 {m8}, FP8 E4M3 weights + fp32 row scales: B=1 K=15"
+                                      + (f" T={wk.T}" if m8 == "sample" else ""),
+                          "ms_per_step": ms8, "step_ms_spread": sp8,
+                          "positions_per_sec": B * (K + 1) / (ms8 * 1e-3),
+                          "accepted_tokens_per_sec": float(out8.counters.cpu().numpy()[2]) / (ms8 * 1e-3),
+                          "tau": float(out8.tau.item()),
+                          "roofline": {"bound": "hbm", "achieved": b8 / (lm8 * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                                       "unit": "GB/s", "frac": b8 / (lm8 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                       "kernel": f"LM-head GEMM over {rows8} rows, FP8 weights", "launch_ms": lm8},
+                          "step_hbm_fraction": step8 / (ms8 * 1e-3) / 1e9 / HBM_PEAK_GBS})
+            log(f"block16/{m8} fp8: {ms8:.3f} ms/step, LM head {lm8:.3f} ms")
+            del call8, out8
+        del w8
         # the batch sweep (K = 7 greedy, same weight shapes): B = 8, 32 HBM-bound, B = 128 MFMA-bound
         for Bs in (8, 32, 128):
             wk2 = wl.SWEEP.with_batch(Bs)
