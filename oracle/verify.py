@@ -36,7 +36,7 @@ R1 the verified tail is a residual SwiGLU MLP followed by the LM head, the LM
    probability, survival = running product, budget filled by descending
    floor(1024 * survival), then request, then position.
 
-R8 FP8 weights (the pages serve FP8 targets: [WB] production model and the
+R13 FP8 weights (the pages serve FP8 targets: [WB] production model and the
    table of off-the-shelf drafters; [VLLM26] "Frequently asked questions";
    [MISHA] "Why is generation slow?" on weight bytes per token) are read as the
    OCP 8-bit E4M3 format with one fp32 scale per output channel (weight row);
@@ -72,7 +72,7 @@ def bf16_rne(x) -> np.ndarray:
 
 
 def from_e4m3_bits(codes) -> np.ndarray:
-    """Decode 8-bit E4M3 codes (uint8) exactly to float64 (reading R8).
+    """Decode 8-bit E4M3 codes (uint8) exactly to float64 (reading R13).
 
     Bit layout s eeee mmm with exponent bias 7: exponent field e > 0 gives
     (-1)^s * (1 + m/8) * 2**(e - 7); e = 0 gives the subnormal (-1)^s * m/8 * 2**-6.
@@ -115,7 +115,7 @@ class Weights:
 
     @classmethod
     def from_fp8(cls, data: dict) -> "Weights":
-        """FP8 weights (reading R8): W = decode(q_*) * s_*[:, None] for every matrix."""
+        """FP8 weights (reading R13): W = decode(q_*) * s_*[:, None] for every matrix."""
         def mat(name):
             q = data.get("q_" + name)
             if q is None:

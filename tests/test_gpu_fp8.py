@@ -1,4 +1,4 @@
-"""GPU parity with FP8 weights (reading R8: E4M3 codes, one fp32 scale per output row).
+"""GPU parity with FP8 weights (reading R13: E4M3 codes, one fp32 scale per output row).
 
 The oracle decodes the same codes exactly and multiplies by the row scales
 (``oracle.Weights.from_fp8``); the library streams the codes, converts them to bf16

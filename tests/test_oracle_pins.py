@@ -94,7 +94,7 @@ def test_from_bf16_bits_exact():
 
 
 def test_e4m3_decode_matches_torch_float8():
-    """The FP8 decoder (reading R8) against torch's own float8_e4m3fn conversion, all codes."""
+    """The FP8 decoder (reading R13) against torch's own float8_e4m3fn conversion, all codes."""
     codes = np.arange(256, dtype=np.uint8)
     mine = oracle.from_e4m3_bits(codes)
     ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
