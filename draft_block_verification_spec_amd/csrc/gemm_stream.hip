@@ -168,15 +168,47 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
       if constexpr (PAIR) sscale[F8_MAX_COLS + i] = a.wscale2[n0 + i];
     }
   }
+  // First step's operands.  The loads are issued in exactly the order in which the loop
+  // refills them (pinned with sched_barrier): the wait counts at the top of the loop are
+  // merged over the loop entry and the back edge, so any other order makes every step
+  // wait for most of its loads before the first refill, emptying the pipeline.
   if (nsteps > 0) {
+    if constexpr (!RELOAD_A) {
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s)
+      for (int s = 0; s < STEPS; ++s)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) A[mb][s] = load_a(0, s, mb);
+        for (int mb = 0; mb < MB; ++mb) A[mb][s] = load_a(0, s, mb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (FULL) {
 #pragma unroll
-    for (int s = 0; s < WL; ++s) {
-      Wr[s] = ldw(wptr(wb, t_begin, 0, s));
-      if constexpr (PAIR) Ur[s] = ldw(wptr(wb2, t_begin, 0, s));
+      for (int g = 0; g < STEPS / GK; ++g) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          Wr[4 * g + i] = ldw(wptr(wb, t_begin, 0, 4 * g + i));
+          if constexpr (PAIR) Ur[4 * g + i] = ldw(wptr(wb2, t_begin, 0, 4 * g + i));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (RELOAD_A) {
+#pragma unroll
+          for (int j = 0; j < GK; ++j) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) A[mb][GK * g + j] = load_a(0, GK * g + j, mb);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s) {
+        Wr[s] = ldw(wptr(wb, t_begin, 0, s));
+        if constexpr (PAIR) Ur[s] = ldw(wptr(wb2, t_begin, 0, s));
+        if constexpr (RELOAD_A) {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) A[mb][s] = load_a(0, s, mb);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 
@@ -326,10 +358,29 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
     const int cols = min(N, t_end * 16) - t_begin * 16;
     const int n0 = t_begin * 16;
     const int rows = min(M, MB * 16);
-    for (int idx = threadIdx.x; idx < rows * cols; idx += blockDim.x) {
-      const int m = idx / cols, c = idx % cols;
-      if constexpr (EPI == EPI_LOGITS) a.logits[(long)m * a.ldl + n0 + c] = obuf[m * a.buf_cols + c];
-      else a.out[(long)m * a.ldo + n0 + c] = reinterpret_cast<const uint16_t *>(obuf)[m * a.buf_cols + c];
+    // one wave per row; 16-byte stores when every row start is 16-byte aligned (the
+    // buffer rows are: buf_cols is a multiple of 16 values)
+    if constexpr (EPI == EPI_LOGITS) {
+      const bool vec = (a.ldl & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0;
+      for (int m = wave; m < rows; m += WAVES) {
+        float *dst = a.logits + (long)m * a.ldl + n0;
+        const float *src = obuf + m * a.buf_cols;
+        if (vec) {
+          for (int c = lane * 4; c < cols; c += 256) {
+            if (c + 4 <= cols) *reinterpret_cast<f32x4 *>(dst + c) = *reinterpret_cast<const f32x4 *>(src + c);
+            else
+              for (int i = c; i < cols; ++i) dst[i] = src[i];
+          }
+        } else {
+          for (int c = lane; c < cols; c += 64) dst[c] = src[c];
+        }
+      }
+    } else {
+      for (int m = wave; m < rows; m += WAVES) {
+        uint16_t *dst = a.out + (long)m * a.ldo + n0;
+        const uint16_t *src = reinterpret_cast<const uint16_t *>(obuf) + m * a.buf_cols;
+        for (int c = lane; c < cols; c += 64) dst[c] = src[c];
+      }
     }
   }
 }
