@@ -418,9 +418,17 @@ int tiled_slots(int N, int bn) { return ((N + bn - 1) / bn) * 2; }
 // gate/up, down at d = 4096 and 8192): the fewer the rows, the more of each slice is
 // weights, and the deeper the pipeline must be to keep HBM busy.
 TileShape tiled_shape(int M, int N, int K, int epi) {
-  (void)N;
   const bool k128 = K % 128 == 0;
-  if (epi == EPI_SWIGLU) return M <= 128 ? TileShape{128, 128, 64, 4} : TileShape{256, 128, 64, 3};
+  if (epi == EPI_SWIGLU) {
+    if (M <= 128) return TileShape{128, 128, 64, 4};
+    // 256-row tiles, one workgroup per CU either way: 256 x 256 when it needs enough fewer
+    // rounds over the CUs than 256 x 128 (a 256 x 256 tile takes ~1.7x as long as a
+    // 256 x 128 one), e.g. 512 rows: 192 tiles in one round against 384 tiles in two
+    const long tm = (M + 255) / 256, cus = num_cus();
+    const long r128 = (tm * ((2L * N + 127) / 128) + cus - 1) / cus;
+    const long r256 = (tm * ((2L * N + 255) / 256) + cus - 1) / cus;
+    return 10 * r128 <= 17 * r256 ? TileShape{256, 128, 64, 3} : TileShape{256, 256, 64, 2};
+  }
   if (epi == EPI_RESID) {
     if (M <= 64) return k128 ? TileShape{64, 128, 128, 3} : TileShape{64, 128, 64, 2};
     return M <= 256 ? TileShape{128, 256, 64, 3} : TileShape{256, 128, 64, 3};
