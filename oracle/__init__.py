@@ -9,6 +9,7 @@ from .verify import (  # noqa: F401
     inverse_cdf, accept_sample, accept_greedy, propose, survival_schedule,
     verify_greedy, verify_sample, verify_scheduled,
 )
+from .commit import commit  # noqa: F401
 from .theory import (  # noqa: F401
     expected_tokens, speedup, best_draft_length, tau_from_position_acceptance,
     conditional_acceptance, acceptance_rate, tau_closed_form, tokens_per_step,
