@@ -287,6 +287,10 @@ def main():
                                        "launch_ms": lm3}})
             log(f"{wk3.name}: {ms3:.3f} ms/step, {M3} verified rows")
             del call3, out3, d3
+        # commit after verification: the scheduled batch (B = 64, Kmax = 15) with tree-shaped
+        # blocks on a hybrid target (8 attention layers x 2 KiB entries, 1 MiB recurrent state)
+        extra.append(bench_commit(bd, torch, wl, dev, to_i32, args.steps, args.warmup))
+        log(f"commit: {extra[-1]['ms_per_call'] * 1e3:.1f} us/call")
         # the wide model (d = 8192, d_ff = 28672, V = 128256), B = 32, K = 4, T = 0.7, sampled
         wk4 = wl.WIDE
         d4 = wl.generate(wk4)
@@ -311,6 +315,48 @@ def main():
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(wk, data, mode, out, w, bd, torch)
     print(json.dumps(result), flush=True)
+
+
+def bench_commit(bd, torch, wl, dev, to_i32, steps, warmup):
+    """spec_commit on the commit workload; in place, so cache lengths are restored before
+    each call (outside its events).  Algorithmic bytes: every committed request's state
+    read from its snapshot and written, and every moved cache entry read and written."""
+    cw = wl.COMMIT
+    cc = wl.commit_case(cw, big=False)
+    K1 = cw.Kmax + 1
+    kv = torch.empty((cw.n_layers, 2, cc["n_blocks"], cw.block_size, cw.entry_bytes), dtype=torch.uint8, device=dev)
+    rs = torch.empty((cw.B, cw.rec_bytes), dtype=torch.uint8, device=dev)
+    sn = torch.empty((cw.B, K1, cw.rec_bytes), dtype=torch.uint8, device=dev)
+    seq0 = to_i32(cc["seq_len"])
+    seq = seq0.clone()
+    acc, vl, path, bt = (to_i32(cc[k]) for k in ("accepted_len", "verify_len", "path", "block_table"))
+
+    def call():
+        bd.spec_commit(acc, seq, Kmax=cw.Kmax, kv=kv, block_table=bt, rec_state=rs, rec_snap=sn, verify_len=vl,
+                       path=path)
+    for _ in range(warmup):
+        seq.copy_(seq0)
+        call()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in evs:
+        seq.copy_(seq0)
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    per = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    A = cc["accepted_len"]
+    moved = sum(int(np.sum(cc["path"][b, 1: A[b] + 1] != np.arange(1, A[b] + 1))) for b in range(cw.B) if A[b] > 0)
+    by = 2.0 * cw.rec_bytes * int((A >= 0).sum()) + 2.0 * moved * cw.n_layers * 2 * cw.entry_bytes
+    ms = float(per.mean())
+    return {"workload": f"commit: B={cw.B} Kmax={cw.Kmax} tree blocks, {cw.n_layers} attention layers x "
+                        f"{cw.entry_bytes} B entries, {cw.rec_bytes >> 20} MiB recurrent state per request",
+            "ms_per_call": ms, "call_ms_spread": {"median": float(np.median(per)), "min": float(per.min()),
+                                                  "max": float(per.max())},
+            "bytes_per_call": by,
+            "roofline": {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "kernel": "k_commit_move + k_commit_len",
+                         "launch_ms": ms}}
 
 
 def traffic_for(config, mode, lm_bytes):

@@ -19,12 +19,12 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libspecverify.so")
 
 SV_OK, SV_EINVAL, SV_EWORKSPACE, SV_EHIP = 0, -1, -2, -3
-SV_DEV_OK, SV_DEV_BAD_TOKEN, SV_DEV_NONFINITE = 0, 1, 2
+SV_DEV_OK, SV_DEV_BAD_TOKEN, SV_DEV_NONFINITE, SV_DEV_BAD_COMMIT = 0, 1, 2, 3
 SV_MODE_GREEDY, SV_MODE_SAMPLE, SV_MODE_SCHEDULED, SV_MODE_PROPOSE = 0, 1, 2, 3
 SV_DIAG_COLS = 8
 
 EXPORTS = ("sv_workspace_bytes", "spec_verify_greedy", "spec_verify_sample", "spec_verify_scheduled",
-           "spec_draft_propose", "sv_version", "sv_strerror", "sv_last_hip_error")
+           "spec_draft_propose", "spec_commit", "sv_version", "sv_strerror", "sv_last_hip_error")
 
 
 class SpecVerifyError(RuntimeError):
@@ -46,6 +46,14 @@ class SvOutputs(ctypes.Structure):
                 ("tau", ctypes.c_void_p), ("counters", ctypes.c_void_p), ("dev_status", ctypes.c_void_p),
                 ("diag", ctypes.c_void_p), ("logits", ctypes.c_void_p), ("hidden", ctypes.c_void_p),
                 ("ev_lm_begin", ctypes.c_void_p), ("ev_lm_end", ctypes.c_void_p)]
+
+
+class SvCache(ctypes.Structure):
+    _fields_ = [("kv", ctypes.c_void_p), ("layer_stride", ctypes.c_int64), ("half_stride", ctypes.c_int64),
+                ("n_layers", ctypes.c_int32), ("block_size", ctypes.c_int32), ("entry_bytes", ctypes.c_int32),
+                ("max_blocks", ctypes.c_int32), ("n_blocks", ctypes.c_int32), ("block_table", ctypes.c_void_p),
+                ("seq_len", ctypes.c_void_p), ("rec_state", ctypes.c_void_p), ("rec_snap", ctypes.c_void_p),
+                ("rec_bytes", ctypes.c_int64)]
 
 
 _lib = None
@@ -74,6 +82,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                           sz, ctypes.POINTER(SvOutputs), vp]
     lib.spec_draft_propose.restype = i32
     lib.spec_draft_propose.argtypes = [ctypes.POINTER(SvWeights), vp, vp, f32, i32, vp, sz, vp, vp, vp]
+    lib.spec_commit.restype = i32
+    lib.spec_commit.argtypes = [ctypes.POINTER(SvCache), vp, vp, vp, i32, i32, vp, vp]
     lib.sv_version.restype = ctypes.c_char_p
     lib.sv_strerror.restype = ctypes.c_char_p
     lib.sv_strerror.argtypes = [i32]
@@ -277,6 +287,39 @@ def spec_draft_propose(w: Weights, h_draft, coins, T: float, *, draft_out=None, 
                                    ws.numel(), _ptr(draft_out), _ptr(conf_out), _stream(stream))
     _raise(rc, "spec_draft_propose")
     return draft_out.view(h_draft.shape[:-1]), conf_out.view(h_draft.shape[:-1])
+
+
+def spec_commit(accepted_len, seq_len, *, Kmax: int, kv=None, block_table=None, rec_state=None, rec_snap=None,
+                verify_len=None, path=None, dev_status=None, stream=None) -> None:
+    """Commit the accepted prefix of the last verify block (in place).
+
+    kv: uint8 [n_layers, 2, n_blocks, block_size, entry_bytes] paged cache (or None);
+    block_table: int32 [B, max_blocks]; seq_len: int32 [B] (advanced); rec_state: uint8
+    [B, rec_bytes] and rec_snap: uint8 [B, Kmax+1, rec_bytes] (or both None);
+    accepted_len / verify_len: int32 [B]; path: int32 [B, Kmax+1] for a tree (or None)."""
+    _check_dev(accepted_len, torch.int32, "accepted_len")
+    _check_dev(seq_len, torch.int32, "seq_len")
+    for t, n in ((verify_len, "verify_len"), (path, "path"), (block_table, "block_table"), (dev_status, "dev_status")):
+        _check_dev(t, torch.int32, n)
+    for t, n in ((kv, "kv"), (rec_state, "rec_state"), (rec_snap, "rec_snap")):
+        _check_dev(t, torch.uint8, n)
+    B = seq_len.numel()
+    c = SvCache()
+    c.seq_len = _ptr(seq_len)
+    if kv is not None:
+        if kv.dim() != 5 or kv.shape[1] != 2 or block_table is None:
+            raise SpecVerifyError("kv must be [n_layers, 2, n_blocks, block_size, entry_bytes] with a block_table")
+        L_, _, nb, bs, eb = kv.shape
+        c.kv, c.n_layers, c.n_blocks, c.block_size, c.entry_bytes = _ptr(kv), L_, nb, bs, eb
+        c.layer_stride, c.half_stride = kv.stride(0), kv.stride(1)
+        c.block_table, c.max_blocks = _ptr(block_table), block_table.shape[-1]
+    if rec_state is not None or rec_snap is not None:
+        if rec_state is None or rec_snap is None or rec_snap.shape[:2] != (B, Kmax + 1):
+            raise SpecVerifyError("rec_state [B, n] and rec_snap [B, Kmax+1, n] go together")
+        c.rec_state, c.rec_snap, c.rec_bytes = _ptr(rec_state), _ptr(rec_snap), rec_state.shape[-1]
+    rc = load().spec_commit(ctypes.byref(c), _ptr(accepted_len), _ptr(verify_len), _ptr(path), B, int(Kmax),
+                            _ptr(dev_status), _stream(stream))
+    _raise(rc, "spec_commit")
 
 
 def version() -> str:

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libspecverify.so")
 ARCH = "gfx950"
 
-SOURCES = ["spec_verify.hip", "gemm_stream.hip", "gemm_tiled.hip", "verify_kernels.hip"]
+SOURCES = ["spec_verify.hip", "gemm_stream.hip", "gemm_tiled.hip", "verify_kernels.hip", "commit.hip"]
 
 # Packed fp32 instructions are left to no one: the compiler must not form them.
 HIPCC_FLAGS = [

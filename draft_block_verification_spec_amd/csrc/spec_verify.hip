@@ -486,6 +486,43 @@ SV_API int spec_draft_propose(const sv_weights *w, const uint16_t *h_draft, cons
   return SV_OK;
 }
 
+SV_API int spec_commit(const sv_cache *c, const int32_t *accepted_len, const int32_t *verify_len,
+                       const int32_t *path, int B, int Kmax, int32_t *dev_status, void *stream) {
+  if (!c || !accepted_len || !c->seq_len || B < 1 || Kmax < 0 || Kmax > 63) return SV_EINVAL;
+  if (c->n_layers < 0 || c->rec_bytes < 0 || c->rec_bytes % 16 != 0) return SV_EINVAL;
+  if (c->n_layers > 0) {
+    if (!c->kv || !aligned16(c->kv) || !c->block_table || c->block_size < 1 || c->max_blocks < 1 ||
+        c->n_blocks < 1 || c->entry_bytes < 16 || c->entry_bytes % 16 != 0 || c->layer_stride < 0 ||
+        c->half_stride < 0 || c->layer_stride % 16 != 0 || c->half_stride % 16 != 0)
+      return SV_EINVAL;
+  }
+  if (c->rec_bytes > 0 &&
+      (!c->rec_state || !c->rec_snap || !aligned16(c->rec_state) || !aligned16(c->rec_snap)))
+    return SV_EINVAL;
+  CommitArgs a{};
+  a.kv = static_cast<uint8_t *>(c->kv);
+  a.layer_stride = c->layer_stride;
+  a.half_stride = c->half_stride;
+  a.n_layers = c->n_layers;
+  a.block_size = c->block_size;
+  a.entry_bytes = c->entry_bytes;
+  a.max_blocks = c->max_blocks;
+  a.n_blocks = c->n_blocks;
+  a.block_table = c->block_table;
+  a.seq_len = c->seq_len;
+  a.rec_state = static_cast<uint8_t *>(c->rec_state);
+  a.rec_snap = static_cast<const uint8_t *>(c->rec_snap);
+  a.rec_bytes = c->rec_bytes;
+  a.accepted_len = accepted_len;
+  a.verify_len = verify_len;
+  a.path = path;
+  a.B = B;
+  a.Kmax = Kmax;
+  a.dev_status = dev_status;
+  SV_CHECK(launch_commit(a, static_cast<hipStream_t>(stream)));
+  return SV_OK;
+}
+
 SV_API const char *sv_last_hip_error(void) { return g_last_hip_error; }
 
 SV_API const char *sv_version(void) { return "specverify 0.1.0 (gfx950)"; }

@@ -178,4 +178,22 @@ hipError_t launch_propose_finish(const StatPart *parts, int nslots, int rows, fl
                                  int32_t *draft_out, float *conf_out, int32_t *dev_status,
                                  int32_t *job_cnt, hipStream_t st);
 
+// Commit after verification (see spec_commit): byte layout of the cache and the call.
+struct CommitArgs {
+  uint8_t *kv;
+  long layer_stride, half_stride;
+  int n_layers, block_size, entry_bytes, max_blocks, n_blocks;
+  const int32_t *block_table;
+  int32_t *seq_len;
+  uint8_t *rec_state;
+  const uint8_t *rec_snap;
+  long rec_bytes;
+  const int32_t *accepted_len;
+  const int32_t *verify_len;  // null: Kmax each
+  const int32_t *path;        // null: chain
+  int B, Kmax;
+  int32_t *dev_status;
+};
+hipError_t launch_commit(const CommitArgs &c, hipStream_t st);
+
 }  // namespace sv

@@ -220,3 +220,76 @@ def to_fp8(data: dict) -> dict:
         out["q_" + name] = q.view(torch.uint8).numpy()
         out["s_" + name] = scale.numpy()
     return out
+
+
+@dataclass(frozen=True)
+class CommitWorkload:
+    """Cached target state around one commit: a paged KV cache and recurrent states.
+
+    ``ctx``: cache length range before the verify block; ``tree``: verify blocks are
+    random trees (node j's parent uniform in 0..j-1) instead of chains."""
+    name: str
+    index: int
+    B: int
+    Kmax: int
+    n_layers: int
+    entry_bytes: int
+    block_size: int
+    rec_bytes: int
+    ctx: tuple = (0, 64)
+    tree: bool = False
+    invalid: int = 0  # requests given an accepted length or path that does not fit (for error tests)
+
+
+# The confidence-scheduled batch (B = 64, 16-token blocks) on a hybrid target: 8 attention
+# layers with 8 KV heads x 128 bf16 values per token (2 KiB entries) and 1 MiB of
+# linear-attention state per request; tree-shaped verify blocks.
+COMMIT = CommitWorkload("commit", 20, B=64, Kmax=15, n_layers=8, entry_bytes=2048, block_size=16,
+                        rec_bytes=1 << 20, ctx=(256, 768), tree=True)
+COMMIT_SMALL = CommitWorkload("commit_small", 21, B=12, Kmax=7, n_layers=3, entry_bytes=48, block_size=4,
+                              rec_bytes=(1 << 15) + 48, ctx=(0, 40), tree=False, invalid=2)
+
+
+def commit_case(cw: CommitWorkload, repeat: int = 0, *, big: bool = True) -> dict:
+    """Seeded inputs of one commit.  Small int32 arrays always; with ``big`` also the byte
+    arrays (kv [n_layers, 2, n_blocks, block_size, entry_bytes], rec_state [B, rec_bytes],
+    rec_snap [B, Kmax+1, rec_bytes]) as uint8.  Verify lengths k_b are uniform in 0..Kmax
+    (k_b = 0 for a quarter of the requests); a chain accepts a uniform prefix length, a tree
+    accepts the root path of a uniform node; ``invalid`` requests get A_b = k_b + 1 (chain)
+    or a path that is not increasing (tree); one request in eight is flagged (A_b = -1)."""
+    rng = np.random.default_rng(BASE_SEED + 100 * cw.index + repeat)
+    B, K1 = cw.B, cw.Kmax + 1
+    seq_len = rng.integers(cw.ctx[0], cw.ctx[1] + 1, size=B).astype(np.int32)
+    k = rng.integers(0, K1, size=B).astype(np.int32)
+    k[rng.random(B) < 0.25] = 0
+    max_blocks = (int(seq_len.max()) + K1 + cw.block_size - 1) // cw.block_size + 1
+    n_blocks = B * max_blocks + 3
+    block_table = rng.permutation(n_blocks)[: B * max_blocks].reshape(B, max_blocks).astype(np.int32)
+    acc = np.zeros(B, np.int32)
+    path = np.zeros((B, K1), np.int32)
+    for b in range(B):
+        if cw.tree:
+            parent = [-1] + [int(rng.integers(j)) for j in range(1, k[b] + 1)]
+            node = int(rng.integers(k[b] + 1))
+            chain = [node]
+            while chain[-1] != 0:
+                chain.append(parent[chain[-1]])
+            chain.reverse()
+        else:
+            chain = list(range(int(rng.integers(k[b] + 1)) + 1))
+        acc[b] = len(chain) - 1
+        path[b, : len(chain)] = chain
+    acc[rng.random(B) < 0.125] = -1
+    bad = rng.choice(B, size=cw.invalid, replace=False) if cw.invalid else np.zeros(0, np.int64)
+    for b in bad:
+        if cw.tree and acc[b] >= 1:
+            path[b, 1] = path[b, 0]
+        else:
+            acc[b] = k[b] + 1
+    out = {"seq_len": seq_len, "verify_len": k, "accepted_len": acc, "path": path, "block_table": block_table,
+           "n_blocks": n_blocks, "invalid": np.asarray(bad, np.int64)}
+    if big:
+        out["kv"] = rng.integers(0, 256, size=(cw.n_layers, 2, n_blocks, cw.block_size, cw.entry_bytes), dtype=np.uint8)
+        out["rec_state"] = rng.integers(0, 256, size=(B, cw.rec_bytes), dtype=np.uint8)
+        out["rec_snap"] = rng.integers(0, 256, size=(B, K1, cw.rec_bytes), dtype=np.uint8)
+    return out

@@ -170,6 +170,61 @@ int spec_draft_propose(const sv_weights *w, const uint16_t *h_draft, const float
                        int rows, void *ws, size_t ws_bytes, int32_t *draft_out, float *conf_out,
                        void *stream);
 
+/* Cached target state of B requests, for the commit after a verify call.
+ *
+ * Paged KV cache of the attention layers: the entry (entry_bytes bytes) of position p
+ * of request b in layer l, half h (0 = keys, 1 = values) starts at
+ *   kv + l * layer_stride + h * half_stride
+ *      + (block_table[b * max_blocks + p / block_size] * block_size + p % block_size) * entry_bytes.
+ * Recurrent states (linear-attention layers, short convolutions, ...) are opaque bytes:
+ * rec_state [B, rec_bytes] is the state each request carries between steps and
+ * rec_snap [B, Kmax+1, rec_bytes] holds, for each input j of the last verify block,
+ * the state after that input (written by the target's forward, outside this library).
+ * rec_state and rec_snap must not overlap. */
+typedef struct sv_cache {
+  void *kv;                    /* NULL iff n_layers == 0; 16-byte aligned */
+  int64_t layer_stride;        /* bytes, multiple of 16 */
+  int64_t half_stride;         /* bytes, multiple of 16 */
+  int32_t n_layers;            /* attention layers with a KV cache (0: none) */
+  int32_t block_size;          /* tokens per cache block, >= 1 */
+  int32_t entry_bytes;         /* bytes of one token's keys (or values) in one layer, multiple of 16 */
+  int32_t max_blocks;          /* columns of block_table */
+  int32_t n_blocks;            /* blocks in the pool: ids in block_table lie in [0, n_blocks) */
+  const int32_t *block_table;  /* [B, max_blocks] block ids */
+  int32_t *seq_len;            /* [B] required: tokens in each request's cache; advanced by a commit */
+  void *rec_state;             /* [B, rec_bytes], 16-byte aligned; NULL iff rec_bytes == 0 */
+  const void *rec_snap;        /* [B, Kmax+1, rec_bytes], 16-byte aligned; NULL iff rec_bytes == 0 */
+  int64_t rec_bytes;           /* multiple of 16, or 0 */
+} sv_cache;
+
+#define SV_DEV_BAD_COMMIT 3 /* spec_commit: an accepted length or path that does not fit its block */
+
+/* Commit after verification: keep the cached state of the accepted prefix only
+ * ("Let's start over, Misha ...", "The KV cache and speculative decoding work together":
+ * the target keeps state for the accepted part of the block and drops the rejected
+ * tail; "Speculative decoding in production ...", "Why hybrid attention matters for
+ * speculation" and the n-gram pitfalls: the linear-attention state must follow the
+ * committed tokens on steps with and without a draft).
+ *
+ * The verify block of request b had k_b + 1 inputs (the last emitted token, then k_b
+ * drafts; k_b = verify_len[b], or Kmax when verify_len is NULL; k_b = 0 is a step
+ * without a draft) whose keys/values the target wrote at positions seq_len[b] + j.
+ * With A_b = accepted_len[b] (from a verify call), inputs 0..A_b are committed:
+ *  - chain (path == NULL): the entries stay where they are; seq_len[b] += A_b + 1;
+ *  - tree (path != NULL, [B, Kmax+1]): node path[b, i] is the accepted node at depth i
+ *    (path[b, 0] = 0, strictly increasing, <= k_b); its entries, written at
+ *    seq_len[b] + path[b, i], move to seq_len[b] + i in every layer and both halves;
+ *  - rec_state[b] = rec_snap[b, n] with n = A_b (chain) or path[b, A_b] (tree).
+ * Requests with A_b < 0 (flagged by the verify call) are left unchanged.  A request whose
+ * A_b > k_b, whose path is not as above, or whose touched positions (seq_len[b] + i and
+ * seq_len[b] + path[b, i] for i <= A_b) run past its block-table row or map to block ids
+ * outside the pool (checked only when n_layers > 0) is left unchanged
+ * and sets *dev_status (may be NULL; only written while it holds SV_DEV_OK, so a verify
+ * call's code is kept) to SV_DEV_BAD_COMMIT.  Entries beyond the new seq_len keep stale
+ * bytes.  Requires 0 <= Kmax <= 63.  Two kernels on `stream`; no workspace. */
+int spec_commit(const sv_cache *c, const int32_t *accepted_len, const int32_t *verify_len,
+                const int32_t *path, int B, int Kmax, int32_t *dev_status, void *stream);
+
 /* Library version string, a text for an SV_E* code, and the HIP error text behind
  * the last SV_EHIP returned on the calling thread. */
 const char *sv_version(void);

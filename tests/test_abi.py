@@ -165,3 +165,31 @@ def test_fp8_weights_workspace_rules(lib):
     assert lib.sv_workspace_bytes(b.SV_MODE_SAMPLE, 1, 15, ctypes.byref(_w8(wtype=7))) == 0
     # without an MLP only the LM-head scales are needed
     assert lib.sv_workspace_bytes(b.SV_MODE_SAMPLE, 1, 15, ctypes.byref(_w8(mlp=False, d_ff=0))) > 0
+
+
+def _cache(**kw):
+    z = 1 << 20
+    c = b.SvCache(kv=z, layer_stride=1 << 24, half_stride=1 << 23, n_layers=4, block_size=16, entry_bytes=2048,
+                  max_blocks=64, n_blocks=1024, block_table=2 * z, seq_len=3 * z, rec_state=4 * z, rec_snap=5 * z,
+                  rec_bytes=1 << 16)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("bad", [
+    dict(seq_len=None), dict(entry_bytes=24), dict(entry_bytes=0), dict(block_size=0), dict(kv=(1 << 20) + 8),
+    dict(block_table=None), dict(n_blocks=0), dict(layer_stride=(1 << 24) + 4), dict(rec_bytes=100),
+    dict(rec_snap=None), dict(rec_state=(1 << 22) + 4), dict(n_layers=-1),
+])
+def test_commit_rejects_bad_cache(lib, bad):
+    c = _cache(**bad)
+    acc = 6 << 20
+    assert lib.spec_commit(ctypes.byref(c), acc, None, None, 8, 15, None, None) == b.SV_EINVAL
+
+
+@pytest.mark.parametrize("B,Kmax,acc", [(0, 15, 6 << 20), (8, -1, 6 << 20), (8, 64, 6 << 20), (8, 15, None)])
+def test_commit_rejects_bad_sizes(lib, B, Kmax, acc):
+    c = _cache()
+    assert lib.spec_commit(ctypes.byref(c), acc, None, None, B, Kmax, None, None) == b.SV_EINVAL
+    assert lib.spec_commit(None, 6 << 20, None, None, 8, 15, None, None) == b.SV_EINVAL
