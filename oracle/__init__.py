@@ -10,6 +10,10 @@ from .verify import (  # noqa: F401
     verify_greedy, verify_sample, verify_scheduled,
 )
 from .commit import commit  # noqa: F401
+from .tree import (  # noqa: F401
+    children as tree_children, next_residual, accept_tree_greedy, accept_tree_sample, verify_tree_greedy,
+    verify_tree_sample,
+)
 from .theory import (  # noqa: F401
     expected_tokens, speedup, best_draft_length, tau_from_position_acceptance,
     conditional_acceptance, acceptance_rate, tau_closed_form, tokens_per_step,
