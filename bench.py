@@ -287,6 +287,11 @@ def main():
                                        "launch_ms": lm3}})
             log(f"{wk3.name}: {ms3:.3f} ms/step, {M3} verified rows")
             del call3, out3, d3
+        # the same block verified as a top-k tree of depth 3 (root: 4 candidates, each 2, then 1)
+        for mt in ("sample", "greedy"):
+            extra.append(bench_tree(bd, torch, wl, wk, data, w_main, dev, to_bf16, to_i32, to_f32, mt, timed,
+                                    args.steps, args.warmup))
+            log(f"block16 tree {mt}: {extra[-1]['ms_per_step']:.3f} ms/step, tau {extra[-1]['tau']:.2f}")
         # commit after verification: the scheduled batch (B = 64, Kmax = 15) with tree-shaped
         # blocks on a hybrid target (8 attention layers x 2 KiB entries, 1 MiB recurrent state)
         extra.append(bench_commit(bd, torch, wl, dev, to_i32, args.steps, args.warmup))
@@ -315,6 +320,47 @@ def main():
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(wk, data, mode, out, w, bd, torch)
     print(json.dumps(result), flush=True)
+
+
+def bench_tree(bd, torch, wl, wk, data, w, dev, to_bf16, to_i32, to_f32, mode, timed, steps, warmup):
+    """spec_verify_tree on the 16-token block shaped as a top-k tree.  Drafts come from
+    the library's drafter step on each child's parent row: the first child of a node takes
+    the argmax, later siblings are samples (coin of the child)."""
+    B, K, V, d = wk.B, wk.K, wk.V, wk.d
+    parent = wl.tree_parents(B, K, "topk")
+    hd = to_bf16(data["h_draft"])  # [B, K, d]: drafter row of node u is row u
+    rows = hd[torch.arange(B, device=dev)[:, None], to_i32(parent).long()].reshape(B * K, d).contiguous()
+    x_s, _ = bd.spec_draft_propose(w, rows, to_f32(data["draft_coins"]).reshape(-1), 1.0)
+    x_g, _ = bd.spec_draft_propose(w, rows, None, 0.0)
+    first = np.ones((B, K), bool)
+    for b in range(B):
+        seen = set()
+        for j in range(K):
+            first[b, j] = parent[b, j] not in seen
+            seen.add(parent[b, j])
+    tokens = torch.where(torch.from_numpy(first.reshape(-1)).to(dev), x_g, x_s).view(B, K).contiguous()
+    T = 0.0 if mode == "greedy" else wk.T
+    h = to_bf16(data["h"])
+    u = to_f32(data["coins"])
+    par = to_i32(parent)
+    mcode = bd.SV_MODE_GREEDY if mode == "greedy" else bd.SV_MODE_SAMPLE
+    out = bd.make_outputs(B, K, dev, mode=mcode, V=V, d=d)
+    out.path = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    ws = bd.workspace(mcode, B, K, w, dev)
+
+    def call():
+        bd.spec_verify_tree(w, h, hd, tokens, par, u, T, out=out, ws=ws)
+    ms, lm, _, sp = timed(call, out, steps, warmup)
+    rows_lm = B * (K + 1) + (0 if mode == "greedy" else B * K)
+    b_lm = 2.0 * V * d + 2.0 * rows_lm * d
+    return {"workload": f"block16 tree {mode}: B={B}, {K + 1} nodes (top-k tree, depth 3)"
+                        + ("" if mode == "greedy" else f", T={wk.T}"),
+            "ms_per_step": ms, "step_ms_spread": sp, "positions_per_sec": B * (K + 1) / (ms * 1e-3),
+            "accepted_tokens_per_sec": float(out.counters.cpu().numpy()[2]) / (ms * 1e-3),
+            "tau": float(out.tau.item()),
+            "roofline": {"bound": "hbm", "achieved": b_lm / (lm * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": b_lm / (lm * 1e-3) / 1e9 / HBM_PEAK_GBS, "kernel": f"LM-head GEMM over {rows_lm} rows",
+                         "launch_ms": lm}}
 
 
 def bench_commit(bd, torch, wl, dev, to_i32, steps, warmup):

@@ -19,12 +19,13 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libspecverify.so")
 
 SV_OK, SV_EINVAL, SV_EWORKSPACE, SV_EHIP = 0, -1, -2, -3
-SV_DEV_OK, SV_DEV_BAD_TOKEN, SV_DEV_NONFINITE, SV_DEV_BAD_COMMIT = 0, 1, 2, 3
+SV_DEV_OK, SV_DEV_BAD_TOKEN, SV_DEV_NONFINITE, SV_DEV_BAD_COMMIT, SV_DEV_BAD_TREE = 0, 1, 2, 3, 4
 SV_MODE_GREEDY, SV_MODE_SAMPLE, SV_MODE_SCHEDULED, SV_MODE_PROPOSE = 0, 1, 2, 3
 SV_DIAG_COLS = 8
 
 EXPORTS = ("sv_workspace_bytes", "spec_verify_greedy", "spec_verify_sample", "spec_verify_scheduled",
-           "spec_draft_propose", "spec_commit", "sv_version", "sv_strerror", "sv_last_hip_error")
+           "spec_draft_propose", "spec_verify_tree", "spec_commit", "sv_version", "sv_strerror",
+           "sv_last_hip_error")
 
 
 class SpecVerifyError(RuntimeError):
@@ -82,6 +83,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                           sz, ctypes.POINTER(SvOutputs), vp]
     lib.spec_draft_propose.restype = i32
     lib.spec_draft_propose.argtypes = [ctypes.POINTER(SvWeights), vp, vp, f32, i32, vp, sz, vp, vp, vp]
+    lib.spec_verify_tree.restype = i32
+    lib.spec_verify_tree.argtypes = [ctypes.POINTER(SvWeights), vp, vp, vp, vp, vp, f32, i32, i32, vp, sz,
+                                     ctypes.POINTER(SvOutputs), vp, vp]
     lib.spec_commit.restype = i32
     lib.spec_commit.argtypes = [ctypes.POINTER(SvCache), vp, vp, vp, i32, i32, vp, vp]
     lib.sv_version.restype = ctypes.c_char_p
@@ -168,6 +172,7 @@ class Outputs:
     logits: torch.Tensor | None = None
     hidden: torch.Tensor | None = None
     ev_lm: tuple | None = None  # (torch.cuda.Event, torch.cuda.Event) around the LM-head GEMM
+    path: torch.Tensor | None = None  # tree verification: node at each depth
 
     def c(self) -> SvOutputs:
         ev0 = ev1 = None
@@ -287,6 +292,33 @@ def spec_draft_propose(w: Weights, h_draft, coins, T: float, *, draft_out=None, 
                                    ws.numel(), _ptr(draft_out), _ptr(conf_out), _stream(stream))
     _raise(rc, "spec_draft_propose")
     return draft_out.view(h_draft.shape[:-1]), conf_out.view(h_draft.shape[:-1])
+
+
+def spec_verify_tree(w: Weights, h, h_draft, tokens, parent, u, T: float, *, out: Outputs | None = None, ws=None,
+                     stream=None, diag=False, logits=False, hidden=False) -> Outputs:
+    """Tree verification of B trees of K+1 nodes: h [B, K+1, d]; h_draft [B, K, d] (T > 0);
+    tokens / parent [B, K] (node j+1); u [B, K+1] (T > 0).  T == 0 is greedy.  The output
+    carries ``path`` [B, K+1] (node at each depth, -1 beyond the accepted depth)."""
+    greedy = float(T) == 0.0
+    _check_dev(h, torch.bfloat16, "h")
+    _check_dev(tokens, torch.int32, "tokens")
+    _check_dev(parent, torch.int32, "parent")
+    if not greedy:
+        _check_dev(h_draft, torch.bfloat16, "h_draft")
+        _check_dev(u, torch.float32, "u")
+    B, K1, _ = h.shape
+    K = K1 - 1
+    mode = SV_MODE_GREEDY if greedy else SV_MODE_SAMPLE
+    out = out or make_outputs(B, K, h.device, mode=mode, V=w.V, d=w.d, diag=diag, logits=logits, hidden=hidden)
+    if out.path is None:
+        out.path = torch.empty(B, K + 1, dtype=torch.int32, device=h.device)
+    ws = ws if ws is not None else workspace(mode, B, K, w, h.device)
+    oc = out.c()
+    rc = load().spec_verify_tree(ctypes.byref(w.c), _ptr(h), None if greedy else _ptr(h_draft), _ptr(tokens),
+                                 _ptr(parent), None if greedy else _ptr(u), float(T), B, K, _ptr(ws), ws.numel(),
+                                 ctypes.byref(oc), _ptr(out.path), _stream(stream))
+    _raise(rc, "spec_verify_tree")
+    return out
 
 
 def spec_commit(accepted_len, seq_len, *, Kmax: int, kv=None, block_table=None, rec_state=None, rec_snap=None,

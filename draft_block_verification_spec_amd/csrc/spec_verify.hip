@@ -486,6 +486,52 @@ SV_API int spec_draft_propose(const sv_weights *w, const uint16_t *h_draft, cons
   return SV_OK;
 }
 
+SV_API int spec_verify_tree(const sv_weights *w, const uint16_t *h, const uint16_t *h_draft, const int32_t *tokens,
+                            const int32_t *parent, const float *u, float T, int B, int K, void *ws, size_t ws_bytes,
+                            sv_outputs *out, int32_t *path, void *stream) {
+  int rc = check_common(w, h, tokens, B, K, ws, out);
+  if (rc) return rc;
+  if (K > 63 || (K > 0 && !parent) || !(T >= 0.f) || !isfinite(T)) return SV_EINVAL;
+  const bool greedy = T == 0.f;
+  if (!greedy && (!u || (K > 0 && (!h_draft || !aligned16(h_draft))))) return SV_EINVAL;
+  Plan p;
+  if (!make_plan(greedy ? SV_MODE_GREEDY : SV_MODE_SAMPLE, B, K, w, 0, p)) return SV_EINVAL;
+  if (ws_bytes < p.total || (p.total && !ws)) return SV_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const float invT = greedy ? 1.f : 1.f / T;
+  int32_t *reset = out->dev_status;
+  const uint16_t *y = h;
+  if (p.d_ff > 0) {
+    uint16_t *ybuf = out->hidden ? out->hidden : at<uint16_t>(ws, p.o_y);
+    SV_CHECK(run_mlp(p, w, h, p.M_t, nullptr, ybuf, ws, reset, st));
+    reset = nullptr;
+    y = ybuf;
+  }
+  float *logits = out->logits ? out->logits : (greedy ? nullptr : at<float>(ws, p.o_logits));
+  GemmArgs g = base_args();
+  g.x1 = y; g.ldx1 = p.d; g.m1 = p.M_t; g.x2 = (!greedy && K > 0) ? h_draft : y; g.ldx2 = p.d;
+  g.M = p.M_lm; g.N = p.V; g.K = p.d; set_lm(g, w);
+  g.logits = logits; g.ldl = p.V;
+  g.parts = at<StatPart>(ws, p.o_parts); g.nslots = p.lm.nslots;
+  g.invT = invT; g.want_s = (!greedy || out->diag) ? 1 : 0;
+  g.status_reset = reset;
+  int32_t *sync = at<int32_t>(ws, p.o_sync);
+  g.counter_reset = sync;
+  SV_CHECK(run_gemm_timed(p.lm, g, EPI_LOGITS, out, st));
+  TreeArgs a = {};
+  a.B = B; a.K = K; a.V = p.V; a.invT = invT; a.greedy = greedy ? 1 : 0;
+  a.parts_t = g.parts; a.nslots_t = p.lm.nslots;
+  a.parts_d = g.parts + (size_t)p.M_t * p.lm.nslots; a.nslots_d = p.lm.nslots;
+  a.logits_t = logits; a.logits_d = logits ? logits + (size_t)p.M_t * p.V : nullptr;
+  a.tokens = tokens; a.parent = parent; a.u = u;
+  a.accepted_len = out->accepted_len; a.emitted = out->emitted; a.path = path;
+  a.dev_status = out->dev_status; a.diag = out->diag;
+  a.done_cnt = sync;
+  a.fin = FinalizeArgs{out->accepted_len, nullptr, B, K, out->tau, out->counters};
+  SV_CHECK(launch_tree(a, st));
+  return SV_OK;
+}
+
 SV_API int spec_commit(const sv_cache *c, const int32_t *accepted_len, const int32_t *verify_len,
                        const int32_t *path, int B, int Kmax, int32_t *dev_status, void *stream) {
   if (!c || !accepted_len || !c->seq_len || B < 1 || Kmax < 0 || Kmax > 63) return SV_EINVAL;

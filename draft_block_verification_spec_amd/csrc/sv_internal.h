@@ -178,6 +178,28 @@ hipError_t launch_propose_finish(const StatPart *parts, int nslots, int rows, fl
                                  int32_t *draft_out, float *conf_out, int32_t *dev_status,
                                  int32_t *job_cnt, hipStream_t st);
 
+// Tree verification tail (see spec_verify_tree): one block per request.
+struct TreeArgs {
+  int B, K, V;
+  float invT;   // 1 when greedy
+  int greedy;
+  const StatPart *parts_t;  // [B*(K+1)][nslots_t]
+  int nslots_t;
+  const StatPart *parts_d;  // [B*K][nslots_d] (sampled)
+  int nslots_d;
+  const float *logits_t;  // [B*(K+1), V] (sampled)
+  const float *logits_d;  // [B*K, V] (sampled)
+  const int32_t *tokens;  // [B, K]
+  const int32_t *parent;  // [B, K]
+  const float *u;         // [B, K+1] (sampled)
+  int32_t *accepted_len, *emitted, *path;
+  int32_t *dev_status;
+  float *diag;
+  int32_t *done_cnt;
+  FinalizeArgs fin;
+};
+hipError_t launch_tree(const TreeArgs &a, hipStream_t st);
+
 // Commit after verification (see spec_commit): byte layout of the cache and the call.
 struct CommitArgs {
   uint8_t *kv;

@@ -851,6 +851,261 @@ __global__ __launch_bounds__(NT) void k_propose_finish(const StatPart *parts, in
   if (!fin) draft_out[r] = -1;
 }
 
+
+// ---- tree verification: one block of TNT threads per request.  The tree (at most 64
+// nodes) and every row's statistics sit in LDS; the walk is block-uniform: every thread
+// takes the same decisions from the same values.  After j failed candidates at node u
+// the residual is max(0, p_u - c q_u) / Z (c_0 = 0, Z_0 = 1, c_{j+1} = c_j + Z_j,
+// Z_{j+1} = sum_v max(0, p_u(v) - c_{j+1} q_u(v))): the normalised max(0, r - q_u) of
+// the previous residual r written in closed form, so each failed candidate costs one
+// pass over the two rows.  The pass keeps the sums of 64-token chunks in LDS, from
+// which the final inverse-CDF draw finds its chunk without another pass.
+constexpr int TNT = 1024;
+constexpr int TCH = 256;                   // tokens per chunk: 4 per lane of a wave
+constexpr int TMAXCH = (1 << 19) / TCH;    // chunks of the largest vocabulary
+constexpr int TU = 4;                      // chunks per wave whose loads are in flight together
+
+struct TreeRows {
+  const float *zt, *zd;  // target / draft logit rows of the current node (zd null: r = p)
+  float lt, ld, invT, cc;
+};
+
+__device__ __forceinline__ float tree_w1(const TreeRows &r, float zt, float zd) {
+  const float p = __expf(zt * r.invT - r.lt);
+  if (!r.zd) return p;
+  return fmaxf(p - r.cc * __expf(zd * r.invT - r.ld), 0.f);
+}
+
+// The residual weights of tokens [v0, v0 + 4) (zero past V); 16-byte loads when VEC.
+template <bool VEC>
+__device__ __forceinline__ void tree_w4(const TreeRows &r, int v0, int V, float w[4]) {
+  if (VEC && v0 + 3 < V) {
+    const f32x4 t = *reinterpret_cast<const f32x4 *>(r.zt + v0);
+    f32x4 d = t;
+    if (r.zd) d = *reinterpret_cast<const f32x4 *>(r.zd + v0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = tree_w1(r, t[k], d[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int v = v0 + k;
+      w[k] = v < V ? tree_w1(r, r.zt[v], r.zd ? r.zd[v] : 0.f) : 0.f;
+    }
+  }
+}
+
+// Sums of the residual weights per 256-token chunk into csum, and their total (fixed
+// order).  Each wave takes chunks wave, wave + 16, ...; TU of them are loaded at once.
+template <bool VEC>
+__device__ float tree_sums(const TreeRows &r, int V, float *csum, float *red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int NW = TNT / 64;
+  const int nch = (V + TCH - 1) / TCH;
+  for (int ch0 = wave; ch0 < nch; ch0 += NW * TU) {
+    float w[TU][4];
+#pragma unroll
+    for (int u = 0; u < TU; ++u) {
+      const int ch = ch0 + u * NW;
+      if (ch < nch) tree_w4<VEC>(r, ch * TCH + 4 * lane, V, w[u]);
+      else w[u][0] = w[u][1] = w[u][2] = w[u][3] = 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < TU; ++u) {
+      float t = (w[u][0] + w[u][1]) + (w[u][2] + w[u][3]);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
+      const int ch = ch0 + u * NW;
+      if (lane == 0 && ch < nch) csum[ch] = t;
+    }
+  }
+  __syncthreads();
+  float s = 0.f;
+  for (int i = threadIdx.x; i < nch; i += TNT) s += csum[i];
+  return block_sum(s, red);
+}
+
+// Inverse-CDF draw over ascending ids: the first v whose running weight exceeds
+// coin * total; with rounding past the end, the last token of positive weight.
+template <bool VEC>
+__device__ int tree_draw(const TreeRows &r, int V, float total, float coin, const float *csum, float *scan,
+                         int *redi, float *sbase) {
+  const int nch = (V + TCH - 1) / TCH;
+  const int per = (nch + TNT - 1) / TNT;
+  const float target = coin * total;
+  float loc = 0.f;
+  for (int i = 0; i < per; ++i) {
+    const int ch = threadIdx.x * per + i;
+    if (ch < nch) loc += csum[ch];
+  }
+  const float incl = block_incl_scan(loc, scan);
+  int found = 0x7fffffff, last = -1;
+  float run = incl - loc;
+  for (int i = 0; i < per; ++i) {
+    const int ch = threadIdx.x * per + i;
+    if (ch >= nch) break;
+    if (csum[ch] > 0.f) last = ch;
+    if (found == 0x7fffffff && run <= target && run + csum[ch] > target) {
+      found = ch;
+      *sbase = run;  // one writer: the chunk whose running sum crosses the target
+    }
+    run += csum[ch];
+  }
+  const int fch = block_min_int(found, redi);
+  int lch = fch;
+  float base = 0.f;
+  if (fch == 0x7fffffff) {  // rounding: fall back to the last chunk with weight
+    lch = -block_min_int(-last, redi);
+    if (lch < 0) return 0;
+  } else {
+    __syncthreads();
+    base = *sbase;
+  }
+  __shared__ int stok;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    float w[4];
+    tree_w4<VEC>(r, lch * TCH + 4 * lane, V, w);
+    const float own = (w[0] + w[1]) + (w[2] + w[3]);
+    float c = own;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float x = __shfl_up(c, off);
+      if (lane >= off) c += x;
+    }
+    float run_l = base + (c - own);  // before this lane's 4 tokens
+    int hitk = -1, lastk = -1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (w[k] > 0.f) lastk = k;
+      if (hitk < 0 && fch != 0x7fffffff && run_l + w[k] > target) hitk = k;
+      run_l += w[k];
+    }
+    const unsigned long long hit = __ballot(hitk >= 0);
+    const unsigned long long pos = __ballot(lastk >= 0);
+    const int hl = hit ? __ffsll((long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
+    const int hk = __shfl(hit ? hitk : lastk, hl);
+    if (lane == 0) stok = lch * TCH + 4 * hl + (hk < 0 ? 0 : hk);
+  }
+  __syncthreads();
+  return stok;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(TNT) void k_tree(const TreeArgs a) {
+  __shared__ float s_lse_t[64], s_lse_d[64];
+  __shared__ int s_amax[64], s_par[64], s_tok[64], s_path[64];
+  __shared__ float csum[TMAXCH];
+  __shared__ float red[TNT / 64], scan[TNT / 64], sbase;
+  __shared__ int redi[TNT / 64], flag, s_err;
+  const int b = blockIdx.x, K = a.K, N = K + 1, V = a.V;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long trow0 = (long)b * N, drow0 = (long)b * K;
+  const bool samp = !a.greedy;
+  if (tid == 0) s_err = 0;
+  if (tid < K) {
+    s_par[tid + 1] = a.parent[drow0 + tid];
+    s_tok[tid + 1] = a.tokens[drow0 + tid];
+  }
+  __syncthreads();
+  if (tid < K) {
+    const int par = s_par[tid + 1], tok = s_tok[tid + 1];
+    if (par < 0 || par > tid) atomicOr(&s_err, 1);
+    if (tok < 0 || tok >= V) atomicOr(&s_err, 2);
+  }
+  const int nrows = N + (samp ? K : 0);
+  for (int r = wave; r < nrows; r += TNT / 64) {
+    const bool tgt = r < N;
+    const int j = tgt ? r : r - N;
+    const StatPart st = tgt ? wave_merge_row(a.parts_t + (trow0 + j) * a.nslots_t, a.nslots_t, a.invT,
+                                             samp || a.diag)
+                            : wave_merge_row(a.parts_d + (drow0 + j) * a.nslots_d, a.nslots_d, a.invT, true);
+    if (lane == 0) {
+      const float lse = st.b1 * a.invT + __logf(st.s);
+      if (tgt) { s_amax[j] = st.i1; s_lse_t[j] = lse; } else { s_lse_d[j] = lse; }
+      if (!isfinite(st.b1) || (samp && !isfinite(lse))) atomicOr(&s_err, 4);
+      if (a.diag) {
+        float *dg = a.diag + (tgt ? trow0 + j : (long)a.B * N + drow0 + j) * SV_DIAG_COLS;
+        dg[0] = lse; dg[1] = (float)st.i1; dg[2] = st.b1 - st.b2; dg[3] = st.b1;
+        dg[4] = NAN; dg[5] = NAN; dg[6] = NAN; dg[7] = 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  const int err = s_err;
+  int depth = 0, final_tok = -1;
+  if (err == 0) {
+    if (tid == 0) s_path[0] = 0;
+    int node = 0;
+    if (!samp) {
+      while (true) {  // uniform: LDS values only
+        int nxt = -1;
+        for (int c = node + 1; c <= K; ++c)
+          if (s_par[c] == node && s_tok[c] == s_amax[node]) { nxt = c; break; }
+        if (nxt < 0) break;
+        node = nxt;
+        ++depth;
+        if (tid == 0) s_path[depth] = nxt;
+      }
+      final_tok = s_amax[node];
+    } else {
+      const float *ub = a.u + (long)b * N;
+      while (true) {
+        TreeRows rw{a.logits_t + (trow0 + node) * (long)V, nullptr, s_lse_t[node], 0.f, a.invT, 0.f};
+        float Z = 1.f;
+        bool sums = false;
+        int nxt = -1;
+        for (int c = node + 1; c <= K; ++c) {
+          if (s_par[c] != node) continue;
+          const int x = s_tok[c];
+          const float *zd = a.logits_d + (drow0 + node) * (long)V;
+          const float px = __expf(rw.zt[x] * a.invT - rw.lt);
+          const float qx = __expf(zd[x] * a.invT - s_lse_d[node]);
+          const float num = fmaxf(px - rw.cc * qx, 0.f);
+          const float ratio = qx > 0.f ? num / (Z * qx) : (num > 0.f ? INFINITY : 0.f);
+          if (ub[c - 1] < fminf(1.f, ratio)) { nxt = c; break; }
+          rw.zd = zd;
+          rw.ld = s_lse_d[node];
+          rw.cc += Z;
+          Z = tree_sums<VEC>(rw, V, csum, red);
+          sums = true;
+          if (!(Z > 0.f)) {  // nothing left of the residual: back to p_u
+            rw.zd = nullptr;
+            rw.cc = 0.f;
+            Z = 1.f;
+            sums = false;
+          }
+        }
+        if (nxt >= 0) {
+          node = nxt;
+          ++depth;
+          if (tid == 0) s_path[depth] = nxt;
+          continue;
+        }
+        if (!sums) Z = tree_sums<VEC>(rw, V, csum, red);
+        final_tok = tree_draw<VEC>(rw, V, Z, ub[K], csum, scan, redi, &sbase);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    if (err & 1) set_status(a.dev_status, SV_DEV_BAD_TREE);
+    else if (err & 2) set_status(a.dev_status, SV_DEV_BAD_TOKEN);
+    else if (err & 4) set_status(a.dev_status, SV_DEV_NONFINITE);
+    a.accepted_len[b] = err ? -1 : depth;
+  }
+  for (int j = tid; j <= K; j += TNT) {
+    int e = -1, p = -1;
+    if (!err && j <= depth) {
+      p = s_path[j];
+      e = j < depth ? s_tok[s_path[j + 1]] : final_tok;
+    }
+    a.emitted[trow0 + j] = e;
+    if (a.path) a.path[trow0 + j] = p;
+  }
+  if (a.fin.acc && arrive_last(a.done_cnt, a.B, &flag)) finalize_block(a.fin);
+}
+
 }  // namespace
 
 hipError_t launch_init(int32_t *zero_i32, size_t n_i32, int32_t *dev_status, hipStream_t st) {
@@ -943,6 +1198,16 @@ hipError_t launch_propose_finish(const StatPart *parts, int nslots, int rows, fl
   const int blocks = (rows + (NT / 64) - 1) / (NT / 64);
   hipLaunchKernelGGL(k_propose_finish, dim3(blocks), dim3(NT), 0, st, parts, nslots, rows, invT, T, logits, V,
                      coins, jobs, draft_out, conf_out, dev_status, job_cnt);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree(const TreeArgs &a, hipStream_t st) {
+  // 16-byte loads of logit rows need every row start 16-byte aligned: V % 4 == 0
+  if (a.V % 4 == 0 && (reinterpret_cast<uintptr_t>(a.logits_t) & 15) == 0 &&
+      (reinterpret_cast<uintptr_t>(a.logits_d) & 15) == 0)
+    hipLaunchKernelGGL(k_tree<true>, dim3(a.B), dim3(TNT), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_tree<false>, dim3(a.B), dim3(TNT), 0, st, a);
   return hipGetLastError();
 }
 

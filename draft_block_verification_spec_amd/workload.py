@@ -293,3 +293,29 @@ def commit_case(cw: CommitWorkload, repeat: int = 0, *, big: bool = True) -> dic
         out["rec_state"] = rng.integers(0, 256, size=(B, cw.rec_bytes), dtype=np.uint8)
         out["rec_snap"] = rng.integers(0, 256, size=(B, K1, cw.rec_bytes), dtype=np.uint8)
     return out
+
+
+def tree_parents(B: int, K: int, kind: str = "topk", seed: int = 0) -> np.ndarray:
+    """Parents [B, K] of verify trees of K+1 nodes (node j+1's parent in 0..j).
+
+    ``chain``: node j+1 follows node j.  ``random``: parent uniform in 0..j.  ``topk``: the
+    shape of an EAGLE-style tree built with top-k candidates per draft step (SGLang's
+    num-steps / eagle-topk / num-draft-tokens), breadth first: the root has 4 children,
+    every depth-1 node 2, every deeper node 1, in node order until K nodes exist."""
+    if kind == "chain":
+        return np.tile(np.arange(K, dtype=np.int32), (B, 1))
+    if kind == "random":
+        rng = np.random.default_rng(BASE_SEED + 7 + seed)
+        return np.array([[rng.integers(j + 1) for j in range(K)] for _ in range(B)], np.int32).reshape(B, K)
+    assert kind == "topk"
+    par, level = [], [0]
+    while len(par) < K:
+        nxt = []
+        for u in level:
+            fan = 4 if u == 0 else (2 if par[u - 1] == 0 else 1)
+            for _ in range(fan):
+                if len(par) < K:
+                    par.append(u)
+                    nxt.append(len(par))
+        level = nxt
+    return np.tile(np.array(par, np.int32), (B, 1))

@@ -170,6 +170,37 @@ int spec_draft_propose(const sv_weights *w, const uint16_t *h_draft, const float
                        int rows, void *ws, size_t ws_bytes, int32_t *draft_out, float *conf_out,
                        void *stream);
 
+#define SV_DEV_BAD_TREE 4 /* spec_verify_tree: a parent index outside [0, j] for node j+1 */
+
+/* Tree (multi-candidate) verification ("Let's start over, Misha ...", "EAGLE" and
+ * "Medusa": candidate trees checked by the target in one pass with tree attention;
+ * "Speculative decoding in vLLM and SGLang ...": draft steps, top-k candidates per step
+ * and a verification token budget).  The pages give no acceptance rule for a tree; this
+ * one is Statement 1 of the Wildberries page applied to a node's candidates in turn.
+ *
+ * Each request verifies a tree of K+1 nodes: node 0 is the last emitted token; node j+1
+ * (j < K) carries draft token tokens[b, j] and has parent parent[b, j] in [0, j].
+ * h: [B, K+1, d] target hidden rows per node (after tree attention over the node's root
+ * path); h_draft: [B, K, d] drafter rows of nodes 0..K-1 (T > 0 only), whose distribution
+ * q_u produced the children of node u.
+ *  - T == 0 (greedy): from node 0, move to the lowest-index child whose token is the
+ *    target argmax at the current node; where no child matches, emit that argmax.
+ *  - T > 0: the children c of the current node u are tested in index order; c (token x)
+ *    passes when u[b, c-1] < r(x) / q_u(x), where r = p_u at first and, after each failed
+ *    child, the normalised max(0, r - q_u) (p_u again if that is all zero).  The first
+ *    child that passes becomes the current node; when none passes, or u has no children,
+ *    the emitted token is drawn from r by inverse CDF over ascending ids with u[b, K].
+ * accepted_len[b] = depth reached; emitted[b, 0..A] = tokens of the path's nodes, then
+ * the final token; path (may be NULL) [B, K+1] = node at each depth, -1 beyond A (the
+ * tree path spec_commit takes).  A chain (parent[b, j] = j) gives exactly the results of
+ * spec_verify_greedy / spec_verify_sample.  diag rows: target rows then (T > 0) draft
+ * rows, records [0..3] as above, [4..6] NaN.  Requires K <= 63.  Workspace:
+ * sv_workspace_bytes(SV_MODE_GREEDY, B, K, w) at T == 0, SV_MODE_SAMPLE at T > 0.  A bad
+ * parent sets SV_DEV_BAD_TREE, a token outside [0, V) SV_DEV_BAD_TOKEN (request outputs -1). */
+int spec_verify_tree(const sv_weights *w, const uint16_t *h, const uint16_t *h_draft, const int32_t *tokens,
+                     const int32_t *parent, const float *u, float T, int B, int K, void *ws, size_t ws_bytes,
+                     sv_outputs *out, int32_t *path, void *stream);
+
 /* Cached target state of B requests, for the commit after a verify call.
  *
  * Paged KV cache of the attention layers: the entry (entry_bytes bytes) of position p
