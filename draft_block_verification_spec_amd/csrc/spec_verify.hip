@@ -2,6 +2,7 @@
 // the launch sequence of each verification mode.  Everything is enqueued on the
 // caller's stream; there is no host synchronisation and no allocation.
 #include <math.h>
+#include <cstdlib>
 #include <mutex>
 
 #include "sv_internal.h"
@@ -77,7 +78,7 @@ struct Plan {
   Gemm gu, dn, lm, s1;
   size_t o_a = 0, o_y = 0, o_part = 0, o_parts = 0, o_parts_d = 0, o_logits = 0, o_logits_d = 0,
          o_jobs = 0, o_sums = 0, o_conf = 0, o_vlen = 0, o_rowoff = 0, o_rowmap = 0, o_mtot = 0,
-         o_hp = 0, o_sync = 0, o_lse = 0, total = 0;
+         o_hp = 0, o_sync = 0, o_lse = 0, o_tree = 0, total = 0;
   bool small_tail = false;  // speculative per-position sampling + acceptance in one kernel
 };
 
@@ -155,6 +156,9 @@ bool make_plan(int mode, int B, int K, const sv_weights *w, int budget, Plan &p)
     p.o_jobs = take(sizeof(SampleJob) * (size_t)B);
     p.o_sums = take(sizeof(float) * 2 * (size_t)(p.small_tail ? NJ : B) * sample_chunks(V));
     if (p.small_tail) p.o_lse = take(sizeof(float) * 3 * (size_t)NJ);  // normalisers + flags
+    // sampled tree verification over several blocks per request: chunk sums and slice totals
+    if (mode == SV_MODE_SAMPLE)
+      p.o_tree = take(sizeof(float) * ((size_t)B * tree_chunks(V) + (size_t)B * 2 * TREE_MAX_BLOCKS));
   }
   // arrival counters: [0] call-wide, [1 + i] per request (or per candidate job)
   p.o_sync = take(sizeof(int32_t) * (size_t)(1 + (p.small_tail ? NJ : B)));
@@ -516,7 +520,8 @@ SV_API int spec_verify_tree(const sv_weights *w, const uint16_t *h, const uint16
   g.invT = invT; g.want_s = (!greedy || out->diag) ? 1 : 0;
   g.status_reset = reset;
   int32_t *sync = at<int32_t>(ws, p.o_sync);
-  g.counter_reset = sync;
+  g.counter_reset = sync;  // [0] the call's arrival counter, [1 + b] request b's block meetings
+  g.counter_reset_n = greedy ? 1 : 1 + B;
   SV_CHECK(run_gemm_timed(p.lm, g, EPI_LOGITS, out, st));
   TreeArgs a = {};
   a.B = B; a.K = K; a.V = p.V; a.invT = invT; a.greedy = greedy ? 1 : 0;
@@ -528,6 +533,14 @@ SV_API int spec_verify_tree(const sv_weights *w, const uint16_t *h, const uint16
   a.dev_status = out->dev_status; a.diag = out->diag;
   a.done_cnt = sync;
   a.fin = FinalizeArgs{out->accepted_len, nullptr, B, K, out->tau, out->counters};
+  if (!greedy) {
+    a.chunk_sums = at<float>(ws, p.o_tree);
+    a.partials = a.chunk_sums + (size_t)B * tree_chunks(p.V);
+    a.meet = sync + 1;
+    a.spin_limit = 1 << 16;  // a block waits for the others at most ~65 ms per pass
+    // test hook: SV_TREE_SPIN_LIMIT overrides the bound (0: every meeting times out)
+    if (const char *e = std::getenv("SV_TREE_SPIN_LIMIT")) a.spin_limit = std::atoi(e);
+  }
   SV_CHECK(launch_tree(a, st));
   return SV_OK;
 }

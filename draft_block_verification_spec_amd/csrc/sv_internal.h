@@ -197,7 +197,17 @@ struct TreeArgs {
   float *diag;
   int32_t *done_cnt;
   FinalizeArgs fin;
+  // sampled trees over several blocks per request (zeroed counters, see launch_tree)
+  float *chunk_sums;  // [B][tree_chunks(V)]
+  float *partials;    // [B][2][TREE_MAX_BLOCKS]
+  int32_t *meet;      // [B] block arrival counters, zero on entry
+  int spin_limit;     // bounded wait of a block for the others (iterations)
 };
+constexpr int TREE_MAX_BLOCKS = 16;
+int tree_chunks(int V);
+// Sampled trees spread each residual pass over up to TREE_MAX_BLOCKS co-resident blocks
+// per request when chunk_sums is set and the device allows a cooperative launch;
+// otherwise one block per request.
 hipError_t launch_tree(const TreeArgs &a, hipStream_t st);
 
 // Commit after verification (see spec_commit): byte layout of the cache and the call.

@@ -1106,6 +1106,198 @@ __global__ __launch_bounds__(TNT) void k_tree(const TreeArgs a) {
   if (a.fin.acc && arrive_last(a.done_cnt, a.B, &flag)) finalize_block(a.fin);
 }
 
+
+// ---- sampled trees over G blocks per request.  Every block merges the row statistics and
+// walks the tree exactly as the others (same values, same order); a residual pass sums one
+// slice of the vocabulary per block and publishes the slice total, and the blocks of the
+// request meet before reading all totals in a fixed order.  Block 0 draws the final
+// token from the chunk sums of the last pass and writes the outputs.
+
+// Arrive at the request's counter and wait until `target` blocks have arrived.  The wait
+// is bounded: past `limit` polls it gives up and returns false.  The shared values are
+// written and read with device-scope atomics, all stores of a block by the wave that
+// arrives; device-scope fences order them against the counter.
+__device__ bool tree_meet(int32_t *cnt, int target, int limit) {
+  __shared__ int s_ok;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    atomicAdd(cnt, 1);
+    int polls = 0;
+    while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target && polls < limit) {
+      __builtin_amdgcn_s_sleep(2);
+      ++polls;
+    }
+    __threadfence();
+    s_ok = polls < limit;
+  }
+  __syncthreads();
+  return s_ok != 0;
+}
+
+// Chunk sums of chunks [c0, c1) into the block's LDS (ls[ch - c0]) and their total
+// (fixed order).
+template <bool VEC>
+__device__ float tree_slice_sums(const TreeRows &r, int V, int c0, int c1, float *ls, float *red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int NW = TNT / 64;
+  float tot = 0.f;
+  for (int ch0 = c0 + wave; ch0 < c1; ch0 += NW * TU) {
+    float w[TU][4];
+#pragma unroll
+    for (int u = 0; u < TU; ++u) {
+      const int ch = ch0 + u * NW;
+      if (ch < c1) tree_w4<VEC>(r, ch * TCH + 4 * lane, V, w[u]);
+      else w[u][0] = w[u][1] = w[u][2] = w[u][3] = 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < TU; ++u) {
+      float t = (w[u][0] + w[u][1]) + (w[u][2] + w[u][3]);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
+      const int ch = ch0 + u * NW;
+      if (ch < c1) {
+        if (lane == 0) ls[ch - c0] = t;
+        tot += t;
+      }
+    }
+  }
+  return block_sum(lane == 0 ? tot : 0.f, red);
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(TNT) void k_tree_coop(const TreeArgs a, int G) {
+  __shared__ float s_lse_t[64], s_lse_d[64];
+  __shared__ int s_par[64], s_tok[64], s_path[64];
+  __shared__ float csum[TMAXCH];
+  __shared__ float red[TNT / 64], scan[TNT / 64], sbase;
+  __shared__ int redi[TNT / 64], flag, s_err;
+  const int b = blockIdx.x / G, gi = blockIdx.x % G;
+  const int K = a.K, N = K + 1, V = a.V;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long trow0 = (long)b * N, drow0 = (long)b * K;
+  const int nch = (V + TCH - 1) / TCH;
+  const int c0 = (int)((long)gi * nch / G), c1 = (int)((long)(gi + 1) * nch / G);
+  float *cs = a.chunk_sums + (long)b * nch;
+  float *pt = a.partials + (long)b * 2 * TREE_MAX_BLOCKS;
+  if (tid == 0) s_err = 0;
+  if (tid < K) {
+    s_par[tid + 1] = a.parent[drow0 + tid];
+    s_tok[tid + 1] = a.tokens[drow0 + tid];
+  }
+  __syncthreads();
+  if (tid < K) {
+    const int par = s_par[tid + 1], tok = s_tok[tid + 1];
+    if (par < 0 || par > tid) atomicOr(&s_err, 1);
+    if (tok < 0 || tok >= V) atomicOr(&s_err, 2);
+  }
+  for (int r = wave; r < N + K; r += TNT / 64) {
+    const bool tgt = r < N;
+    const int j = tgt ? r : r - N;
+    const StatPart st = tgt ? wave_merge_row(a.parts_t + (trow0 + j) * a.nslots_t, a.nslots_t, a.invT, true)
+                            : wave_merge_row(a.parts_d + (drow0 + j) * a.nslots_d, a.nslots_d, a.invT, true);
+    if (lane == 0) {
+      const float lse = st.b1 * a.invT + __logf(st.s);
+      if (tgt) s_lse_t[j] = lse; else s_lse_d[j] = lse;
+      if (!isfinite(st.b1) || !isfinite(lse)) atomicOr(&s_err, 4);
+      if (a.diag && gi == 0) {
+        float *dg = a.diag + (tgt ? trow0 + j : (long)a.B * N + drow0 + j) * SV_DIAG_COLS;
+        dg[0] = lse; dg[1] = (float)st.i1; dg[2] = st.b1 - st.b2; dg[3] = st.b1;
+        dg[4] = NAN; dg[5] = NAN; dg[6] = NAN; dg[7] = 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  int err = s_err;
+  int depth = 0, final_tok = -1, pass = 0;
+  // one residual pass of the request: every block its slice, then the total of all
+  // Wave 0 makes every global store of the pass, so the release in tree_meet (by its
+  // lane 0) covers all of them.
+  auto coop_sums = [&](const TreeRows &rw) -> float {
+    const float loc = tree_slice_sums<VEC>(rw, V, c0, c1, csum, red);
+    __syncthreads();
+    if (wave == 0) {
+      for (int i = lane; i < c1 - c0; i += 64)
+        __hip_atomic_store(cs + c0 + i, csum[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0)
+        __hip_atomic_store(pt + (pass & 1) * TREE_MAX_BLOCKS + gi, loc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const bool ok = tree_meet(a.meet + b, G * (pass + 1), a.spin_limit);
+    float Z = 0.f;
+    for (int i = 0; i < G; ++i)
+      Z += __hip_atomic_load(pt + (pass & 1) * TREE_MAX_BLOCKS + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ++pass;
+    if (!ok) err |= 8;
+    return Z;
+  };
+  if (err == 0) {
+    if (tid == 0) s_path[0] = 0;
+    int node = 0;
+    const float *ub = a.u + (long)b * N;
+    while (err == 0) {
+      TreeRows rw{a.logits_t + (trow0 + node) * (long)V, nullptr, s_lse_t[node], 0.f, a.invT, 0.f};
+      float Z = 1.f;
+      bool sums = false;
+      int nxt = -1;
+      for (int c = node + 1; c <= K && err == 0; ++c) {
+        if (s_par[c] != node) continue;
+        const int x = s_tok[c];
+        const float *zd = a.logits_d + (drow0 + node) * (long)V;
+        const float px = __expf(rw.zt[x] * a.invT - rw.lt);
+        const float qx = __expf(zd[x] * a.invT - s_lse_d[node]);
+        const float num = fmaxf(px - rw.cc * qx, 0.f);
+        const float ratio = qx > 0.f ? num / (Z * qx) : (num > 0.f ? INFINITY : 0.f);
+        if (ub[c - 1] < fminf(1.f, ratio)) { nxt = c; break; }
+        rw.zd = zd;
+        rw.ld = s_lse_d[node];
+        rw.cc += Z;
+        Z = coop_sums(rw);
+        sums = true;
+        if (!(Z > 0.f)) {
+          rw.zd = nullptr;
+          rw.cc = 0.f;
+          Z = 1.f;
+          sums = false;
+        }
+      }
+      if (err) break;
+      if (nxt >= 0) {
+        node = nxt;
+        ++depth;
+        if (tid == 0) s_path[depth] = nxt;
+        continue;
+      }
+      if (!sums) Z = coop_sums(rw);
+      if (err) break;
+      if (gi == 0) {
+        for (int i = tid; i < nch; i += TNT) csum[i] = __hip_atomic_load(cs + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        final_tok = tree_draw<VEC>(rw, V, Z, ub[K], csum, scan, redi, &sbase);
+      }
+      break;
+    }
+  }
+  if (gi != 0) return;
+  __syncthreads();
+  if (tid == 0) {
+    if (err & 1) set_status(a.dev_status, SV_DEV_BAD_TREE);
+    else if (err & 2) set_status(a.dev_status, SV_DEV_BAD_TOKEN);
+    else if (err & 4) set_status(a.dev_status, SV_DEV_NONFINITE);
+    else if (err & 8) set_status(a.dev_status, SV_DEV_TIMEOUT);
+    a.accepted_len[b] = err ? -1 : depth;
+  }
+  for (int j = tid; j <= K; j += TNT) {
+    int e = -1, p = -1;
+    if (!err && j <= depth) {
+      p = s_path[j];
+      e = j < depth ? s_tok[s_path[j + 1]] : final_tok;
+    }
+    a.emitted[trow0 + j] = e;
+    if (a.path) a.path[trow0 + j] = p;
+  }
+  if (a.fin.acc && arrive_last(a.done_cnt, a.B, &flag)) finalize_block(a.fin);
+}
+
 }  // namespace
 
 hipError_t launch_init(int32_t *zero_i32, size_t n_i32, int32_t *dev_status, hipStream_t st) {
@@ -1201,10 +1393,27 @@ hipError_t launch_propose_finish(const StatPart *parts, int nslots, int rows, fl
   return hipGetLastError();
 }
 
+int tree_chunks(int V) { return (V + TCH - 1) / TCH; }
+
 hipError_t launch_tree(const TreeArgs &a, hipStream_t st) {
   // 16-byte loads of logit rows need every row start 16-byte aligned: V % 4 == 0
-  if (a.V % 4 == 0 && (reinterpret_cast<uintptr_t>(a.logits_t) & 15) == 0 &&
-      (reinterpret_cast<uintptr_t>(a.logits_d) & 15) == 0)
+  const bool vec = a.V % 4 == 0 && (reinterpret_cast<uintptr_t>(a.logits_t) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(a.logits_d) & 15) == 0;
+  if (!a.greedy && a.chunk_sums && a.partials && a.meet) {
+    // all B * G blocks resident at once (one per CU at most): a cooperative launch
+    // guarantees it or fails, and then the one-block kernel runs instead
+    int G = num_cus() / a.B;
+    if (G > TREE_MAX_BLOCKS) G = TREE_MAX_BLOCKS;
+    if (G >= 2) {
+      TreeArgs ac = a;
+      void *args[] = {&ac, &G};
+      const void *fn = vec ? reinterpret_cast<const void *>(&k_tree_coop<true>)
+                           : reinterpret_cast<const void *>(&k_tree_coop<false>);
+      if (hipLaunchCooperativeKernel(fn, dim3(a.B * G), dim3(TNT), args, 0, st) == hipSuccess) return hipSuccess;
+      (void)hipGetLastError();
+    }
+  }
+  if (vec)
     hipLaunchKernelGGL(k_tree<true>, dim3(a.B), dim3(TNT), 0, st, a);
   else
     hipLaunchKernelGGL(k_tree<false>, dim3(a.B), dim3(TNT), 0, st, a);

@@ -171,6 +171,7 @@ int spec_draft_propose(const sv_weights *w, const uint16_t *h_draft, const float
                        void *stream);
 
 #define SV_DEV_BAD_TREE 4 /* spec_verify_tree: a parent index outside [0, j] for node j+1 */
+#define SV_DEV_TIMEOUT 5  /* spec_verify_tree: the blocks of a request never met (outputs -1) */
 
 /* Tree (multi-candidate) verification ("Let's start over, Misha ...", "EAGLE" and
  * "Medusa": candidate trees checked by the target in one pass with tree attention;
