@@ -78,3 +78,46 @@ def test_fp8_rejects_batches_past_the_streaming_kernel():
     draft = torch.zeros(wk.B, wk.K, dtype=torch.int32, device="cuda")
     with pytest.raises(bd.SpecVerifyError):
         bd.spec_verify_greedy(w, pt.dev_bf16(data["h"]), draft)
+
+
+@pytest.mark.parametrize("T", [0.0, 1.0], ids=["greedy", "sample"])
+def test_fp8_tree_block16(T):
+    """Tree verification with FP8 weights: the 16-token block as a top-k tree."""
+    wk = wl.BLOCK16
+    data = wl.to_fp8(wl.generate(wk, 1))
+    W = oracle.Weights.from_fp8(data)
+    w = pt.dev_fp8_weights(data)
+    parent = wl.tree_parents(wk.B, wk.K, "topk")
+    hd64 = oracle.from_bf16_bits(data["h_draft"])
+    z_t = oracle.lm_logits(W.w_lm, oracle.target_hidden(oracle.from_bf16_bits(data["h"]), W))
+    z_d = oracle.lm_logits(W.w_lm, hd64)
+    coins = data["coins"].astype(np.float64)
+    tok = np.zeros((wk.B, wk.K), np.int64)
+    for j in range(wk.K):  # child j+1 of node u: u's (rank)-th best draft token
+        u = int(parent[0, j])
+        r = int(np.sum(parent[0, :j] == u))
+        tok[0, j] = np.argsort(-z_d[0, u], kind="stable")[r]
+    if T == 0.0:
+        ref = oracle.accept_tree_greedy(z_t, tok, parent)
+    else:
+        ref = oracle.accept_tree_sample(oracle.softmax_t(z_t, T), oracle.softmax_t(z_d, T), tok, parent, coins)
+    i32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
+    out = bd.spec_verify_tree(w, pt.dev_bf16(data["h"]), pt.dev_bf16(data["h_draft"]), i32(tok), i32(parent),
+                              torch.from_numpy(coins.astype(np.float32)).cuda(), T, logits=True)
+    torch.cuda.synchronize()
+    assert int(out.dev_status.item()) == 0
+    lg = out.logits.cpu().numpy()
+    assert np.abs(lg[: wk.K + 1] - z_t[0]).max() <= pt.LOGIT_TOL
+    A = int(out.accepted_len.item())
+    path, em = out.path.cpu().numpy()[0], out.emitted.cpu().numpy()[0]
+    if A == ref["accepted"][0] and np.array_equal(em[: A + 1], ref["emitted"][0, : A + 1]):
+        return
+    # a difference must come from a near tie of a stated class
+    if T == 0.0:
+        node = int(ref["path"][0, min(A, int(ref["accepted"][0]))])
+        top = np.sort(z_t[0, node])[-2:]
+        assert top[1] - top[0] < pt.GAP_BAND
+    else:
+        near = [abs(c - min(1.0, r)) < pt.RATIO_BAND for _, r, c, _ in ref["decisions"][0]]
+        lo, hi = ref["cdf"][0]
+        assert any(near) or min(abs(coins[0, -1] - lo), abs(coins[0, -1] - hi)) < pt.CDF_BAND
