@@ -206,3 +206,34 @@ def test_tree_meeting_timeout_is_reported(monkeypatch):
     out = bd.spec_verify_tree(*args)
     torch.cuda.synchronize()
     assert int(out.dev_status.item()) == 0 and np.all(out.accepted_len.cpu().numpy() >= 0)
+
+
+@pytest.mark.parametrize("T", [0.0, 1.0], ids=["greedy", "sample"])
+def test_tree_without_drafts(T):
+    """K = 0: the tree is its root; greedy emits the argmax, sampling draws from p."""
+    wk = wl.SMALL.with_batch(4)
+    data = wl.generate(wk, 5)
+    W = oracle.Weights.from_bits(data)
+    h = data["h"][:, :1]
+    coins = data["coins"][:, -1:].astype(np.float64)
+    z_t = oracle.lm_logits(W.w_lm, oracle.target_hidden(oracle.from_bf16_bits(h), W))
+    empty = np.zeros((wk.B, 0), np.int64)
+    if T == 0.0:
+        ref = oracle.accept_tree_greedy(z_t, empty, empty)
+    else:
+        ref = oracle.accept_tree_sample(oracle.softmax_t(z_t, T), np.zeros((wk.B, 0, wk.V)), empty, empty, coins)
+    out = bd.spec_verify_tree(pt.dev_weights(data), pt.dev_bf16(h), pt.dev_bf16(data["h_draft"][:, :0]),
+                              torch.zeros(wk.B, 0, dtype=torch.int32, device="cuda"),
+                              torch.zeros(wk.B, 0, dtype=torch.int32, device="cuda"), _f32(coins), T)
+    torch.cuda.synchronize()
+    assert int(out.dev_status.item()) == 0
+    np.testing.assert_array_equal(out.accepted_len.cpu().numpy(), 0)
+    em = out.emitted.cpu().numpy()[:, 0]
+    for b in range(wk.B):
+        if em[b] != ref["emitted"][b, 0]:
+            if T == 0.0:
+                top = np.sort(z_t[b, 0])[-2:]
+                assert top[1] - top[0] < pt.GAP_BAND
+            else:
+                lo, hi = ref["cdf"][b]
+                assert min(abs(coins[b, 0] - lo), abs(coins[b, 0] - hi)) < pt.CDF_BAND
