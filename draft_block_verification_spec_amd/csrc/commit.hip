@@ -72,6 +72,21 @@ __global__ __launch_bounds__(CT) void k_commit_move(const CommitArgs c, int nchu
   const int q = rec ? bid : bid - nrec_blocks;
   const int b = rec ? q / nchunk : q / (2 * c.n_layers);
   const int part = rec ? q % nchunk : q % (2 * c.n_layers);
+  // State copies: the source snapshot follows from A_b (and the path) alone, so its
+  // loads are issued before the request is validated, from an index clamped into
+  // [0, Kmax] (always in bounds); they are stored only if the commit is valid.
+  const long off = (long)part * REC_CHUNK;
+  const bool full = rec && c.rec_bytes - off >= REC_CHUNK;
+  int guess = 0;
+  u32x4 v[RU];
+  if (full) {
+    guess = min(max(c.accepted_len[b], 0), c.Kmax);
+    if (c.path) guess = min(max(c.path[(long)b * (c.Kmax + 1) + guess], 0), c.Kmax);
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(
+        c.rec_snap + ((long)b * (c.Kmax + 1) + guess) * c.rec_bytes + off);
+#pragma unroll
+    for (int u = 0; u < RU; ++u) v[u] = __builtin_nontemporal_load(src + u * CT + tid);
+  }
   if (tid < 64) {
     const CommitReq r = commit_req(c, b, tid, rec ? nullptr : slots);
     if (tid == 0) sreq = r;
@@ -80,15 +95,11 @@ __global__ __launch_bounds__(CT) void k_commit_move(const CommitArgs c, int nchu
   const CommitReq r = sreq;
   if (!r.ok) return;
   if (rec) {
-    const long off = (long)part * REC_CHUNK;
     const long n = min(REC_CHUNK, c.rec_bytes - off);
     const u32x4 *src = reinterpret_cast<const u32x4 *>(
         c.rec_snap + ((long)b * (c.Kmax + 1) + r.last) * c.rec_bytes + off);
     u32x4 *dst = reinterpret_cast<u32x4 *>(c.rec_state + (long)b * c.rec_bytes + off);
-    if (n == REC_CHUNK) {  // every load of the thread in flight before its first store
-      u32x4 v[RU];
-#pragma unroll
-      for (int u = 0; u < RU; ++u) v[u] = __builtin_nontemporal_load(src + u * CT + tid);
+    if (full && guess == r.last) {
 #pragma unroll
       for (int u = 0; u < RU; ++u) __builtin_nontemporal_store(v[u], dst + u * CT + tid);
     } else {
