@@ -78,11 +78,15 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
   const int N = a.N;
   const int nks = a.K >> 5;
   const int nch = (nks + CHUNK_KS - 1) / CHUNK_KS;
-  const int ntiles = (N + 15) >> 4;
+  // The workgroup's columns [c_begin, c_end) split N in groups of 4 columns, so that no
+  // workgroup streams more than a sixteenth of a tile beyond its share: its last tile
+  // may be partial, and its missing rows repeat the last valid row's addresses, which
+  // the memory pipeline merges (no extra HBM bytes).
   const int G = gridDim.x, g = blockIdx.x;
-  const int t_begin = (int)((long)g * ntiles / G);
-  const int t_end = (int)((long)(g + 1) * ntiles / G);
-  const int nsteps = (t_end - t_begin) * nch;
+  const int nq = (N + 3) >> 2;
+  const int c_begin = min(N, 4 * (int)((long)g * nq / G));
+  const int c_end = min(N, 4 * (int)((long)(g + 1) * nq / G));
+  const int nsteps = ((c_end - c_begin + 15) >> 4) * nch;
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
   const long K = a.K;
 
@@ -114,11 +118,11 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
   // MFMA layout straight from memory (row l%16, 8 values at 8 (l/16)).
   auto wptr = [&](const uint8_t *base, int tile, int chunk, int s) -> const uint8_t * {
     if constexpr (FULL) {
-      const int n = min(tile * 16 + 4 * (s & 3) + (lane >> 4), N - 1);
+      const int n = min(c_begin + tile * 16 + 4 * (s & 3) + (lane >> 4), c_end - 1);
       return base + ((long)n * K + chunk * (CHUNK_KS * 32) + wave * (STEPS * 32)) * ES + (s >> 2) * 256 + r16 * 16;
     } else {
       const int ks = min(kstep(chunk, s), nks - 1);
-      const int n = min(tile * 16 + r16, N - 1);
+      const int n = min(c_begin + tile * 16 + r16, c_end - 1);
       return base + ((long)n * K + ks * 32 + kq) * ES;
     }
   };
@@ -162,7 +166,7 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
 
   if constexpr (F8) {
     // row scales of this workgroup's columns (the launcher checks they fit)
-    const int n0 = t_begin * 16, cols = min(N, t_end * 16) - n0;
+    const int n0 = c_begin, cols = c_end - c_begin;
     for (int i = threadIdx.x; i < cols; i += blockDim.x) {
       sscale[i] = a.wscale[n0 + i];
       if constexpr (PAIR) sscale[F8_MAX_COLS + i] = a.wscale2[n0 + i];
@@ -185,8 +189,8 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
       for (int g = 0; g < STEPS / GK; ++g) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          Wr[4 * g + i] = ldw(wptr(wb, t_begin, 0, 4 * g + i));
-          if constexpr (PAIR) Ur[4 * g + i] = ldw(wptr(wb2, t_begin, 0, 4 * g + i));
+          Wr[4 * g + i] = ldw(wptr(wb, 0, 0, 4 * g + i));
+          if constexpr (PAIR) Ur[4 * g + i] = ldw(wptr(wb2, 0, 0, 4 * g + i));
           __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (RELOAD_A) {
@@ -201,8 +205,8 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
     } else {
 #pragma unroll
       for (int s = 0; s < STEPS; ++s) {
-        Wr[s] = ldw(wptr(wb, t_begin, 0, s));
-        if constexpr (PAIR) Ur[s] = ldw(wptr(wb2, t_begin, 0, s));
+        Wr[s] = ldw(wptr(wb, 0, 0, s));
+        if constexpr (PAIR) Ur[s] = ldw(wptr(wb2, 0, 0, s));
         if constexpr (RELOAD_A) {
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) A[mb][s] = load_a(0, s, mb);
@@ -221,7 +225,7 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
     constexpr bool PF = decltype(pf)::value;
     const int c = stp % nch;
     const int nstp = stp + 1;
-    const int ntile = t_begin + nstp / nch, nc = nstp % nch;
+    const int ntile = nstp / nch, nc = nstp % nch;  // tile index within the workgroup
     if (c == 0) {
 #pragma unroll
       for (int q = 0; q < NACC; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -291,7 +295,7 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
     }
   };
   for (int stp = 0; stp < nsteps; ++stp) {
-    const int tile = t_begin + stp / nch, c = stp % nch;
+    const int tile = stp / nch, c = stp % nch;
     if (stp + 1 < nsteps) mma_step(stp, std::true_type{});
     else mma_step(stp, std::false_type{});
     if (c != nch - 1) continue;
@@ -304,7 +308,7 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
       for (int r = 0; r < 4; ++r) rb[((wave * NACC + q) * 4 + r) * 64 + lane] = acc[q][r];
     __syncthreads();
     if (has_elem) {
-      const int n = tile * 16 + e_n16;
+      const int n = c_begin + tile * 16 + e_n16;
       const int m = e_m;
       float v0 = 0.f, v1 = 0.f;
       const int q0 = PAIR ? 2 * e_mb : e_mb;
@@ -313,8 +317,8 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
         v0 += rb[((w * NACC + q0) * 4 + e_r) * 64 + e_ln];
         if constexpr (PAIR) v1 += rb[((w * NACC + q0 + 1) * 4 + e_r) * 64 + e_ln];
       }
-      if (m < M && n < N) {
-        const int bc = n - t_begin * 16;  // column within the workgroup's range
+      if (m < M && n < c_end) {
+        const int bc = n - c_begin;  // column within the workgroup's range
         if constexpr (F8) {
           v0 *= sscale[bc];
           if constexpr (PAIR) v1 *= sscale[F8_MAX_COLS + bc];
@@ -355,8 +359,8 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
   // flush the buffered outputs: each row's column range is contiguous in memory
   if (a.buf_cols && nsteps > 0 && (EPI != EPI_LOGITS || a.logits)) {
     __syncthreads();
-    const int cols = min(N, t_end * 16) - t_begin * 16;
-    const int n0 = t_begin * 16;
+    const int cols = c_end - c_begin;
+    const int n0 = c_begin;
     const int rows = min(M, MB * 16);
     // one wave per row; 16-byte stores when every row start is 16-byte aligned (the
     // buffer rows are: buf_cols is a multiple of 16 values)
@@ -414,8 +418,9 @@ template <int MB, int EPI, int KM, bool F8>
 hipError_t launch_one(GemmArgs a, int grid, hipStream_t st) {
   constexpr size_t stat = stream_static_lds<MB, EPI, KM, F8>();
   constexpr size_t dyn_max = LDS_PER_CU - stat < OBUF_MAX ? LDS_PER_CU - stat : OBUF_MAX;
-  const int ntiles = (a.N + 15) / 16;
-  const int cols = 16 * ((ntiles + grid - 1) / grid);
+  // columns of the widest workgroup (groups of 4), rounded up to whole tiles
+  const int nq = (a.N + 3) / 4;
+  const int cols = 16 * ((4 * ((nq + grid - 1) / grid) + 15) / 16);
   if (F8 && cols > F8_MAX_COLS) return hipErrorInvalidValue;
   const size_t esz = EPI == EPI_LOGITS ? 4 : 2;
   size_t shm = (size_t)MB * 16 * cols * esz;

@@ -439,11 +439,42 @@ __device__ void scan_flags(const int32_t *fl, int Kb, int &A, int &bad) {
   bad = badm;
 }
 
+// Merge the partials of two rows at once with the whole block (fixed order); the
+// second row is optional (p1 null); n0 / n1 partials per row.  f0 / f1 are this thread's first partials (slot
+// threadIdx.x), loaded by the caller ahead of its other loads.  Every thread gets both
+// results.  red holds one record per wave and row.
+__device__ void block_merge_two(const StatPart *p0, int n0, const StatPart *p1, int n1, float invT, StatPart s0,
+                                StatPart s1, StatPart (*red)[NT / 64], StatPart &r0, StatPart &r1) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x + blockDim.x; i < n0; i += blockDim.x) s0 = stat_merge(s0, p0[i], invT, true);
+  if (p1)
+    for (int i = threadIdx.x + blockDim.x; i < n1; i += blockDim.x) s1 = stat_merge(s1, p1[i], invT, true);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    s0 = stat_merge(s0, stat_shfl_xor(s0, off), invT, true);
+    if (p1) s1 = stat_merge(s1, stat_shfl_xor(s1, off), invT, true);
+  }
+  if (lane == 0) {
+    red[0][wave] = s0;
+    red[1][wave] = s1;
+  }
+  __syncthreads();
+  r0 = red[0][0];
+  r1 = red[1][0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) {
+    r0 = stat_merge(r0, red[0][w], invT, true);
+    if (p1) r1 = stat_merge(r1, red[1][w], invT, true);
+  }
+}
+
 // VEC: V and the chunk length are multiples of 4, so each thread reads 16-byte pieces.
+// Every load the block needs is issued before the first wait: the acceptance inputs of
+// draft token j (token id first, then its two logits as soon as the id is in), this
+// thread's first statistic partial of both rows, and its logits of the block's chunks.
 template <bool VEC>
 __global__ __launch_bounds__(NT) void k_tail1(const AcceptArgs a, int chunk, int C, float *sums, float *lse_buf) {
   __shared__ float red[NT / 64][2 * SUBS];
-  __shared__ StatPart reds[NT / 64];
+  __shared__ StatPart reds[2][NT / 64];
   const int Kmax = a.K, NJ = a.B * (Kmax + 1);
   int32_t *flags = reinterpret_cast<int32_t *>(lse_buf + 2 * NJ);
   const int job = blockIdx.y, cb = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -454,11 +485,21 @@ __global__ __launch_bounds__(NT) void k_tail1(const AcceptArgs a, int chunk, int
   const long drow0 = (long)b * Kmax;
   const bool resid_row = j < Kb;
   const float invT = a.invT;
+  const bool acc_thr = cb == 0 && t == 0 && resid_row;  // decides acceptance of draft token j
+  int x = -1;
+  float coin = 0.f;
+  if (acc_thr) {
+    x = a.draft[drow0 + j];
+    coin = a.u[(long)b * (Kmax + 1) + j];
+  }
+  const StatPart *pt = a.parts_t + (trow0 + j) * a.nslots_t;
+  const StatPart *pd = resid_row ? a.parts_d + (drow0 + j) * a.nslots_d : nullptr;
+  const StatPart ft = t < a.nslots_t ? pt[t] : stat_empty();
+  const StatPart fd = (pd && t < a.nslots_d) ? pd[t] : stat_empty();
   {
     const float *z1 = a.logits_t + (trow0 + j) * (long)a.V;
     const float *z2 = resid_row ? a.logits_d + (drow0 + j) * (long)a.V : nullptr;
-    // this thread's logits of the block's chunks (chunk <= NT * PER), loaded before the
-    // row statistics are merged so the memory round trips overlap
+    // this thread's logits of the block's chunks (chunk <= NT * PER)
     auto tok = [&](int q, int i) {
       const int v0 = (cb * SUBS + q) * chunk;
       return VEC ? v0 + (i >> 2) * (4 * NT) + 4 * t + (i & 3) : v0 + t + i * NT;
@@ -472,12 +513,12 @@ __global__ __launch_bounds__(NT) void k_tail1(const AcceptArgs a, int chunk, int
         for (int i = 0; i < PER; i += 4) {
           const int v = tok(q, i);
           const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-          const f32x4 x = v < v1 ? *reinterpret_cast<const f32x4 *>(z1 + v) : zero4;
-          const f32x4 y = (z2 && v < v1) ? *reinterpret_cast<const f32x4 *>(z2 + v) : zero4;
+          const f32x4 xv = v < v1 ? *reinterpret_cast<const f32x4 *>(z1 + v) : zero4;
+          const f32x4 yv = (z2 && v < v1) ? *reinterpret_cast<const f32x4 *>(z2 + v) : zero4;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            zt[q][i + e] = x[e];
-            zd[q][i + e] = y[e];
+            zt[q][i + e] = xv[e];
+            zd[q][i + e] = yv[e];
           }
         }
       } else {
@@ -489,9 +530,14 @@ __global__ __launch_bounds__(NT) void k_tail1(const AcceptArgs a, int chunk, int
         }
       }
     }
-    const StatPart st_t = block_merge_row(a.parts_t + (trow0 + j) * a.nslots_t, a.nslots_t, invT, true, reds);
-    StatPart st_d = stat_empty();
-    if (resid_row) st_d = block_merge_row(a.parts_d + (drow0 + j) * a.nslots_d, a.nslots_d, invT, true, reds);
+    const bool x_ok = x >= 0 && x < a.V;
+    float zx = 0.f, zdx = 0.f;
+    if (acc_thr && x_ok) {
+      zx = z1[x];
+      zdx = z2[x];
+    }
+    StatPart st_t, st_d;
+    block_merge_two(pt, a.nslots_t, pd, a.nslots_d, invT, ft, fd, reds, st_t, st_d);
     const float lse1 = st_t.b1 * invT + __logf(st_t.s);
     const float lse2 = resid_row ? st_d.b1 * invT + __logf(st_d.s) : 0.f;
     // per chunk: sum of max(0, p - q) and of p over this thread's tokens (token order)
@@ -535,15 +581,13 @@ __global__ __launch_bounds__(NT) void k_tail1(const AcceptArgs a, int chunk, int
       int flag = 0;
       if (!isfinite(lse1) || (resid_row && !isfinite(lse2))) flag |= FLAG_NONFINITE;
       if (resid_row) {
-        const int x = a.draft[drow0 + j];
-        if (x < 0 || x >= a.V) {
+        if (!x_ok) {
           flag |= FLAG_BAD_TOKEN;
         } else {
-          const float zx = z1[x], zdx = z2[x];
           const float lpt = zx * invT - lse1;
           const float lqd = zdx * invT - lse2;
           const float ratio = __expf(lpt - lqd);
-          if (a.u[(long)b * (Kmax + 1) + j] < ratio) flag |= FLAG_ACCEPT;
+          if (coin < ratio) flag |= FLAG_ACCEPT;
           if (a.diag) {
             float *dt = a.diag + ((long)b * (Kmax + 1) + j) * SV_DIAG_COLS;
             dt[4] = zx; dt[5] = __expf(lpt); dt[6] = ratio;
@@ -566,16 +610,137 @@ __global__ __launch_bounds__(NT) void k_tail1(const AcceptArgs a, int chunk, int
   }
 }
 
-__global__ __launch_bounds__(NT) void k_tail2(const AcceptArgs a, int chunk, int C, const float *sums,
-                                              const float *lse_buf, FinalizeArgs fin) {
-  __shared__ float redf[NT / 64];
-  __shared__ int redi[NT / 64];
-  __shared__ float buf[NT / 64];
-  __shared__ float buf2[NT];
-  __shared__ int s_flag;
+// Inclusive prefix sum over the 64 lanes of a wave, in lane order.
+__device__ __forceinline__ float wave_incl_scan(float v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float x = __shfl_up(v, off);
+    if (lane >= off) v += x;
+  }
+  return v;
+}
+
+// Position of a draw inside a sequence held by the lanes of a wave in lane order.
+// Lane l holds the weights w[0..n) of consecutive items starting at item0 (n <= NI),
+// incl is the wave's inclusive prefix sum of the lane totals, base the sum of all items
+// before the sequence.  Returns (in every lane) the first item whose running sum
+// exceeds target; if rounding leaves none, the last item of positive weight; if no
+// item has weight, item0 of lane 0.  *run_before gets the running sum before that item.
+template <int NI>
+__device__ int wave_find(const float (&w)[NI], int n, int item0, float base, float incl, float lane_tot,
+                         float target, float *run_before) {
+  const int lane = threadIdx.x & 63;
+  float run = base + incl - lane_tot;
+  int hit = -1, last = -1;
+  float hit_run = 0.f, last_run = 0.f;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (i < n && w[i] > 0.f) {
+      if (hit < 0 && run + w[i] > target) {
+        hit = item0 + i;
+        hit_run = run;
+      }
+      last = item0 + i;
+      last_run = run;
+    }
+    if (i < n) run += w[i];
+  }
+  const unsigned long long mh = __ballot(hit >= 0);
+  if (mh) {
+    const int src = __ffsll((long long)mh) - 1;
+    *run_before = __shfl(hit_run, src);
+    return __shfl(hit, src);
+  }
+  const unsigned long long ml = __ballot(last >= 0);
+  if (ml) {
+    const int src = 63 - __clzll((long long)ml);
+    *run_before = __shfl(last_run, src);
+    return __shfl(last, src);
+  }
+  *run_before = 0.f;
+  return __shfl(item0, 0);
+}
+
+// The same search when lane l holds NE consecutive items of each of NG groups, the
+// groups following each other: item = first + g * gstride + l * NE + e (gstride =
+// 64 * NE).  Items past the end must carry weight 0.  Each load instruction of such a
+// layout reads one contiguous run (lane-interleaved), unlike a per-lane contiguous one.
+template <int NG, int NE>
+__device__ int wave_find_grouped(const float (&w)[NG][NE], int first, float base, float target, float *run_before) {
+  const int lane = threadIdx.x & 63;
+  float sg[NG], inc[NG], gt[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    float x = 0.f;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) x += w[g][e];
+    sg[g] = x;
+    inc[g] = wave_incl_scan(x);
+    gt[g] = __shfl(inc[g], 63);
+  }
+  // the group holding the draw (uniform over the wave)
+  float run = base, gbase = 0.f, lbase = 0.f;
+  int gs = -1, gl = -1;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    if (gt[g] > 0.f) {
+      if (gs < 0 && run + gt[g] > target) {
+        gs = g;
+        gbase = run;
+      }
+      gl = g;
+      lbase = run;
+    }
+    run += gt[g];
+  }
+  float tgt = target;
+  if (gs < 0) {
+    if (gl < 0) {
+      *run_before = base;
+      return first;
+    }
+    gs = gl;  // rounding left the target beyond the end: the last item of positive weight
+    gbase = lbase;
+    tgt = INFINITY;
+  }
+  float ws[NE], ss = 0.f, is = 0.f;
+#pragma unroll
+  for (int e = 0; e < NE; ++e) ws[e] = 0.f;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    if (g == gs) {
+#pragma unroll
+      for (int e = 0; e < NE; ++e) ws[e] = w[g][e];
+      ss = sg[g];
+      is = inc[g];
+    }
+  }
+  return wave_find(ws, NE, first + gs * 64 * NE + lane * NE, gbase, is, ss, tgt, run_before);
+}
+
+constexpr int T2_CG = 4;     // groups of 64 chunk sums in tail2 (C <= 256)
+constexpr int T2_NT2 = 512;  // threads reading the chosen chunk in tail2, 4 tokens each (chunk <= 2048)
+
+// tail2: one block per request.  Phase 1: wave w takes the candidate first-rejection
+// points j = w, w + nw, ... and finds, from tail1's chunk sums and the request's final
+// coin, the chunk its draw falls in; wave 0 meanwhile scans the acceptance flags.
+// Phase 2 (after one barrier): the first 512 threads read the chosen candidate's chunk
+// (4 tokens each, in token order over the threads) and the draw is located with a
+// block-wide scan.  Block 0 also does the call-wide bookkeeping from the flags of every
+// request.
+template <bool VEC>
+__global__ __launch_bounds__(1024) void k_tail2(const AcceptArgs a, int chunk, int C, const float *sums,
+                                                const float *lse_buf, FinalizeArgs fin) {
+  __shared__ int s_pick[64];
+  __shared__ float s_base[64], s_target[64];
+  __shared__ int s_resid[64];
+  __shared__ int s_A, s_v;
+  __shared__ float s_wt[T2_NT2 / 64];
+  __shared__ long long s_tot[16][4];
   const int Kmax = a.K, NJ = a.B * (Kmax + 1);
   const int32_t *flags = reinterpret_cast<const int32_t *>(lse_buf + 2 * NJ);
-  const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6, nw = blockDim.x >> 6;
   const int Kb = a.verify_len ? a.verify_len[b] : Kmax;
   const long trow0 = a.row_off ? a.row_off[b] : (long)b * (Kmax + 1);
   const long drow0 = (long)b * Kmax;
@@ -584,113 +749,172 @@ __global__ __launch_bounds__(NT) void k_tail2(const AcceptArgs a, int chunk, int
   if (wave == 0) {
     int A, bad;
     scan_flags(flags + jb0, Kb, A, bad);
-    if (t == 0) {
+    if (lane == 0) {
       if (bad & FLAG_BAD_TOKEN) set_status(a.dev_status, SV_DEV_BAD_TOKEN);
       if (bad & FLAG_NONFINITE) set_status(a.dev_status, SV_DEV_NONFINITE);
-      s_flag = bad ? -1 : A;
+      s_A = bad ? -1 : A;
+    }
+  }
+  if (b == 0 && fin.acc) {
+    // bookkeeping over every request (integer sums: order-independent)
+    long long sa = 0, sd = 0, se = 0, nv = 0;
+    for (int bb = wave; bb < a.B; bb += nw) {
+      const int Kbb = a.verify_len ? a.verify_len[bb] : Kmax;
+      int Ab, bad;
+      scan_flags(flags + bb * (Kmax + 1), Kbb, Ab, bad);
+      if (!bad) {
+        sa += Ab;
+        sd += Kbb;
+        se += Ab + 1;
+        nv += 1;
+      }
+    }
+    if (lane == 0) {
+      s_tot[wave][0] = sa;
+      s_tot[wave][1] = sd;
+      s_tot[wave][2] = se;
+      s_tot[wave][3] = nv;
+    }
+  }
+  const float coin = a.u[(long)b * (Kmax + 1) + Kmax];
+  // ---- phase 1: the chunk of every candidate's draw
+  for (int j = wave; j <= Kb && j < 64; j += nw) {
+    const int cj = jb0 + j;
+    // chunk sums of the candidate (sum of max(0, p - q), sum of p): chunk 64 g + lane
+    float wr[T2_CG][1], wp[T2_CG][1];
+#pragma unroll
+    for (int g = 0; g < T2_CG; ++g) {
+      const int c = 64 * g + lane;
+      float2 v = make_float2(0.f, 0.f);
+      if (c < C) v = *reinterpret_cast<const float2 *>(sums + ((long)cj * C + c) * 2);
+      wr[g][0] = v.x;
+      wp[g][0] = v.y;
+    }
+    float lr = 0.f, lp = 0.f;
+#pragma unroll
+    for (int g = 0; g < T2_CG; ++g) {
+      lr += wr[g][0];
+      lp += wp[g][0];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      lr += __shfl_xor(lr, off);
+      lp += __shfl_xor(lp, off);
+    }
+    const bool resid = j < Kb && lr > 0.f;
+    const float target = coin * (resid ? lr : lp);
+    float base;
+    const int pick = resid ? wave_find_grouped(wr, 0, 0.f, target, &base) : wave_find_grouped(wp, 0, 0.f, target, &base);
+    if (lane == 0) {
+      s_pick[j] = pick;
+      s_base[j] = base;
+      s_target[j] = target;
+      s_resid[j] = resid;
     }
   }
   __syncthreads();
-  const int A = s_flag;
-  if (A < 0) {
-    for (int jj = t; jj <= Kmax; jj += NT) a.emitted[(long)b * (Kmax + 1) + jj] = -1;
-    if (t == 0) a.accepted_len[b] = -1;
-  } else {
-    // ---- draw the token of the candidate at the first rejection
-    const int cj = jb0 + A;
-    const bool resid_cand = A < Kb;
-    const float lse1 = lse_buf[cj], lse2 = lse_buf[NJ + cj];
+  const int A = s_A;
+  if (A >= 0) {
+    // ---- phase 2: the token inside the chosen chunk of candidate A
+    const int pick = s_pick[A];
+    const float base = s_base[A], target = s_target[A];
+    const bool resid = s_resid[A] != 0;
+    const float lse1 = lse_buf[jb0 + A], lse2 = lse_buf[NJ + jb0 + A];
     const float *z1 = a.logits_t + (trow0 + A) * (long)a.V;
-    const float *z2 = resid_cand ? a.logits_d + (drow0 + A) * (long)a.V : nullptr;
-    const float coin = a.u[(long)b * (Kmax + 1) + Kmax];
-    const float wr = t < C ? sums[((long)cj * C + t) * 2 + 0] : 0.f;
-    const float wp = t < C ? sums[((long)cj * C + t) * 2 + 1] : 0.f;
-    const float tr = block_sum(wr, redf);
-    const float tp = block_sum(wp, redf);
-    const bool resid = z2 != nullptr && tr > 0.f;
-    const float total = resid ? tr : tp;
-    const float target = coin * total;
-    const float w = resid ? wr : wp;
-    const float incl = block_incl_scan(w, buf);
-    int pick = block_min_int((t < C && incl > target) ? t : 0x7fffffff, redi);
-    if (pick == 0x7fffffff) {
-      pick = -block_min_int((t < C && w > 0.f) ? -t : 1, redi);
-      if (pick < 0) pick = 0;
-    }
-    buf2[t] = incl - w;
-    __syncthreads();
-    const float base = buf2[pick];
+    const float *z2 = resid ? a.logits_d + (drow0 + A) * (long)a.V : nullptr;
     const int v0 = pick * chunk, v1 = min(a.V, v0 + chunk);
-    const int per = (chunk + NT - 1) / NT;
-    const int a0 = v0 + t * per;
-    float wv[PER];
+    const int vt = v0 + 4 * t;  // this thread's first token
+    float w4[4];
     float mine = 0.f;
+    if (t < T2_NT2) {
+      float zt[4], zd[4];
+      if constexpr (VEC) {
+        const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 xv = vt < v1 ? *reinterpret_cast<const f32x4 *>(z1 + vt) : zero4;
+        const f32x4 yv = (z2 && vt < v1) ? *reinterpret_cast<const f32x4 *>(z2 + vt) : zero4;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      float x = 0.f;
-      if (i < per && a0 + i < v1) {
-        const float p = __expf(z1[a0 + i] * invT - lse1);
-        x = resid ? fmaxf(p - __expf(z2[a0 + i] * invT - lse2), 0.f) : p;
-      }
-      wv[i] = x;
-      mine += x;
-    }
-    const float incl2 = block_incl_scan(mine, buf);
-    int tp2 = block_min_int((mine > 0.f && base + incl2 > target) ? t : 0x7fffffff, redi);
-    if (tp2 == 0x7fffffff) {
-      tp2 = -block_min_int(mine > 0.f ? -t : 1, redi);
-      if (tp2 < 0) tp2 = 0;
-    }
-    int v_pick = -1;
-    if (t == tp2) {
-      float run = base + incl2 - mine;
-      int v_last = -1;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        if (v_pick >= 0) break;
-        if (wv[i] > 0.f) {
-          v_last = a0 + i;
-          if (run + wv[i] > target) v_pick = a0 + i;
+        for (int e = 0; e < 4; ++e) {
+          zt[e] = xv[e];
+          zd[e] = yv[e];
         }
-        run += wv[i];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          zt[e] = vt + e < v1 ? z1[vt + e] : 0.f;
+          zd[e] = (z2 && vt + e < v1) ? z2[vt + e] : 0.f;
+        }
       }
-      if (v_pick < 0) v_pick = v_last >= 0 ? v_last : min(max(a0, 0), a.V - 1);
-      buf2[0] = __int_as_float(v_pick);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float xw = 0.f;
+        if (vt + e < v1) {
+          const float p = __expf(zt[e] * invT - lse1);
+          xw = resid ? fmaxf(p - __expf(zd[e] * invT - lse2), 0.f) : p;
+        }
+        w4[e] = xw;
+        mine += xw;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w4[e] = 0.f;
+    }
+    const float incl = wave_incl_scan(mine);
+    if (t < T2_NT2 && lane == 63) s_wt[wave] = incl;
+    __syncthreads();
+    // the wave holding the draw (same decision in every wave)
+    float run = base, hbase = 0.f, lbase = 0.f;
+    int hw = -1, lw = -1;
+#pragma unroll
+    for (int w = 0; w < T2_NT2 / 64; ++w) {
+      const float x = s_wt[w];
+      if (x > 0.f) {
+        if (hw < 0 && run + x > target) {
+          hw = w;
+          hbase = run;
+        }
+        lw = w;
+        lbase = run;
+      }
+      run += x;
+    }
+    float tgt = target;
+    if (hw < 0) {  // rounding left the target beyond the end: the last token of positive weight
+      hw = lw;
+      hbase = lbase;
+      tgt = INFINITY;
+    }
+    if (hw < 0) {
+      if (t == 0) s_v = v0;
+    } else if (wave == hw) {
+      float dummy;
+      const int v = wave_find(w4, 4, vt, hbase, incl, mine, tgt, &dummy);
+      if (lane == 0) s_v = min(max(v, 0), a.V - 1);
     }
     __syncthreads();
-    v_pick = __float_as_int(buf2[0]);
-    for (int jj = t; jj <= Kmax; jj += NT) {
-      int v = -1;
+  }
+  const int v_pick = A >= 0 ? s_v : -1;
+  for (int jj = t; jj <= Kmax; jj += blockDim.x) {
+    int v = -1;
+    if (A >= 0) {
       if (jj < A) v = a.draft[drow0 + jj];
       if (jj == A) v = v_pick;
-      a.emitted[(long)b * (Kmax + 1) + jj] = v;
     }
-    if (t == 0) a.accepted_len[b] = A;
+    a.emitted[(long)b * (Kmax + 1) + jj] = v;
   }
-  if (b != 0 || !fin.acc) return;
-  // ---- block 0: acceptance of every request, tau, counters
-  __syncthreads();
-  __shared__ unsigned long long tot[4];  // integer sums: order-independent
-  if (t == 0) { tot[0] = tot[1] = tot[2] = tot[3] = 0; }
-  __syncthreads();
-  for (int bb = wave; bb < a.B; bb += NT / 64) {
-    const int Kbb = a.verify_len ? a.verify_len[bb] : Kmax;
-    int Ab, bad;
-    scan_flags(flags + bb * (Kmax + 1), Kbb, Ab, bad);
-    if (lane == 0 && !bad) {
-      atomicAdd(&tot[0], (unsigned long long)Ab);
-      atomicAdd(&tot[1], (unsigned long long)Kbb);
-      atomicAdd(&tot[2], (unsigned long long)(Ab + 1));
-      atomicAdd(&tot[3], 1ull);
+  if (t == 0) a.accepted_len[b] = A;
+  if (b == 0 && fin.acc && t == 0) {
+    long long ta = 0, td = 0, te = 0, valid = 0;
+    for (int w = 0; w < nw; ++w) {
+      ta += s_tot[w][0];
+      td += s_tot[w][1];
+      te += s_tot[w][2];
+      valid += s_tot[w][3];
     }
-  }
-  __syncthreads();
-  if (t == 0) {
-    *fin.tau = tot[3] ? (float)((double)tot[2] / (double)tot[3]) : 0.f;
+    *fin.tau = valid ? (float)((double)te / (double)valid) : 0.f;
     if (fin.counters) {
-      fin.counters[0] = (int64_t)tot[0];
-      fin.counters[1] = (int64_t)tot[1];
-      fin.counters[2] = (int64_t)tot[2];
+      fin.counters[0] = (int64_t)ta;
+      fin.counters[1] = (int64_t)td;
+      fin.counters[2] = (int64_t)te;
     }
   }
 }
@@ -1351,8 +1575,14 @@ hipError_t launch_tail_small(const AcceptArgs &a, float *sums, float *lse_buf, c
     hipLaunchKernelGGL(k_tail1<true>, grid, dim3(NT), 0, st, a, chunk, C, sums, lse_buf);
   else
     hipLaunchKernelGGL(k_tail1<false>, grid, dim3(NT), 0, st, a, chunk, C, sums, lse_buf);
-  hipLaunchKernelGGL(k_tail2, dim3(a.B), dim3(NT), 0, st, a, chunk, C, (const float *)sums, (const float *)lse_buf,
-                     fin);
+  // tail2: 1024 threads (phase 1: one wave per candidate; phase 2: the first 512 threads
+  // cover a chunk of at most 2048 tokens)
+  if (a.V % 4 == 0)
+    hipLaunchKernelGGL(k_tail2<true>, dim3(a.B), dim3(1024), 0, st, a, chunk, C, (const float *)sums,
+                       (const float *)lse_buf, fin);
+  else
+    hipLaunchKernelGGL(k_tail2<false>, dim3(a.B), dim3(1024), 0, st, a, chunk, C, (const float *)sums,
+                       (const float *)lse_buf, fin);
   return hipGetLastError();
 }
 
