@@ -314,7 +314,7 @@ void k_tiled(const GemmArgs a) {
         q.b1 = b1;
         q.b2 = b2;
         q.s = sum;
-        q.i1 = b1 > -INFINITY ? nb + j1 * 32 : 0x7fffffff;
+        q.i1 = b1 > -INFINITY ? a.n_off + nb + j1 * 32 : 0x7fffffff;
         return q;
       };
       // first level straight from the folds: lanes with bit 4 set keep rows 8..15

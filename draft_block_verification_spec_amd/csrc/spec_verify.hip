@@ -42,6 +42,10 @@ struct Gemm {
   int splits = 1;
   int nslots = 0;  // statistics slots per row (EPI_LOGITS)
   size_t partial_floats = 0;
+  // EPI_LOGITS: columns [0, n_split) in whole rounds of `shape` tiles over the CUs, the
+  // rest in a second launch of `shape2` tiles (0: one launch)
+  int n_split = 0;
+  TileShape shape2{256, 128, 64, 3};
 };
 
 Gemm choose(int M, int N, int K, int epi) {
@@ -68,7 +72,25 @@ Gemm choose(int M, int N, int K, int epi) {
     g.splits = want < maxs ? want : maxs;
   }
   if (g.splits > 1) g.partial_floats = (size_t)g.splits * M * Ncols;
-  if (epi == EPI_LOGITS) g.nslots = tiled_slots(N, g.shape.bn);
+  if (epi == EPI_LOGITS) {
+    g.nslots = tiled_slots(N, g.shape.bn);
+    // A last round of 256 x 256 tiles at most half full would cost a whole round: its
+    // columns go to a second launch of 256 x 128 tiles that fits in one round (half the
+    // work per tile).  Measured at 1024 rows: 9.28 rounds -> 9 + one half-size round.
+    const TileShape big{256, 256, 64, 2};
+    if (g.shape.bm == big.bm && g.shape.bn == big.bn && g.shape.bk == big.bk && g.shape.ns == big.ns) {
+      const long tm = (M + 255) / 256, nt = (N + 255) / 256;
+      const long full = tiles / slots, rem = tiles % slots;
+      if (full >= 1 && rem > 0 && 2 * rem <= slots && slots % tm == 0) {
+        const long n1 = full * (slots / tm) * 256;
+        const long tiles2 = tm * ((N - n1 + 127) / 128);
+        if (n1 < N && nt * tm == tiles && tiles2 <= (long)tiled_per_cu(g.shape2) * num_cus()) {
+          g.n_split = (int)n1;
+          g.nslots = tiled_slots((int)n1, 256) + tiled_slots(N - (int)n1, 128);
+        }
+      }
+    }
+  }
   return g;
 }
 
@@ -201,6 +223,21 @@ thread_local const char *g_last_hip_error = "no error";
 
 hipError_t run_gemm(const Gemm &g, GemmArgs a, int epi, hipStream_t st) {
   if (g.stream) return launch_gemm_stream(a, epi, g.grid, st);
+  if (g.n_split > 0) {  // EPI_LOGITS in two launches over disjoint column ranges
+    GemmArgs a1 = a;
+    a1.N = g.n_split;
+    hipError_t e = launch_gemm_tiled(a1, epi, g.shape, 1, st);
+    if (e != hipSuccess) return e;
+    GemmArgs a2 = a;
+    a2.N = a.N - g.n_split;
+    a2.w = a.w + (size_t)g.n_split * a.K;
+    if (a.logits) a2.logits = a.logits + g.n_split;
+    a2.parts = a.parts + tiled_slots(g.n_split, g.shape.bn);
+    a2.n_off = a.n_off + g.n_split;
+    a2.status_reset = nullptr;
+    a2.counter_reset = nullptr;
+    return launch_gemm_tiled(a2, epi, g.shape2, 1, st);
+  }
   if (g.splits > 1) {
     hipError_t e = launch_gemm_tiled(a, epi, g.shape, g.splits, st);
     if (e != hipSuccess) return e;

@@ -20,7 +20,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // Per-row partial statistics of a logit row over a subset of its columns:
 // b1 = max z, b2 = second largest z, i1 = lowest column index attaining b1,
 // s = sum over the subset of exp((z - b1) * invT).  Empty: b1 = b2 = -inf, s = 0.
-struct StatPart {
+struct alignas(16) StatPart {
   float b1, b2, s;
   int i1;
 };
@@ -64,6 +64,7 @@ struct GemmArgs {
   int32_t *counter_reset;  // counter_reset[0 .. counter_reset_n) are zeroed (n >= 1 when set)
   int counter_reset_n;
   int buf_cols;  // set by the streaming launcher: columns of the per-workgroup output buffer
+  int n_off;     // EPI_LOGITS: column index of output column 0 (argmax indices of a later launch)
   // FP8 (E4M3) weights: w / w2 hold one code per element and every output row n is
   // multiplied by wscale[n] (w) / wscale2[n] (w2); weight-streaming kernel only
   int wfp8;

@@ -22,11 +22,24 @@ __device__ void set_status(int32_t *st, int code) {
   if (st) atomicCAS(st, 0, code);
 }
 
-// Merge the nslots partials of one row with one wave; result valid in every lane.
+// Merge the nslots partials of one row with one wave; result valid in every lane.  Each
+// lane merges slots lane, lane + 64, ... in order; their loads are issued in batches of
+// BATCH ahead of the merges, so a row of ~1200 partials costs 2 memory round trips with
+// BATCH = 12 (3 with 8), not 19.
+template <int BATCH = 8>
 __device__ StatPart wave_merge_row(const StatPart *parts, int nslots, float invT, bool want_s) {
   const int lane = threadIdx.x & 63;
   StatPart st = stat_empty();
-  for (int i = lane; i < nslots; i += 64) st = stat_merge(st, parts[i], invT, want_s);
+  for (int i0 = 0; i0 < nslots; i0 += 64 * BATCH) {
+    StatPart p[BATCH];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int i = i0 + 64 * k + lane;
+      p[k] = i < nslots ? parts[i] : stat_empty();
+    }
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) st = stat_merge(st, p[k], invT, want_s);
+  }
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) st = stat_merge(st, stat_shfl_xor(st, off), invT, want_s);
   return st;
@@ -148,7 +161,7 @@ __global__ __launch_bounds__(1024) void k_accept_sample(const AcceptArgs a) {
     const bool is_t = r <= Kb;
     const int j = is_t ? r : r - Kb - 1;
     const StatPart *pp = is_t ? a.parts_t + (trow0 + j) * a.nslots_t : a.parts_d + (drow0 + j) * a.nslots_d;
-    const StatPart st = wave_merge_row(pp, is_t ? a.nslots_t : a.nslots_d, a.invT, true);
+    const StatPart st = wave_merge_row<12>(pp, is_t ? a.nslots_t : a.nslots_d, a.invT, true);
     const float lse = st.b1 * a.invT + __logf(st.s);
     if (lane == 0) {
       if (is_t) lse_t[j] = lse; else lse_d[j] = lse;
@@ -240,8 +253,10 @@ __global__ __launch_bounds__(1024) void k_accept_greedy(const AcceptArgs a) {
   if (threadIdx.x == 0) bad = 0;
   __syncthreads();
   const int nw = blockDim.x >> 6;
+  // draft tokens of the first 64 positions, loaded ahead of the statistics
+  const int x0 = (wave == 0 && lane < K) ? a.draft[(long)b * K + lane] : -1;
   for (int j = wave; j <= K; j += nw) {
-    const StatPart st = wave_merge_row(a.parts_t + (trow0 + j) * a.nslots_t, a.nslots_t, 1.f, a.diag != nullptr);
+    const StatPart st = wave_merge_row<12>(a.parts_t + (trow0 + j) * a.nslots_t, a.nslots_t, 1.f, a.diag != nullptr);
     if (lane == 0) {
       amax[j] = st.i1;
       if (!isfinite(st.b1)) bad = SV_DEV_NONFINITE;
@@ -260,7 +275,7 @@ __global__ __launch_bounds__(1024) void k_accept_greedy(const AcceptArgs a) {
       const int j = base + lane;
       bool match = false;
       if (j < K) {
-        const int x = a.draft[(long)b * K + j];
+        const int x = base == 0 ? x0 : a.draft[(long)b * K + j];
         if (x < 0 || x >= a.V) ok = false;
         match = (x == amax[j]);
         if (a.diag && x >= 0 && x < a.V && a.logits_t) a.diag[(trow0 + j) * SV_DIAG_COLS + 4] = a.logits_t[(trow0 + j) * (long)a.V + x];
@@ -281,12 +296,21 @@ __global__ __launch_bounds__(1024) void k_accept_greedy(const AcceptArgs a) {
     }
     for (int j = lane; j <= K; j += 64) {
       int v = -1;
-      if (good && j < A) v = a.draft[(long)b * K + j];
+      if (good && j < A) v = j < 64 ? x0 : a.draft[(long)b * K + j];
       if (good && j == A) v = amax[A];
       a.emitted[(long)b * (K + 1) + j] = v;
     }
+    if (a.B == 1 && a.fin.acc && lane == 0) {
+      // a single request: the bookkeeping needs no other block
+      *a.fin.tau = good ? (float)(A + 1) : 0.f;
+      if (a.fin.counters) {
+        a.fin.counters[0] = good ? A : 0;
+        a.fin.counters[1] = good ? K : 0;
+        a.fin.counters[2] = good ? A + 1 : 0;
+      }
+    }
   }
-  if (a.fin.acc && arrive_last(a.done_cnt, a.B, &flag)) finalize_block(a.fin);
+  if (a.B > 1 && a.fin.acc && arrive_last(a.done_cnt, a.B, &flag)) finalize_block(a.fin);
 }
 
 // ---- inverse-CDF sampling over V, split in chunks.  Every block sums the weights of
@@ -413,7 +437,7 @@ __device__ StatPart block_merge_row(const StatPart *parts, int nslots, float inv
 //  * tail2, one block per request: the acceptance scan over the flags, then the draw
 //    of the candidate at the first rejection from its chunk sums and chunk; block 0
 //    also does the call-wide bookkeeping.
-constexpr int SUBS = 4;  // sampling chunks per tail1 block
+constexpr int SUBS = 5;  // sampling chunks per tail1 block
 // acceptance flag bits
 constexpr int FLAG_ACCEPT = 1, FLAG_BAD_TOKEN = 2, FLAG_NONFINITE = 4;
 
@@ -925,7 +949,7 @@ __global__ __launch_bounds__(NT) void k_row_conf(const StatPart *parts, int nslo
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = blockIdx.x * (NT / 64) + wave;
   if (r >= rows) return;
-  const StatPart st = wave_merge_row(parts + (long)r * nslots, nslots, invT, true);
+  const StatPart st = wave_merge_row<12>(parts + (long)r * nslots, nslots, invT, true);
   if (lane == 0) {
     conf[r] = 1.f / st.s;
     if (!isfinite(st.b1) || !(st.s >= 1.f)) set_status(dev_status, SV_DEV_NONFINITE);
@@ -1052,7 +1076,7 @@ __global__ __launch_bounds__(NT) void k_propose_finish(const StatPart *parts, in
   const int r = blockIdx.x * (NT / 64) + wave;
   if (r >= rows) return;
   const bool samp = T > 0.f;
-  const StatPart st = wave_merge_row(parts + (long)r * nslots, nslots, samp ? invT : 1.f, samp);
+  const StatPart st = wave_merge_row<12>(parts + (long)r * nslots, nslots, samp ? invT : 1.f, samp);
   if (lane != 0) return;
   job_cnt[r] = 0;
   const float lse = st.b1 * invT + __logf(st.s);
