@@ -154,6 +154,18 @@ __global__ __launch_bounds__(1024) void k_accept_sample(const AcceptArgs a) {
   }
   __syncthreads();
   const int nw = blockDim.x >> 6;
+  // wave 0: the inputs of the first 64 acceptance decisions, loaded ahead of the
+  // statistics (the logits at the draft token do not depend on the normalisers)
+  int x0 = 0;
+  float u0 = 0.f, zt0 = 0.f, zd0 = 0.f;
+  if (wave == 0 && lane < Kb) {
+    x0 = a.draft[drow0 + lane];
+    u0 = a.u[(long)b * (Kmax + 1) + lane];
+    if (x0 >= 0 && x0 < a.V) {
+      zt0 = a.logits_t[(trow0 + lane) * (long)a.V + x0];
+      zd0 = a.logits_d[(drow0 + lane) * (long)a.V + x0];
+    }
+  }
 
   // row statistics: target rows 0..Kb, draft rows 0..Kb-1
   const int nrows = 2 * Kb + 1;
@@ -185,16 +197,16 @@ __global__ __launch_bounds__(1024) void k_accept_sample(const AcceptArgs a) {
       const int j = base + lane;
       bool acc = false, bad_tok = false;
       if (j < Kb) {
-        const int x = a.draft[drow0 + j];
+        const int x = base == 0 ? x0 : a.draft[drow0 + j];
         if (x < 0 || x >= a.V) {
           bad_tok = true;
         } else {
-          const float zt = a.logits_t[(trow0 + j) * (long)a.V + x];
-          const float zd = a.logits_d[(drow0 + j) * (long)a.V + x];
+          const float zt = base == 0 ? zt0 : a.logits_t[(trow0 + j) * (long)a.V + x];
+          const float zd = base == 0 ? zd0 : a.logits_d[(drow0 + j) * (long)a.V + x];
           const float lpt = zt * a.invT - lse_t[j];
           const float lqd = zd * a.invT - lse_d[j];
           const float ratio = __expf(lpt - lqd);
-          const float u = a.u[(long)b * (Kmax + 1) + j];
+          const float u = base == 0 ? u0 : a.u[(long)b * (Kmax + 1) + j];
           acc = u < ratio;
           if (a.diag) {
             float *dt = a.diag + ((long)b * (Kmax + 1) + j) * SV_DIAG_COLS;
@@ -311,100 +323,6 @@ __global__ __launch_bounds__(1024) void k_accept_greedy(const AcceptArgs a) {
     }
   }
   if (a.B > 1 && a.fin.acc && arrive_last(a.done_cnt, a.B, &flag)) finalize_block(a.fin);
-}
-
-// ---- inverse-CDF sampling over V, split in chunks.  Every block sums the weights of
-// its chunk; the last block of a job locates the chunk and then the token with block
-// prefix scans; the last job block overall runs the end-of-call bookkeeping.
-// Weights are recomputed from the fp32 logits in ascending token order.
-__device__ __forceinline__ float job_weight(const SampleJob &jb, int v, float invT, bool resid) {
-  const float p = __expf(jb.z1[v] * invT - jb.lse1);
-  if (!resid) return p;
-  const float q = __expf(jb.z2[v] * invT - jb.lse2);
-  return fmaxf(p - q, 0.f);
-}
-
-__global__ __launch_bounds__(NT) void k_sample(const SampleJob *jobs, int njobs, int V, int chunk, float invT,
-                                               float *sums, int32_t *out, int32_t *job_cnt, int32_t *done_cnt,
-                                               FinalizeArgs fin) {
-  __shared__ float red[NT / 64];
-  __shared__ int redi[NT / 64];
-  __shared__ float buf[NT / 64];
-  __shared__ float buf2[NT];
-  __shared__ int flag;
-  const int job = blockIdx.y, c = blockIdx.x, C = gridDim.x, t = threadIdx.x;
-  const SampleJob jb = jobs[job];
-  {
-    const int v0 = c * chunk, v1 = min(V, v0 + chunk);
-    float sr = 0.f, sp = 0.f;
-    if (jb.out_index >= 0) {
-      for (int v = v0 + t; v < v1; v += NT) {
-        const float p = __expf(jb.z1[v] * invT - jb.lse1);
-        sp += p;
-        if (jb.z2) sr += fmaxf(p - __expf(jb.z2[v] * invT - jb.lse2), 0.f);
-      }
-    }
-    const float tr = block_sum(sr, red);
-    const float tp = block_sum(sp, red);
-    if (t == 0) {
-      sums[((long)job * C + c) * 2 + 0] = tr;
-      sums[((long)job * C + c) * 2 + 1] = tp;
-    }
-  }
-  if (!arrive_last(job_cnt + job, C, &flag)) return;
-
-  if (jb.out_index >= 0) {
-    const float wr = t < C ? sums[((long)job * C + t) * 2 + 0] : 0.f;
-    const float wp = t < C ? sums[((long)job * C + t) * 2 + 1] : 0.f;
-    const float tr = block_sum(wr, red);
-    const float tp = block_sum(wp, red);
-    const bool resid = jb.z2 != nullptr && tr > 0.f;
-    const float total = resid ? tr : tp;
-    const float target = jb.u * total;
-    const float w = resid ? wr : wp;
-    const float incl = block_incl_scan(w, buf);
-    int pick = block_min_int((t < C && incl > target) ? t : 0x7fffffff, redi);
-    if (pick == 0x7fffffff) {  // rounding put the target at the very end: last non-empty chunk
-      pick = -block_min_int((t < C && w > 0.f) ? -t : 1, redi);
-      if (pick < 0) pick = 0;
-    }
-    buf2[t] = incl - w;  // exclusive prefix of the chunk sums
-    __syncthreads();
-    const float base = buf2[pick];
-    const int v0 = pick * chunk, v1 = min(V, v0 + chunk);
-    // each thread owns a contiguous run of at most PER tokens, weights kept in registers
-    const int per = (chunk + NT - 1) / NT;
-    const int a0 = v0 + t * per;
-    float wv[PER];
-    float mine = 0.f;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      wv[i] = (i < per && a0 + i < v1) ? job_weight(jb, a0 + i, invT, resid) : 0.f;
-      mine += wv[i];
-    }
-    const float incl2 = block_incl_scan(mine, buf);
-    int tp2 = block_min_int((mine > 0.f && base + incl2 > target) ? t : 0x7fffffff, redi);
-    if (tp2 == 0x7fffffff) {
-      tp2 = -block_min_int(mine > 0.f ? -t : 1, redi);
-      if (tp2 < 0) tp2 = 0;
-    }
-    if (t == tp2) {
-      float run = base + incl2 - mine;
-      int v_pick = -1, v_last = -1;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        if (v_pick >= 0) break;
-        if (wv[i] > 0.f) {
-          v_last = a0 + i;
-          if (run + wv[i] > target) v_pick = a0 + i;
-        }
-        run += wv[i];
-      }
-      if (v_pick < 0) v_pick = v_last >= 0 ? v_last : min(max(a0, 0), V - 1);
-      out[jb.out_index] = v_pick;
-    }
-  }
-  if (fin.acc && arrive_last(done_cnt, njobs, &flag)) finalize_block(fin);
 }
 
 // Merge the nslots partials of one row with the whole block (fixed order); every
@@ -941,6 +859,187 @@ __global__ __launch_bounds__(1024) void k_tail2(const AcceptArgs a, int chunk, i
       fin.counters[2] = (int64_t)te;
     }
   }
+}
+
+// ---- inverse-CDF sampling of one token per job (larger batches, drafter step), two
+// kernels with no inter-block signalling: sample_sums sums the weights of every job over
+// SUBS chunks per block; sample_pick (one block per job) finds the chunk from those sums
+// and the token inside it, as tail2 does; its block 0 also writes the call-wide
+// bookkeeping (the accepted lengths are final before the draw).  The weight of token v
+// is max(0, p_v - q_v) (p_v if the job has no second row or all of those are zero),
+// recomputed from the fp32 logits in ascending token order.
+template <bool VEC>
+__global__ __launch_bounds__(NT) void k_sample_sums(const SampleJob *jobs, int V, int chunk, int C, float invT,
+                                                    float *sums) {
+  __shared__ float red[NT / 64][2 * SUBS];
+  const int job = blockIdx.y, cb = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const SampleJob jb = jobs[job];
+  if (jb.out_index < 0) return;
+  const float *z1 = jb.z1, *z2 = jb.z2;
+  auto tok = [&](int q, int i) {
+    const int v0 = (cb * SUBS + q) * chunk;
+    return VEC ? v0 + (i >> 2) * (4 * NT) + 4 * t + (i & 3) : v0 + t + i * NT;
+  };
+  float zt[SUBS][PER], zd[SUBS][PER];
+#pragma unroll
+  for (int q = 0; q < SUBS; ++q) {
+    const int v1 = min(V, (cb * SUBS + q) * chunk + chunk);
+    if constexpr (VEC) {
+#pragma unroll
+      for (int i = 0; i < PER; i += 4) {
+        const int v = tok(q, i);
+        const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 xv = v < v1 ? *reinterpret_cast<const f32x4 *>(z1 + v) : zero4;
+        const f32x4 yv = (z2 && v < v1) ? *reinterpret_cast<const f32x4 *>(z2 + v) : zero4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          zt[q][i + e] = xv[e];
+          zd[q][i + e] = yv[e];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int v = tok(q, i);
+        zt[q][i] = v < v1 ? z1[v] : 0.f;
+        zd[q][i] = (z2 && v < v1) ? z2[v] : 0.f;
+      }
+    }
+  }
+  float part[2 * SUBS];
+#pragma unroll
+  for (int q = 0; q < SUBS; ++q) {
+    const int v1 = min(V, (cb * SUBS + q) * chunk + chunk);
+    float sr = 0.f, sp = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (tok(q, i) < v1) {
+        const float p = __expf(zt[q][i] * invT - jb.lse1);
+        sp += p;
+        if (z2) sr += fmaxf(p - __expf(zd[q][i] * invT - jb.lse2), 0.f);
+      }
+    }
+    part[2 * q] = sr;
+    part[2 * q + 1] = sp;
+  }
+#pragma unroll
+  for (int k = 0; k < 2 * SUBS; ++k) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) part[k] += __shfl_xor(part[k], off);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < 2 * SUBS; ++k) red[wave][k] = part[k];
+  }
+  __syncthreads();
+  if (t < 2 * SUBS) {
+    const int c = cb * SUBS + (t >> 1);
+    float tot = 0.f;
+    for (int w = 0; w < NT / 64; ++w) tot += red[w][t];
+    if (c < C) sums[((long)job * C + c) * 2 + (t & 1)] = tot;
+  }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(T2_NT2) void k_sample_pick(const SampleJob *jobs, int V, int chunk, int C, float invT,
+                                                        const float *sums, int32_t *out, FinalizeArgs fin) {
+  __shared__ float s_wt[T2_NT2 / 64];
+  __shared__ int s_v;
+  const int job = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const SampleJob jb = jobs[job];
+  if (jb.out_index >= 0) {
+    // the chunk of the draw (every wave finds it; no barrier needed)
+    float wr[T2_CG][1], wp[T2_CG][1];
+#pragma unroll
+    for (int g = 0; g < T2_CG; ++g) {
+      const int c = 64 * g + lane;
+      float2 v = make_float2(0.f, 0.f);
+      if (c < C) v = *reinterpret_cast<const float2 *>(sums + ((long)job * C + c) * 2);
+      wr[g][0] = v.x;
+      wp[g][0] = v.y;
+    }
+    float lr = 0.f, lp = 0.f;
+#pragma unroll
+    for (int g = 0; g < T2_CG; ++g) {
+      lr += wr[g][0];
+      lp += wp[g][0];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      lr += __shfl_xor(lr, off);
+      lp += __shfl_xor(lp, off);
+    }
+    const bool resid = jb.z2 != nullptr && lr > 0.f;
+    const float target = jb.u * (resid ? lr : lp);
+    float base;
+    const int pick = resid ? wave_find_grouped(wr, 0, 0.f, target, &base) : wave_find_grouped(wp, 0, 0.f, target, &base);
+    // the token inside the chunk: 4 tokens per thread in token order
+    const float *z1 = jb.z1;
+    const float *z2 = resid ? jb.z2 : nullptr;
+    const int v0 = pick * chunk, v1 = min(V, v0 + chunk);
+    const int vt = v0 + 4 * t;
+    float zt[4], zd[4];
+    if constexpr (VEC) {
+      const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 xv = vt < v1 ? *reinterpret_cast<const f32x4 *>(z1 + vt) : zero4;
+      const f32x4 yv = (z2 && vt < v1) ? *reinterpret_cast<const f32x4 *>(z2 + vt) : zero4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        zt[e] = xv[e];
+        zd[e] = yv[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        zt[e] = vt + e < v1 ? z1[vt + e] : 0.f;
+        zd[e] = (z2 && vt + e < v1) ? z2[vt + e] : 0.f;
+      }
+    }
+    float w4[4];
+    float mine = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float xw = 0.f;
+      if (vt + e < v1) {
+        const float p = __expf(zt[e] * invT - jb.lse1);
+        xw = resid ? fmaxf(p - __expf(zd[e] * invT - jb.lse2), 0.f) : p;
+      }
+      w4[e] = xw;
+      mine += xw;
+    }
+    const float incl = wave_incl_scan(mine);
+    if (lane == 63) s_wt[wave] = incl;
+    __syncthreads();
+    float run = base, hbase = 0.f, lbase = 0.f;
+    int hw = -1, lw = -1;
+#pragma unroll
+    for (int w = 0; w < T2_NT2 / 64; ++w) {
+      const float x = s_wt[w];
+      if (x > 0.f) {
+        if (hw < 0 && run + x > target) {
+          hw = w;
+          hbase = run;
+        }
+        lw = w;
+        lbase = run;
+      }
+      run += x;
+    }
+    float tgt = target;
+    if (hw < 0) {  // rounding left the target beyond the end: the last token of positive weight
+      hw = lw;
+      hbase = lbase;
+      tgt = INFINITY;
+    }
+    if (hw < 0) {
+      if (t == 0) out[jb.out_index] = min(max(v0, 0), V - 1);
+    } else if (wave == hw) {
+      float dummy;
+      const int v = wave_find(w4, 4, vt, hbase, incl, mine, tgt, &dummy);
+      if (lane == 0) out[jb.out_index] = min(max(v, 0), V - 1);
+    }
+  }
+  if (job == 0 && fin.acc) finalize_block(fin);
 }
 
 // Confidence of each draft row: conf = max_v q(v) = 1 / sum_v exp((z_v - max z)/T).  One wave per row.
@@ -1580,11 +1679,22 @@ int sample_chunks(int V) {
 
 hipError_t launch_sample(const SampleJob *jobs, int njobs, int V, float invT, float *chunk_sums, int32_t *out,
                          int32_t *job_cnt, int32_t *done_cnt, const FinalizeArgs &fin, hipStream_t st) {
+  (void)job_cnt;
+  (void)done_cnt;
   if (njobs <= 0) return hipSuccess;
   const int C = sample_chunks(V);
-  const int chunk = (V + C - 1) / C;
-  hipLaunchKernelGGL(k_sample, dim3(C, njobs), dim3(NT), 0, st, jobs, njobs, V, chunk, invT, chunk_sums, out, job_cnt,
-                     done_cnt, fin);
+  // chunks of a multiple of 64 tokens (at most NT * PER): 16-byte aligned when V % 4 == 0
+  const int chunk = (((V + C - 1) / C) + 63) / 64 * 64;
+  const dim3 grid((C + SUBS - 1) / SUBS, njobs);
+  if (V % 4 == 0) {
+    hipLaunchKernelGGL(k_sample_sums<true>, grid, dim3(NT), 0, st, jobs, V, chunk, C, invT, chunk_sums);
+    hipLaunchKernelGGL(k_sample_pick<true>, dim3(njobs), dim3(T2_NT2), 0, st, jobs, V, chunk, C, invT,
+                       (const float *)chunk_sums, out, fin);
+  } else {
+    hipLaunchKernelGGL(k_sample_sums<false>, grid, dim3(NT), 0, st, jobs, V, chunk, C, invT, chunk_sums);
+    hipLaunchKernelGGL(k_sample_pick<false>, dim3(njobs), dim3(T2_NT2), 0, st, jobs, V, chunk, C, invT,
+                       (const float *)chunk_sums, out, fin);
+  }
   return hipGetLastError();
 }
 
