@@ -1061,83 +1061,130 @@ __global__ __launch_bounds__(NT) void k_row_conf(const StatPart *parts, int nslo
 }
 
 // ---- confidence schedule (single block).
+// Exclusive prefix sum of v over the block in thread order (blockDim.x <= 1024); *total
+// gets the block total.  buf needs 16 ints.  Every thread must call it.
+__device__ int block_excl_scan_int(int v, int *buf, int *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) buf[wave] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int bw = buf[w];
+    if (w < wave) base += bw;
+    tot += bw;
+  }
+  *total = tot;
+  return base + x - v;
+}
+
+// The verify length of every request (one block of 1024 threads).  Survival s_b(k) is
+// the running product of the draft confidences; entries with s >= threshold are
+// eligible (a prefix of each request).  When the eligible entries exceed the budget
+// beyond the B target rows (R), the R entries with the largest key floor(1024 s) are
+// kept, ties in (request, position) order: the cut key comes from a suffix scan of the
+// key histogram, the rank of each entry at the cut key from a prefix scan.  Because keys
+// do not increase along a request, the kept entries are a prefix of each request.
 __global__ __launch_bounds__(1024) void k_schedule(const ScheduleArgs a) {
   extern __shared__ int smi[];
   const int B = a.B, Km = a.Kmax, n = B * Km;
-  int *keys = smi;          // [n]   key of eligible entries, -1 otherwise
+  int *keys = smi;          // [n]   confidences (as float bits), then keys: -1 if not eligible
   int *hist = smi + n;      // [1025]
   int *kb = hist + 1025;    // [B]
-  __shared__ int s_cut, s_take_at_cut, s_nelig;
+  __shared__ int s_buf[16];
+  __shared__ int s_nelig, s_cut, s_take, s_S1;
   const int tid = threadIdx.x, nt = blockDim.x;
   if (a.status_reset && tid == 0) *a.status_reset = 0;
-  __syncthreads();
+  for (int i = tid; i < n; i += nt) keys[i] = __float_as_int(a.conf[i]);
   for (int i = tid; i < 1025; i += nt) hist[i] = 0;
+  if (tid == 0) {
+    s_nelig = 0;
+    s_cut = -2;
+  }
   __syncthreads();
-  // 2. survival products per request (fp32, ascending k) and keys
+  // survival products per request (fp32, ascending k) and keys
   for (int b = tid; b < B; b += nt) {
-    float s = 1.f;
+    float sv = 1.f;
     int lead = 0;
     bool alive = true;
     for (int k = 0; k < Km; ++k) {
-      s *= a.conf[b * Km + k];
-      const bool el = alive && (s >= a.threshold);
+      sv *= __int_as_float(keys[b * Km + k]);
+      const bool el = alive && (sv >= a.threshold);
       alive = el;
-      keys[b * Km + k] = el ? (int)floorf(1024.f * s) : -1;
+      keys[b * Km + k] = el ? (int)floorf(1024.f * sv) : -1;
       if (el) ++lead;
     }
     kb[b] = lead;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int tot = 0;
-    for (int b = 0; b < B; ++b) tot += kb[b];
-    s_nelig = tot;
+    atomicAdd(&s_nelig, lead);
   }
   __syncthreads();
   const int R = a.budget - B;  // positions that may be added beyond the B target rows
-  if (s_nelig > R) {
+  if (s_nelig > R) {           // block-uniform
     for (int i = tid; i < n; i += nt)
       if (keys[i] >= 0) atomicAdd(&hist[min(keys[i], 1024)], 1);
+    for (int b = tid; b < B; b += nt) kb[b] = 0;
     __syncthreads();
-    if (tid == 0) {
-      int above = 0, cut = 1024;
-      for (; cut >= 0; --cut) {
-        if (above + hist[cut] >= R) break;
-        above += hist[cut];
+    // S(c) = number of eligible keys >= c; thread t covers c = 1024 - t (c >= 1)
+    {
+      const int c = 1024 - tid;
+      const int h = (tid < 1024 && c >= 1) ? hist[c] : 0;
+      int tot;
+      const int excl = block_excl_scan_int(h, s_buf, &tot);
+      const int incl = excl + h;  // S(c); excl = S(c + 1)
+      if (tid < 1024 && c >= 1 && incl >= R && excl < R) {
+        s_cut = c;
+        s_take = R - excl;
       }
-      s_cut = cut;
-      s_take_at_cut = R - above;  // entries with key == cut to keep, in (b, k) order
+      if (c == 1) s_S1 = incl;
     }
     __syncthreads();
-    if (tid == 0) {
-      int left = s_take_at_cut;
-      for (int b = 0; b < B; ++b) {
-        int k = 0;
-        for (; k < Km; ++k) {
-          const int key = keys[b * Km + k];
-          if (key > s_cut) continue;
-          if (key == s_cut && left > 0) { --left; continue; }
-          break;
-        }
-        kb[b] = k;
+    if (tid == 0 && s_cut == -2) {
+      if (R <= 0) {  // nothing beyond the target rows: the cut sits above every key
+        s_cut = 1024;
+        s_take = 0;
+      } else {       // S(1) < R <= S(0)
+        s_cut = 0;
+        s_take = R - s_S1;
       }
+    }
+    __syncthreads();
+    const int cut = s_cut, take = s_take;
+    // rank of each entry at the cut key in (request, position) order, 1024 entries a pass
+    int carry = 0;
+    for (int i0 = 0; i0 < n; i0 += nt) {
+      const int i = i0 + tid;
+      const int key = i < n ? keys[i] : -1;
+      int tot;
+      const int rank = carry + block_excl_scan_int(key == cut ? 1 : 0, s_buf, &tot);
+      if (i < n && (key > cut || (key == cut && rank < take))) atomicAdd(&kb[i / Km], 1);
+      carry += tot;
     }
     __syncthreads();
   }
-  // 3. offsets and the packed row map
-  if (tid == 0) {
-    int off = 0;
-    for (int b = 0; b < B; ++b) {
+  // offsets (exclusive scan of k_b + 1), the packed row map and the verify lengths
+  int carry = 0;
+  for (int b0 = 0; b0 < B; b0 += nt) {
+    const int b = b0 + tid;
+    const int len = b < B ? kb[b] + 1 : 0;
+    int tot;
+    const int off = carry + block_excl_scan_int(len, s_buf, &tot);
+    if (b < B) {
       a.row_off[b] = off;
-      for (int j = 0; j <= kb[b]; ++j) a.row_map[off + j] = b * (Km + 1) + j;
-      off += kb[b] + 1;
+      for (int j = 0; j < len; ++j) a.row_map[off + j] = b * (Km + 1) + j;
+      a.verify_len[b] = len - 1;
+      if (a.verify_len_out) a.verify_len_out[b] = len - 1;
     }
-    a.row_off[B] = off;
-    *a.m_total = off;
+    carry += tot;
   }
-  for (int b = tid; b < B; b += nt) {
-    a.verify_len[b] = kb[b];
-    if (a.verify_len_out) a.verify_len_out[b] = kb[b];
+  if (tid == 0) {
+    a.row_off[B] = carry;
+    *a.m_total = carry;
   }
 }
 
