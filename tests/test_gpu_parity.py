@@ -132,6 +132,31 @@ def _run_greedy(wk, rep=0, fp8=False):
     return ref, out
 
 
+# Two reduced shapes aimed at tiling paths of the larger-batch GEMMs:
+#  * 20 requests x 8 rows = 160 target rows: gate/up and down run on 192-row tiles (one row
+#    tile per column tile), the 300-row sampled LM head on 128 x 256 tiles;
+#  * 128 requests x 8 rows = 1024 rows, V = 24000: 94 column tiles of 256 x 4 row tiles =
+#    376 tiles = one round of 256 + 120, so columns [0, 16384) run as 256 x 256 tiles and
+#    the ragged rest (7616 columns, 240 tiles of 256 x 128) as a second launch whose
+#    argmax indices and statistic slots are offset.
+MLP160 = wl.Workload("mlp160", 14, B=20, K=7, d=256, d_ff=1536, V=5003, T=1.0, sigma=(0.3, 1.2))
+LM_SPLIT = wl.Workload("lm_split", 15, B=128, K=7, d=256, d_ff=512, V=24000, T=1.0, sigma=(0.3, 1.2))
+
+
+def test_sample_parity_160_rows():
+    _run_sample(MLP160)
+
+
+def test_greedy_parity_160_rows():
+    ref, out = _run_greedy(MLP160)
+    _check_hidden(out.hidden, ref["y"], MLP160.M_t)
+
+
+def test_greedy_parity_lm_head_in_two_launches():
+    ref, out = _run_greedy(LM_SPLIT)
+    _check_hidden(out.hidden, ref["y"], LM_SPLIT.M_t)
+
+
 @pytest.mark.parametrize("name", ["small", "small_wide", "small_batch", "tiny"])
 def test_greedy_parity(name):
     wk = wl.PRESETS[name]
