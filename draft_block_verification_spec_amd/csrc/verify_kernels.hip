@@ -325,232 +325,7 @@ __global__ __launch_bounds__(1024) void k_accept_greedy(const AcceptArgs a) {
   if (a.B > 1 && a.fin.acc && arrive_last(a.done_cnt, a.B, &flag)) finalize_block(a.fin);
 }
 
-// Merge the nslots partials of one row with the whole block (fixed order); every
-// thread gets the result.  red holds one record per wave.
-__device__ StatPart block_merge_row(const StatPart *parts, int nslots, float invT, bool want_s, StatPart *red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  StatPart st = stat_empty();
-  for (int i = threadIdx.x; i < nslots; i += blockDim.x) st = stat_merge(st, parts[i], invT, want_s);
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) st = stat_merge(st, stat_shfl_xor(st, off), invT, want_s);
-  __syncthreads();
-  if (lane == 0) red[wave] = st;
-  __syncthreads();
-  StatPart r = red[0];
-  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r = stat_merge(r, red[w], invT, want_s);
-  return r;
-}
-
-// ---- small-batch tail.  For every request b and every possible first rejection
-// point j = 0..K_b the token that would be emitted there is drawn with the request's
-// final coin: from the normalised max(0, p_j - q_j) (p_j if that is all zero) for
-// j < K_b, from p_{K_b} for j = K_b.  That is the same draw as after the acceptance
-// scan, prepared for every j at once so the scan and the sampling do not wait on each
-// other.  Two kernels, no inter-block signalling (a device-scope release per block
-// costs more than the kernel boundary it would save):
-//  * tail1, blocks (chunk group, candidate): merges the row statistics of the
-//    candidate's rows and sums the sampling weights over SUBS chunks of V; the first
-//    chunk group also decides acceptance of draft token j and writes the row
-//    diagnostics;
-//  * tail2, one block per request: the acceptance scan over the flags, then the draw
-//    of the candidate at the first rejection from its chunk sums and chunk; block 0
-//    also does the call-wide bookkeeping.
-constexpr int SUBS = 5;  // sampling chunks per tail1 block
-// acceptance flag bits
-constexpr int FLAG_ACCEPT = 1, FLAG_BAD_TOKEN = 2, FLAG_NONFINITE = 4;
-
-// Acceptance scan of one request over the flags (one wave): A = first rejected position
-// (K_b if none); bad = union of the problem bits of positions 0..K_b.
-__device__ void scan_flags(const int32_t *fl, int Kb, int &A, int &bad) {
-  const int lane = threadIdx.x & 63;
-  A = Kb;
-  bool rej = false;
-  int badm = 0;
-  for (int base = 0; base <= Kb; base += 64) {
-    const int jj = base + lane;
-    const int f = jj <= Kb ? fl[jj] : FLAG_ACCEPT;
-    badm |= f & (FLAG_BAD_TOKEN | FLAG_NONFINITE);
-    const unsigned long long rm = __ballot(jj < Kb && !(f & FLAG_ACCEPT));
-    if (!rej && rm) {
-      A = base + __ffsll((long long)rm) - 1;
-      rej = true;
-    }
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) badm |= __shfl_xor(badm, off);
-  bad = badm;
-}
-
-// Merge the partials of two rows at once with the whole block (fixed order); the
-// second row is optional (p1 null); n0 / n1 partials per row.  f0 / f1 are this thread's first partials (slot
-// threadIdx.x), loaded by the caller ahead of its other loads.  Every thread gets both
-// results.  red holds one record per wave and row.
-__device__ void block_merge_two(const StatPart *p0, int n0, const StatPart *p1, int n1, float invT, StatPart s0,
-                                StatPart s1, StatPart (*red)[NT / 64], StatPart &r0, StatPart &r1) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int i = threadIdx.x + blockDim.x; i < n0; i += blockDim.x) s0 = stat_merge(s0, p0[i], invT, true);
-  if (p1)
-    for (int i = threadIdx.x + blockDim.x; i < n1; i += blockDim.x) s1 = stat_merge(s1, p1[i], invT, true);
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    s0 = stat_merge(s0, stat_shfl_xor(s0, off), invT, true);
-    if (p1) s1 = stat_merge(s1, stat_shfl_xor(s1, off), invT, true);
-  }
-  if (lane == 0) {
-    red[0][wave] = s0;
-    red[1][wave] = s1;
-  }
-  __syncthreads();
-  r0 = red[0][0];
-  r1 = red[1][0];
-  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) {
-    r0 = stat_merge(r0, red[0][w], invT, true);
-    if (p1) r1 = stat_merge(r1, red[1][w], invT, true);
-  }
-}
-
-// VEC: V and the chunk length are multiples of 4, so each thread reads 16-byte pieces.
-// Every load the block needs is issued before the first wait: the acceptance inputs of
-// draft token j (token id first, then its two logits as soon as the id is in), this
-// thread's first statistic partial of both rows, and its logits of the block's chunks.
-template <bool VEC>
-__global__ __launch_bounds__(NT) void k_tail1(const AcceptArgs a, int chunk, int C, float *sums, float *lse_buf) {
-  __shared__ float red[NT / 64][2 * SUBS];
-  __shared__ StatPart reds[2][NT / 64];
-  const int Kmax = a.K, NJ = a.B * (Kmax + 1);
-  int32_t *flags = reinterpret_cast<int32_t *>(lse_buf + 2 * NJ);
-  const int job = blockIdx.y, cb = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int b = job / (Kmax + 1), j = job % (Kmax + 1);
-  const int Kb = a.verify_len ? a.verify_len[b] : Kmax;
-  if (j > Kb) return;
-  const long trow0 = a.row_off ? a.row_off[b] : (long)b * (Kmax + 1);
-  const long drow0 = (long)b * Kmax;
-  const bool resid_row = j < Kb;
-  const float invT = a.invT;
-  const bool acc_thr = cb == 0 && t == 0 && resid_row;  // decides acceptance of draft token j
-  int x = -1;
-  float coin = 0.f;
-  if (acc_thr) {
-    x = a.draft[drow0 + j];
-    coin = a.u[(long)b * (Kmax + 1) + j];
-  }
-  const StatPart *pt = a.parts_t + (trow0 + j) * a.nslots_t;
-  const StatPart *pd = resid_row ? a.parts_d + (drow0 + j) * a.nslots_d : nullptr;
-  const StatPart ft = t < a.nslots_t ? pt[t] : stat_empty();
-  const StatPart fd = (pd && t < a.nslots_d) ? pd[t] : stat_empty();
-  {
-    const float *z1 = a.logits_t + (trow0 + j) * (long)a.V;
-    const float *z2 = resid_row ? a.logits_d + (drow0 + j) * (long)a.V : nullptr;
-    // this thread's logits of the block's chunks (chunk <= NT * PER)
-    auto tok = [&](int q, int i) {
-      const int v0 = (cb * SUBS + q) * chunk;
-      return VEC ? v0 + (i >> 2) * (4 * NT) + 4 * t + (i & 3) : v0 + t + i * NT;
-    };
-    float zt[SUBS][PER], zd[SUBS][PER];
-#pragma unroll
-    for (int q = 0; q < SUBS; ++q) {
-      const int v1 = min(a.V, (cb * SUBS + q) * chunk + chunk);
-      if constexpr (VEC) {
-#pragma unroll
-        for (int i = 0; i < PER; i += 4) {
-          const int v = tok(q, i);
-          const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-          const f32x4 xv = v < v1 ? *reinterpret_cast<const f32x4 *>(z1 + v) : zero4;
-          const f32x4 yv = (z2 && v < v1) ? *reinterpret_cast<const f32x4 *>(z2 + v) : zero4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            zt[q][i + e] = xv[e];
-            zd[q][i + e] = yv[e];
-          }
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-          const int v = tok(q, i);
-          zt[q][i] = v < v1 ? z1[v] : 0.f;
-          zd[q][i] = (z2 && v < v1) ? z2[v] : 0.f;
-        }
-      }
-    }
-    const bool x_ok = x >= 0 && x < a.V;
-    float zx = 0.f, zdx = 0.f;
-    if (acc_thr && x_ok) {
-      zx = z1[x];
-      zdx = z2[x];
-    }
-    StatPart st_t, st_d;
-    block_merge_two(pt, a.nslots_t, pd, a.nslots_d, invT, ft, fd, reds, st_t, st_d);
-    const float lse1 = st_t.b1 * invT + __logf(st_t.s);
-    const float lse2 = resid_row ? st_d.b1 * invT + __logf(st_d.s) : 0.f;
-    // per chunk: sum of max(0, p - q) and of p over this thread's tokens (token order)
-    float part[2 * SUBS];
-#pragma unroll
-    for (int q = 0; q < SUBS; ++q) {
-      const int v1 = min(a.V, (cb * SUBS + q) * chunk + chunk);
-      float sr = 0.f, sp = 0.f;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        if (tok(q, i) < v1) {
-          const float p = __expf(zt[q][i] * invT - lse1);
-          sp += p;
-          if (z2) sr += fmaxf(p - __expf(zd[q][i] * invT - lse2), 0.f);
-        }
-      }
-      part[2 * q] = sr;
-      part[2 * q + 1] = sp;
-    }
-    // block sums of the 2*SUBS values: wave butterflies, then waves in a fixed order
-#pragma unroll
-    for (int k = 0; k < 2 * SUBS; ++k) {
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) part[k] += __shfl_xor(part[k], off);
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int k = 0; k < 2 * SUBS; ++k) red[wave][k] = part[k];
-    }
-    __syncthreads();
-    if (t < 2 * SUBS) {
-      const int c = cb * SUBS + (t >> 1);
-      float tot = 0.f;
-      for (int w = 0; w < NT / 64; ++w) tot += red[w][t];
-      if (c < C) sums[((long)job * C + c) * 2 + (t & 1)] = tot;
-    }
-    if (cb == 0 && t == 0) {
-      // first chunk group: normalisers, acceptance of draft token j, diagnostics
-      lse_buf[job] = lse1;
-      lse_buf[NJ + job] = lse2;
-      int flag = 0;
-      if (!isfinite(lse1) || (resid_row && !isfinite(lse2))) flag |= FLAG_NONFINITE;
-      if (resid_row) {
-        if (!x_ok) {
-          flag |= FLAG_BAD_TOKEN;
-        } else {
-          const float lpt = zx * invT - lse1;
-          const float lqd = zdx * invT - lse2;
-          const float ratio = __expf(lpt - lqd);
-          if (coin < ratio) flag |= FLAG_ACCEPT;
-          if (a.diag) {
-            float *dt = a.diag + ((long)b * (Kmax + 1) + j) * SV_DIAG_COLS;
-            dt[4] = zx; dt[5] = __expf(lpt); dt[6] = ratio;
-            float *dd = a.diag + ((long)a.B * (Kmax + 1) + drow0 + j) * SV_DIAG_COLS;
-            dd[4] = zdx; dd[5] = __expf(lqd);
-          }
-        }
-      }
-      flags[job] = flag;
-      if (a.diag) {
-        float *dg = a.diag + ((long)b * (Kmax + 1) + j) * SV_DIAG_COLS;
-        dg[0] = lse1; dg[1] = (float)st_t.i1; dg[2] = st_t.b1 - st_t.b2; dg[3] = st_t.b1; dg[7] = 0.f;
-        if (resid_row) {
-          float *dd = a.diag + ((long)a.B * (Kmax + 1) + drow0 + j) * SV_DIAG_COLS;
-          dd[0] = lse2; dd[1] = (float)st_d.i1; dd[2] = st_d.b1 - st_d.b2; dd[3] = st_d.b1;
-          dd[6] = 1.f / st_d.s; dd[7] = 0.f;
-        }
-      }
-    }
-  }
-}
+constexpr int SUBS = 5;  // sampling chunks per block of the chunk-sum kernel
 
 // Inclusive prefix sum over the 64 lanes of a wave, in lane order.
 __device__ __forceinline__ float wave_incl_scan(float v) {
@@ -661,204 +436,356 @@ __device__ int wave_find_grouped(const float (&w)[NG][NE], int first, float base
   return wave_find(ws, NE, first + gs * 64 * NE + lane * NE, gbase, is, ss, tgt, run_before);
 }
 
-constexpr int T2_CG = 4;     // groups of 64 chunk sums in tail2 (C <= 256)
-constexpr int T2_NT2 = 512;  // threads reading the chosen chunk in tail2, 4 tokens each (chunk <= 2048)
+constexpr int T2_CG = 4;     // groups of 64 chunk sums in a draw (C <= 256)
+constexpr int T2_NT2 = 512;  // threads reading the chosen chunk in a draw, 4 tokens each (chunk <= 2048)
 
-// tail2: one block per request.  Phase 1: wave w takes the candidate first-rejection
-// points j = w, w + nw, ... and finds, from tail1's chunk sums and the request's final
-// coin, the chunk its draw falls in; wave 0 meanwhile scans the acceptance flags.
-// Phase 2 (after one barrier): the first 512 threads read the chosen candidate's chunk
-// (4 tokens each, in token order over the threads) and the draw is located with a
-// block-wide scan.  Block 0 also does the call-wide bookkeeping from the flags of every
-// request.
+// The draw of one token by inverse CDF.  csums holds, per chunk of `chunk` tokens, the sum
+// of max(0, p - q) and the sum of p over the chunk (q from z2; without z2, or when all of
+// max(0, p - q) is zero, the draw is from p).  The chunk holding u * total comes from the
+// chunk sums (every wave finds it), the token from that chunk's logits: thread t holds
+// tokens 4t .. 4t+3 of the chunk and a block scan locates the draw.  Called by all T2_NT2
+// threads of the block; every thread gets the token.
 template <bool VEC>
-__global__ __launch_bounds__(1024) void k_tail2(const AcceptArgs a, int chunk, int C, const float *sums,
-                                                const float *lse_buf, FinalizeArgs fin) {
-  __shared__ int s_pick[64];
-  __shared__ float s_base[64], s_target[64];
-  __shared__ int s_resid[64];
-  __shared__ int s_A, s_v;
-  __shared__ float s_wt[T2_NT2 / 64];
-  __shared__ long long s_tot[16][4];
-  const int Kmax = a.K, NJ = a.B * (Kmax + 1);
-  const int32_t *flags = reinterpret_cast<const int32_t *>(lse_buf + 2 * NJ);
-  const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6, nw = blockDim.x >> 6;
+__device__ int pick_token(const float *z1, const float *z2, float lse1, float lse2, float u, const float *csums, int C,
+                          int chunk, int V, float invT, float *s_wt, int *s_v) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  float wr[T2_CG][1], wp[T2_CG][1];
+#pragma unroll
+  for (int g = 0; g < T2_CG; ++g) {
+    const int c = 64 * g + lane;
+    float2 v = make_float2(0.f, 0.f);
+    if (c < C) v = *reinterpret_cast<const float2 *>(csums + 2 * (long)c);
+    wr[g][0] = v.x;
+    wp[g][0] = v.y;
+  }
+  float lr = 0.f, lp = 0.f;
+#pragma unroll
+  for (int g = 0; g < T2_CG; ++g) {
+    lr += wr[g][0];
+    lp += wp[g][0];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    lr += __shfl_xor(lr, off);
+    lp += __shfl_xor(lp, off);
+  }
+  const bool resid = z2 != nullptr && lr > 0.f;
+  const float target = u * (resid ? lr : lp);
+  float base;
+  const int pick = resid ? wave_find_grouped(wr, 0, 0.f, target, &base) : wave_find_grouped(wp, 0, 0.f, target, &base);
+  const float *zq = resid ? z2 : nullptr;
+  const int v0 = pick * chunk, v1 = min(V, v0 + chunk);
+  const int vt = v0 + 4 * t;
+  float zt[4], zd[4];
+  if constexpr (VEC) {
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 xv = vt < v1 ? *reinterpret_cast<const f32x4 *>(z1 + vt) : zero4;
+    const f32x4 yv = (zq && vt < v1) ? *reinterpret_cast<const f32x4 *>(zq + vt) : zero4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      zt[e] = xv[e];
+      zd[e] = yv[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      zt[e] = vt + e < v1 ? z1[vt + e] : 0.f;
+      zd[e] = (zq && vt + e < v1) ? zq[vt + e] : 0.f;
+    }
+  }
+  float w4[4];
+  float mine = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float xw = 0.f;
+    if (vt + e < v1) {
+      const float p = __expf(zt[e] * invT - lse1);
+      xw = resid ? fmaxf(p - __expf(zd[e] * invT - lse2), 0.f) : p;
+    }
+    w4[e] = xw;
+    mine += xw;
+  }
+  const float incl = wave_incl_scan(mine);
+  if (lane == 63) s_wt[wave] = incl;
+  __syncthreads();
+  // the wave holding the draw (same decision in every wave)
+  float run = base, hbase = 0.f, lbase = 0.f;
+  int hw = -1, lw = -1;
+#pragma unroll
+  for (int w = 0; w < T2_NT2 / 64; ++w) {
+    const float x = s_wt[w];
+    if (x > 0.f) {
+      if (hw < 0 && run + x > target) {
+        hw = w;
+        hbase = run;
+      }
+      lw = w;
+      lbase = run;
+    }
+    run += x;
+  }
+  float tgt = target;
+  if (hw < 0) {  // rounding left the target beyond the end: the last token of positive weight
+    hw = lw;
+    hbase = lbase;
+    tgt = INFINITY;
+  }
+  if (hw < 0) {
+    if (t == 0) *s_v = min(max(v0, 0), V - 1);
+  } else if (wave == hw) {
+    float dummy;
+    const int v = wave_find(w4, 4, vt, hbase, incl, mine, tgt, &dummy);
+    if (lane == 0) *s_v = min(max(v, 0), V - 1);
+  }
+  __syncthreads();
+  return *s_v;
+}
+
+// Merge two rows' statistic partials with one wave, the loads of both rows issued
+// together (BATCH per lane and row at a time); p1 may be null.  Same order of merges as
+// wave_merge_row, so the same results.
+template <int BATCH>
+__device__ void wave_merge_rows2(const StatPart *p0, const StatPart *p1, int nslots, float invT, StatPart &o0,
+                                 StatPart &o1) {
+  const int lane = threadIdx.x & 63;
+  StatPart s0 = stat_empty(), s1 = stat_empty();
+  for (int i0 = 0; i0 < nslots; i0 += 64 * BATCH) {
+    StatPart q0[BATCH], q1[BATCH];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int i = i0 + 64 * k + lane;
+      q0[k] = i < nslots ? p0[i] : stat_empty();
+      q1[k] = (p1 && i < nslots) ? p1[i] : stat_empty();
+    }
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      s0 = stat_merge(s0, q0[k], invT, true);
+      if (p1) s1 = stat_merge(s1, q1[k], invT, true);
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    s0 = stat_merge(s0, stat_shfl_xor(s0, off), invT, true);
+    if (p1) s1 = stat_merge(s1, stat_shfl_xor(s1, off), invT, true);
+  }
+  o0 = s0;
+  o1 = s1;
+}
+
+// ---- small-batch tail (B * (K+1) <= 32), two kernels, no inter-block signalling.
+// tail_a, blocks (pair of sampling chunks, request): every block merges its request's row
+// statistics (one wave per pair of rows; the draft ids, coins and logits at the drafts
+// are loaded first), decides acceptance left to right (Statement 1: u < p(x)/q(x)), and
+// sums the sampling weights of the draw at the first rejection A over its two chunks:
+// max(0, p - q) and p from target row A and draft row A (p alone for the bonus row
+// A = K_b).  So only the accepted candidate's two rows are read.  The request's first
+// block also writes A, the accepted length, the row diagnostics and the device status.
+// tail_b, one block per request: the draw (pick_token) with the request's final coin and
+// the emitted tokens; its block 0 writes tau and the counters.
+constexpr int TA_NT = 1024;  // tail_a: 512 threads per chunk, 4 tokens each
+
+template <bool VEC>
+__global__ __launch_bounds__(TA_NT) void k_tail_a(const AcceptArgs a, int chunk, int C, float *sums, float *req) {
+  __shared__ float s_lse_t[64], s_lse_d[64];
+  __shared__ int s_rowbad[128];
+  __shared__ int s_A;
+  __shared__ float s_red[TA_NT / 64][2];
+  const int Kmax = a.K;
+  const int b = blockIdx.y, cb = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  constexpr int NW = TA_NT / 64;
   const int Kb = a.verify_len ? a.verify_len[b] : Kmax;
   const long trow0 = a.row_off ? a.row_off[b] : (long)b * (Kmax + 1);
   const long drow0 = (long)b * Kmax;
   const float invT = a.invT;
-  const int jb0 = b * (Kmax + 1);
-  if (wave == 0) {
-    int A, bad;
-    scan_flags(flags + jb0, Kb, A, bad);
-    if (lane == 0) {
-      if (bad & FLAG_BAD_TOKEN) set_status(a.dev_status, SV_DEV_BAD_TOKEN);
-      if (bad & FLAG_NONFINITE) set_status(a.dev_status, SV_DEV_NONFINITE);
-      s_A = bad ? -1 : A;
+  const bool lead = cb == 0;  // the request's first block writes its results
+  // wave 0: the inputs of the first 64 acceptance decisions, ahead of the statistics
+  int x0 = 0;
+  float u0 = 0.f, zt0 = 0.f, zd0 = 0.f;
+  if (wave == 0 && lane < Kb) {
+    x0 = a.draft[drow0 + lane];
+    u0 = a.u[(long)b * (Kmax + 1) + lane];
+    if (x0 >= 0 && x0 < a.V) {
+      zt0 = a.logits_t[(trow0 + lane) * (long)a.V + x0];
+      zd0 = a.logits_d[(drow0 + lane) * (long)a.V + x0];
     }
   }
-  if (b == 0 && fin.acc) {
-    // bookkeeping over every request (integer sums: order-independent)
-    long long sa = 0, sd = 0, se = 0, nv = 0;
-    for (int bb = wave; bb < a.B; bb += nw) {
-      const int Kbb = a.verify_len ? a.verify_len[bb] : Kmax;
-      int Ab, bad;
-      scan_flags(flags + bb * (Kmax + 1), Kbb, Ab, bad);
-      if (!bad) {
-        sa += Ab;
-        sd += Kbb;
-        se += Ab + 1;
-        nv += 1;
+  // row statistics: rows r = 0..Kb are target rows, r = Kb+1..2Kb draft rows 0..Kb-1
+  const int nrows = 2 * Kb + 1;
+  auto rowp = [&](int r) -> const StatPart * {
+    if (r >= nrows) return nullptr;
+    return r <= Kb ? a.parts_t + (trow0 + r) * a.nslots_t : a.parts_d + (drow0 + r - Kb - 1) * a.nslots_d;
+  };
+  auto finish_row = [&](int r, const StatPart &st) {
+    const bool is_t = r <= Kb;
+    const int j = is_t ? r : r - Kb - 1;
+    const float lse = st.b1 * invT + __logf(st.s);
+    if (lane == 0) {
+      if (is_t) s_lse_t[j] = lse; else s_lse_d[j] = lse;
+      s_rowbad[r] = isfinite(lse) ? 0 : 1;
+      if (lead && a.diag) {
+        const long drow = is_t ? (long)b * (Kmax + 1) + j : (long)a.B * (Kmax + 1) + drow0 + j;
+        float *dg = a.diag + drow * SV_DIAG_COLS;
+        dg[0] = lse; dg[1] = (float)st.i1; dg[2] = st.b1 - st.b2; dg[3] = st.b1;
+        dg[4] = NAN; dg[5] = NAN; dg[6] = is_t ? NAN : 1.f / st.s; dg[7] = 0.f;
       }
     }
-    if (lane == 0) {
-      s_tot[wave][0] = sa;
-      s_tot[wave][1] = sd;
-      s_tot[wave][2] = se;
-      s_tot[wave][3] = nv;
+  };
+  for (int r0 = wave; r0 < nrows; r0 += 2 * NW) {
+    const int r1 = r0 + NW;
+    if (a.nslots_t == a.nslots_d || (r0 <= Kb) == (r1 <= Kb)) {
+      const int ns = r0 <= Kb ? a.nslots_t : a.nslots_d;
+      StatPart s0, s1;
+      wave_merge_rows2<4>(rowp(r0), rowp(r1), ns, invT, s0, s1);
+      finish_row(r0, s0);
+      if (r1 < nrows) finish_row(r1, s1);
+    } else {
+      finish_row(r0, wave_merge_row<8>(rowp(r0), r0 <= Kb ? a.nslots_t : a.nslots_d, invT, true));
+      if (r1 < nrows) finish_row(r1, wave_merge_row<8>(rowp(r1), r1 <= Kb ? a.nslots_t : a.nslots_d, invT, true));
     }
   }
-  const float coin = a.u[(long)b * (Kmax + 1) + Kmax];
-  // ---- phase 1: the chunk of every candidate's draw
-  for (int j = wave; j <= Kb && j < 64; j += nw) {
-    const int cj = jb0 + j;
-    // chunk sums of the candidate (sum of max(0, p - q), sum of p): chunk 64 g + lane
-    float wr[T2_CG][1], wp[T2_CG][1];
-#pragma unroll
-    for (int g = 0; g < T2_CG; ++g) {
-      const int c = 64 * g + lane;
-      float2 v = make_float2(0.f, 0.f);
-      if (c < C) v = *reinterpret_cast<const float2 *>(sums + ((long)cj * C + c) * 2);
-      wr[g][0] = v.x;
-      wp[g][0] = v.y;
+  __syncthreads();
+  // acceptance, left to right: lane j of wave 0 handles draft position j+1
+  if (wave == 0) {
+    bool ok = true, rej = false;
+    int A = 0;
+    for (int base = 0; base < Kb; base += 64) {
+      const int j = base + lane;
+      bool acc = false, bad_tok = false;
+      if (j < Kb) {
+        const int x = base == 0 ? x0 : a.draft[drow0 + j];
+        if (x < 0 || x >= a.V) {
+          bad_tok = true;
+        } else {
+          const float zt = base == 0 ? zt0 : a.logits_t[(trow0 + j) * (long)a.V + x];
+          const float zd = base == 0 ? zd0 : a.logits_d[(drow0 + j) * (long)a.V + x];
+          const float lpt = zt * invT - s_lse_t[j];
+          const float lqd = zd * invT - s_lse_d[j];
+          const float ratio = __expf(lpt - lqd);
+          const float u = base == 0 ? u0 : a.u[(long)b * (Kmax + 1) + j];
+          acc = u < ratio;
+          if (lead && a.diag) {
+            float *dt = a.diag + ((long)b * (Kmax + 1) + j) * SV_DIAG_COLS;
+            dt[4] = zt; dt[5] = __expf(lpt); dt[6] = ratio;
+            float *dd = a.diag + ((long)a.B * (Kmax + 1) + drow0 + j) * SV_DIAG_COLS;
+            dd[4] = zd; dd[5] = __expf(lqd);
+          }
+        }
+      }
+      if (__any(bad_tok)) ok = false;
+      if (!rej) {
+        const unsigned long long live = (Kb - base >= 64) ? ~0ull : ((1ull << (Kb - base)) - 1ull);
+        const unsigned long long rejm = __ballot(!acc) & live;
+        if (rejm) {
+          A = base + __ffsll((long long)rejm) - 1;
+          rej = true;
+        } else {
+          A = min(Kb, base + 64);
+        }
+      }
     }
-    float lr = 0.f, lp = 0.f;
-#pragma unroll
-    for (int g = 0; g < T2_CG; ++g) {
-      lr += wr[g][0];
-      lp += wp[g][0];
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      lr += __shfl_xor(lr, off);
-      lp += __shfl_xor(lp, off);
-    }
-    const bool resid = j < Kb && lr > 0.f;
-    const float target = coin * (resid ? lr : lp);
-    float base;
-    const int pick = resid ? wave_find_grouped(wr, 0, 0.f, target, &base) : wave_find_grouped(wp, 0, 0.f, target, &base);
+    int rb = 0;
+    for (int r = lane; r < nrows; r += 64) rb |= s_rowbad[r];
+    const bool nonfinite = __any(rb != 0);
     if (lane == 0) {
-      s_pick[j] = pick;
-      s_base[j] = base;
-      s_target[j] = target;
-      s_resid[j] = resid;
+      const bool good = ok && !nonfinite;
+      s_A = good ? A : -1;
+      if (lead) {
+        if (!ok) set_status(a.dev_status, SV_DEV_BAD_TOKEN);
+        if (nonfinite) set_status(a.dev_status, SV_DEV_NONFINITE);
+        a.accepted_len[b] = good ? A : -1;
+      }
     }
   }
   __syncthreads();
   const int A = s_A;
+  if (A < 0) {
+    if (lead && t == 0) req[3 * b] = __int_as_float(-1);
+    return;
+  }
+  // sampling weights of the draw at A over this block's chunks 2 cb and 2 cb + 1
+  const bool resid = A < Kb;
+  const float lse1 = s_lse_t[A], lse2 = resid ? s_lse_d[A] : 0.f;
+  const float *z1 = a.logits_t + (trow0 + A) * (long)a.V;
+  const float *z2 = resid ? a.logits_d + (drow0 + A) * (long)a.V : nullptr;
+  const int c = 2 * cb + (t >> 9);
+  const int v0 = c * chunk, v1 = min(a.V, v0 + chunk);
+  const int vt = v0 + 4 * (t & 511);
+  float zt[4], zd[4];
+  if constexpr (VEC) {
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 xv = vt < v1 ? *reinterpret_cast<const f32x4 *>(z1 + vt) : zero4;
+    const f32x4 yv = (z2 && vt < v1) ? *reinterpret_cast<const f32x4 *>(z2 + vt) : zero4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      zt[e] = xv[e];
+      zd[e] = yv[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      zt[e] = vt + e < v1 ? z1[vt + e] : 0.f;
+      zd[e] = (z2 && vt + e < v1) ? z2[vt + e] : 0.f;
+    }
+  }
+  float sr = 0.f, sp = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (vt + e < v1) {
+      const float p = __expf(zt[e] * invT - lse1);
+      sp += p;
+      if (z2) sr += fmaxf(p - __expf(zd[e] * invT - lse2), 0.f);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    sr += __shfl_xor(sr, off);
+    sp += __shfl_xor(sp, off);
+  }
+  if (lane == 0) {
+    s_red[wave][0] = sr;
+    s_red[wave][1] = sp;
+  }
+  __syncthreads();
+  if (t < 4) {
+    const int h = t >> 1, k = t & 1;  // chunk 2 cb + h: waves 8 h .. 8 h + 7, in order
+    float tot = 0.f;
+    for (int w = 8 * h; w < 8 * h + 8; ++w) tot += s_red[w][k];
+    const int cc = 2 * cb + h;
+    if (cc < C) sums[((long)b * C + cc) * 2 + k] = tot;
+  }
+  if (lead && t == 0) {
+    req[3 * b] = __int_as_float(A);
+    req[3 * b + 1] = lse1;
+    req[3 * b + 2] = lse2;
+  }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(T2_NT2) void k_tail_b(const AcceptArgs a, int chunk, int C, const float *sums,
+                                                   const float *req, FinalizeArgs fin) {
+  __shared__ float s_wt[T2_NT2 / 64];
+  __shared__ int s_v;
+  const int Kmax = a.K, b = blockIdx.x, t = threadIdx.x;
+  const int A = __float_as_int(req[3 * b]);
+  const int Kb = a.verify_len ? a.verify_len[b] : Kmax;
+  const long trow0 = a.row_off ? a.row_off[b] : (long)b * (Kmax + 1);
+  const long drow0 = (long)b * Kmax;
+  int v = -1;
   if (A >= 0) {
-    // ---- phase 2: the token inside the chosen chunk of candidate A
-    const int pick = s_pick[A];
-    const float base = s_base[A], target = s_target[A];
-    const bool resid = s_resid[A] != 0;
-    const float lse1 = lse_buf[jb0 + A], lse2 = lse_buf[NJ + jb0 + A];
     const float *z1 = a.logits_t + (trow0 + A) * (long)a.V;
-    const float *z2 = resid ? a.logits_d + (drow0 + A) * (long)a.V : nullptr;
-    const int v0 = pick * chunk, v1 = min(a.V, v0 + chunk);
-    const int vt = v0 + 4 * t;  // this thread's first token
-    float w4[4];
-    float mine = 0.f;
-    if (t < T2_NT2) {
-      float zt[4], zd[4];
-      if constexpr (VEC) {
-        const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 xv = vt < v1 ? *reinterpret_cast<const f32x4 *>(z1 + vt) : zero4;
-        const f32x4 yv = (z2 && vt < v1) ? *reinterpret_cast<const f32x4 *>(z2 + vt) : zero4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          zt[e] = xv[e];
-          zd[e] = yv[e];
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          zt[e] = vt + e < v1 ? z1[vt + e] : 0.f;
-          zd[e] = (z2 && vt + e < v1) ? z2[vt + e] : 0.f;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float xw = 0.f;
-        if (vt + e < v1) {
-          const float p = __expf(zt[e] * invT - lse1);
-          xw = resid ? fmaxf(p - __expf(zd[e] * invT - lse2), 0.f) : p;
-        }
-        w4[e] = xw;
-        mine += xw;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w4[e] = 0.f;
-    }
-    const float incl = wave_incl_scan(mine);
-    if (t < T2_NT2 && lane == 63) s_wt[wave] = incl;
-    __syncthreads();
-    // the wave holding the draw (same decision in every wave)
-    float run = base, hbase = 0.f, lbase = 0.f;
-    int hw = -1, lw = -1;
-#pragma unroll
-    for (int w = 0; w < T2_NT2 / 64; ++w) {
-      const float x = s_wt[w];
-      if (x > 0.f) {
-        if (hw < 0 && run + x > target) {
-          hw = w;
-          hbase = run;
-        }
-        lw = w;
-        lbase = run;
-      }
-      run += x;
-    }
-    float tgt = target;
-    if (hw < 0) {  // rounding left the target beyond the end: the last token of positive weight
-      hw = lw;
-      hbase = lbase;
-      tgt = INFINITY;
-    }
-    if (hw < 0) {
-      if (t == 0) s_v = v0;
-    } else if (wave == hw) {
-      float dummy;
-      const int v = wave_find(w4, 4, vt, hbase, incl, mine, tgt, &dummy);
-      if (lane == 0) s_v = min(max(v, 0), a.V - 1);
-    }
-    __syncthreads();
+    const float *z2 = A < Kb ? a.logits_d + (drow0 + A) * (long)a.V : nullptr;
+    v = pick_token<VEC>(z1, z2, req[3 * b + 1], req[3 * b + 2], a.u[(long)b * (Kmax + 1) + Kmax],
+                        sums + (long)b * C * 2, C, chunk, a.V, a.invT, s_wt, &s_v);
   }
-  const int v_pick = A >= 0 ? s_v : -1;
   for (int jj = t; jj <= Kmax; jj += blockDim.x) {
-    int v = -1;
+    int e = -1;
     if (A >= 0) {
-      if (jj < A) v = a.draft[drow0 + jj];
-      if (jj == A) v = v_pick;
+      if (jj < A) e = a.draft[drow0 + jj];
+      if (jj == A) e = v;
     }
-    a.emitted[(long)b * (Kmax + 1) + jj] = v;
+    a.emitted[(long)b * (Kmax + 1) + jj] = e;
   }
-  if (t == 0) a.accepted_len[b] = A;
-  if (b == 0 && fin.acc && t == 0) {
-    long long ta = 0, td = 0, te = 0, valid = 0;
-    for (int w = 0; w < nw; ++w) {
-      ta += s_tot[w][0];
-      td += s_tot[w][1];
-      te += s_tot[w][2];
-      valid += s_tot[w][3];
-    }
-    *fin.tau = valid ? (float)((double)te / (double)valid) : 0.f;
-    if (fin.counters) {
-      fin.counters[0] = (int64_t)ta;
-      fin.counters[1] = (int64_t)td;
-      fin.counters[2] = (int64_t)te;
-    }
-  }
+  if (b == 0 && fin.acc) finalize_block(fin);
 }
 
 // ---- inverse-CDF sampling of one token per job (larger batches, drafter step), two
@@ -945,99 +872,12 @@ __global__ __launch_bounds__(T2_NT2) void k_sample_pick(const SampleJob *jobs, i
                                                         const float *sums, int32_t *out, FinalizeArgs fin) {
   __shared__ float s_wt[T2_NT2 / 64];
   __shared__ int s_v;
-  const int job = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int job = blockIdx.x;
   const SampleJob jb = jobs[job];
   if (jb.out_index >= 0) {
-    // the chunk of the draw (every wave finds it; no barrier needed)
-    float wr[T2_CG][1], wp[T2_CG][1];
-#pragma unroll
-    for (int g = 0; g < T2_CG; ++g) {
-      const int c = 64 * g + lane;
-      float2 v = make_float2(0.f, 0.f);
-      if (c < C) v = *reinterpret_cast<const float2 *>(sums + ((long)job * C + c) * 2);
-      wr[g][0] = v.x;
-      wp[g][0] = v.y;
-    }
-    float lr = 0.f, lp = 0.f;
-#pragma unroll
-    for (int g = 0; g < T2_CG; ++g) {
-      lr += wr[g][0];
-      lp += wp[g][0];
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      lr += __shfl_xor(lr, off);
-      lp += __shfl_xor(lp, off);
-    }
-    const bool resid = jb.z2 != nullptr && lr > 0.f;
-    const float target = jb.u * (resid ? lr : lp);
-    float base;
-    const int pick = resid ? wave_find_grouped(wr, 0, 0.f, target, &base) : wave_find_grouped(wp, 0, 0.f, target, &base);
-    // the token inside the chunk: 4 tokens per thread in token order
-    const float *z1 = jb.z1;
-    const float *z2 = resid ? jb.z2 : nullptr;
-    const int v0 = pick * chunk, v1 = min(V, v0 + chunk);
-    const int vt = v0 + 4 * t;
-    float zt[4], zd[4];
-    if constexpr (VEC) {
-      const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-      const f32x4 xv = vt < v1 ? *reinterpret_cast<const f32x4 *>(z1 + vt) : zero4;
-      const f32x4 yv = (z2 && vt < v1) ? *reinterpret_cast<const f32x4 *>(z2 + vt) : zero4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        zt[e] = xv[e];
-        zd[e] = yv[e];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        zt[e] = vt + e < v1 ? z1[vt + e] : 0.f;
-        zd[e] = (z2 && vt + e < v1) ? z2[vt + e] : 0.f;
-      }
-    }
-    float w4[4];
-    float mine = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float xw = 0.f;
-      if (vt + e < v1) {
-        const float p = __expf(zt[e] * invT - jb.lse1);
-        xw = resid ? fmaxf(p - __expf(zd[e] * invT - jb.lse2), 0.f) : p;
-      }
-      w4[e] = xw;
-      mine += xw;
-    }
-    const float incl = wave_incl_scan(mine);
-    if (lane == 63) s_wt[wave] = incl;
-    __syncthreads();
-    float run = base, hbase = 0.f, lbase = 0.f;
-    int hw = -1, lw = -1;
-#pragma unroll
-    for (int w = 0; w < T2_NT2 / 64; ++w) {
-      const float x = s_wt[w];
-      if (x > 0.f) {
-        if (hw < 0 && run + x > target) {
-          hw = w;
-          hbase = run;
-        }
-        lw = w;
-        lbase = run;
-      }
-      run += x;
-    }
-    float tgt = target;
-    if (hw < 0) {  // rounding left the target beyond the end: the last token of positive weight
-      hw = lw;
-      hbase = lbase;
-      tgt = INFINITY;
-    }
-    if (hw < 0) {
-      if (t == 0) out[jb.out_index] = min(max(v0, 0), V - 1);
-    } else if (wave == hw) {
-      float dummy;
-      const int v = wave_find(w4, 4, vt, hbase, incl, mine, tgt, &dummy);
-      if (lane == 0) out[jb.out_index] = min(max(v, 0), V - 1);
-    }
+    const int v = pick_token<VEC>(jb.z1, jb.z2, jb.lse1, jb.lse2, jb.u, sums + (long)job * C * 2, C, chunk, V, invT,
+                                  s_wt, &s_v);
+    if (threadIdx.x == 0) out[jb.out_index] = v;
   }
   if (job == 0 && fin.acc) finalize_block(fin);
 }
@@ -1748,22 +1588,18 @@ hipError_t launch_sample(const SampleJob *jobs, int njobs, int V, float invT, fl
 hipError_t launch_tail_small(const AcceptArgs &a, float *sums, float *lse_buf, const FinalizeArgs &fin,
                              hipStream_t st) {
   const int C = sample_chunks(a.V);
-  // chunks of a multiple of 64 tokens (at most NT * PER): 16-byte aligned when V % 4 == 0
+  // chunks of a multiple of 64 tokens (at most NT * PER = 2048): 16-byte aligned when V % 4 == 0
   const int chunk = (((a.V + C - 1) / C) + 63) / 64 * 64;
-  const int NJ = a.B * (a.K + 1);
-  const dim3 grid((C + SUBS - 1) / SUBS, NJ);
-  if (a.V % 4 == 0)
-    hipLaunchKernelGGL(k_tail1<true>, grid, dim3(NT), 0, st, a, chunk, C, sums, lse_buf);
-  else
-    hipLaunchKernelGGL(k_tail1<false>, grid, dim3(NT), 0, st, a, chunk, C, sums, lse_buf);
-  // tail2: 1024 threads (phase 1: one wave per candidate; phase 2: the first 512 threads
-  // cover a chunk of at most 2048 tokens)
-  if (a.V % 4 == 0)
-    hipLaunchKernelGGL(k_tail2<true>, dim3(a.B), dim3(1024), 0, st, a, chunk, C, (const float *)sums,
+  const dim3 grid((C + 1) / 2, a.B);
+  if (a.V % 4 == 0) {
+    hipLaunchKernelGGL(k_tail_a<true>, grid, dim3(TA_NT), 0, st, a, chunk, C, sums, lse_buf);
+    hipLaunchKernelGGL(k_tail_b<true>, dim3(a.B), dim3(T2_NT2), 0, st, a, chunk, C, (const float *)sums,
                        (const float *)lse_buf, fin);
-  else
-    hipLaunchKernelGGL(k_tail2<false>, dim3(a.B), dim3(1024), 0, st, a, chunk, C, (const float *)sums,
+  } else {
+    hipLaunchKernelGGL(k_tail_a<false>, grid, dim3(TA_NT), 0, st, a, chunk, C, sums, lse_buf);
+    hipLaunchKernelGGL(k_tail_b<false>, dim3(a.B), dim3(T2_NT2), 0, st, a, chunk, C, (const float *)sums,
                        (const float *)lse_buf, fin);
+  }
   return hipGetLastError();
 }
 
