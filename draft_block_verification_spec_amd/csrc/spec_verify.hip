@@ -101,7 +101,7 @@ struct Plan {
   size_t o_a = 0, o_y = 0, o_part = 0, o_parts = 0, o_parts_d = 0, o_logits = 0, o_logits_d = 0,
          o_jobs = 0, o_sums = 0, o_conf = 0, o_vlen = 0, o_rowoff = 0, o_rowmap = 0, o_mtot = 0,
          o_hp = 0, o_sync = 0, o_lse = 0, o_tree = 0, total = 0;
-  bool small_tail = false;  // speculative per-position sampling + acceptance in one kernel
+  bool small_tail = false;  // B*(K+1) <= 32: acceptance in every chunk block, then the draw
 };
 
 bool valid_weights(const sv_weights *w) {
@@ -176,8 +176,8 @@ bool make_plan(int mode, int B, int K, const sv_weights *w, int budget, Plan &p)
     p.small_tail = NJ <= SMALL_TAIL_JOBS;
     p.o_logits = take(sizeof(float) * (size_t)p.M_lm * V);
     p.o_jobs = take(sizeof(SampleJob) * (size_t)B);
-    p.o_sums = take(sizeof(float) * 2 * (size_t)(p.small_tail ? NJ : B) * sample_chunks(V));
-    if (p.small_tail) p.o_lse = take(sizeof(float) * 3 * (size_t)NJ);  // normalisers + flags
+    p.o_sums = take(sizeof(float) * 2 * (size_t)B * sample_chunks(V));  // per request: chunk sums
+    if (p.small_tail) p.o_lse = take(sizeof(float) * 3 * (size_t)B);  // per request: A, normalisers
     // sampled tree verification over several blocks per request: chunk sums and slice totals
     if (mode == SV_MODE_SAMPLE)
       p.o_tree = take(sizeof(float) * ((size_t)B * tree_chunks(V) + (size_t)B * 2 * TREE_MAX_BLOCKS));

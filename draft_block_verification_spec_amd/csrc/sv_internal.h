@@ -138,11 +138,10 @@ hipError_t launch_accept_sample(const AcceptArgs &a, hipStream_t st);
 hipError_t launch_accept_greedy(const AcceptArgs &a, hipStream_t st);
 
 int sample_chunks(int V);
-// Small batches: the draw for every candidate first-rejection position is prepared at
-// once, then the acceptance scan keeps the one at the first rejection.
-// sums [B*(K+1)*C*2], lse_buf [3*B*(K+1)] (two normalisers per candidate, then an int
-// acceptance flag per candidate).
-hipError_t launch_tail_small(const AcceptArgs &a, float *sums, float *lse_buf, const FinalizeArgs &fin,
+// Small batches (B*(K+1) <= 32): acceptance decided in every chunk block, then the
+// weights and the draw of the accepted candidate only.  sums [B*C*2] (chunk sums of
+// max(0, p-q) and p), req [3*B] (first rejection A as int bits, then the two normalisers).
+hipError_t launch_tail_small(const AcceptArgs &a, float *sums, float *req, const FinalizeArgs &fin,
                              hipStream_t st);
 hipError_t launch_sample(const SampleJob *jobs, int njobs, int V, float invT, float *chunk_sums,
                          int32_t *out, int32_t *job_cnt, int32_t *done_cnt, const FinalizeArgs &fin,

@@ -791,7 +791,7 @@ __global__ __launch_bounds__(T2_NT2) void k_tail_b(const AcceptArgs a, int chunk
 // ---- inverse-CDF sampling of one token per job (larger batches, drafter step), two
 // kernels with no inter-block signalling: sample_sums sums the weights of every job over
 // SUBS chunks per block; sample_pick (one block per job) finds the chunk from those sums
-// and the token inside it, as tail2 does; its block 0 also writes the call-wide
+// and the token inside it (pick_token); its block 0 also writes the call-wide
 // bookkeeping (the accepted lengths are final before the draw).  The weight of token v
 // is max(0, p_v - q_v) (p_v if the job has no second row or all of those are zero),
 // recomputed from the fp32 logits in ascending token order.
@@ -1585,20 +1585,20 @@ hipError_t launch_sample(const SampleJob *jobs, int njobs, int V, float invT, fl
   return hipGetLastError();
 }
 
-hipError_t launch_tail_small(const AcceptArgs &a, float *sums, float *lse_buf, const FinalizeArgs &fin,
+hipError_t launch_tail_small(const AcceptArgs &a, float *sums, float *req, const FinalizeArgs &fin,
                              hipStream_t st) {
   const int C = sample_chunks(a.V);
   // chunks of a multiple of 64 tokens (at most NT * PER = 2048): 16-byte aligned when V % 4 == 0
   const int chunk = (((a.V + C - 1) / C) + 63) / 64 * 64;
   const dim3 grid((C + 1) / 2, a.B);
   if (a.V % 4 == 0) {
-    hipLaunchKernelGGL(k_tail_a<true>, grid, dim3(TA_NT), 0, st, a, chunk, C, sums, lse_buf);
+    hipLaunchKernelGGL(k_tail_a<true>, grid, dim3(TA_NT), 0, st, a, chunk, C, sums, req);
     hipLaunchKernelGGL(k_tail_b<true>, dim3(a.B), dim3(T2_NT2), 0, st, a, chunk, C, (const float *)sums,
-                       (const float *)lse_buf, fin);
+                       (const float *)req, fin);
   } else {
-    hipLaunchKernelGGL(k_tail_a<false>, grid, dim3(TA_NT), 0, st, a, chunk, C, sums, lse_buf);
+    hipLaunchKernelGGL(k_tail_a<false>, grid, dim3(TA_NT), 0, st, a, chunk, C, sums, req);
     hipLaunchKernelGGL(k_tail_b<false>, dim3(a.B), dim3(T2_NT2), 0, st, a, chunk, C, (const float *)sums,
-                       (const float *)lse_buf, fin);
+                       (const float *)req, fin);
   }
   return hipGetLastError();
 }
