@@ -543,10 +543,11 @@ __device__ int pick_token(const float *z1, const float *z2, float lse1, float ls
 
 // Merge two rows' statistic partials with one wave, the loads of both rows issued
 // together (BATCH per lane and row at a time); p1 may be null.  Same order of merges as
-// wave_merge_row, so the same results.
-template <int BATCH>
+// wave_merge_row, so the same results.  after_issue() runs once every load of the first
+// batch has been issued (a caller's own loads go there, behind the partials).
+template <int BATCH, typename F>
 __device__ void wave_merge_rows2(const StatPart *p0, const StatPart *p1, int nslots, float invT, StatPart &o0,
-                                 StatPart &o1) {
+                                 StatPart &o1, F after_issue) {
   const int lane = threadIdx.x & 63;
   StatPart s0 = stat_empty(), s1 = stat_empty();
   for (int i0 = 0; i0 < nslots; i0 += 64 * BATCH) {
@@ -557,6 +558,7 @@ __device__ void wave_merge_rows2(const StatPart *p0, const StatPart *p1, int nsl
       q0[k] = i < nslots ? p0[i] : stat_empty();
       q1[k] = (p1 && i < nslots) ? p1[i] : stat_empty();
     }
+    if (i0 == 0) after_issue();
 #pragma unroll
     for (int k = 0; k < BATCH; ++k) {
       s0 = stat_merge(s0, q0[k], invT, true);
@@ -598,17 +600,21 @@ __global__ __launch_bounds__(TA_NT) void k_tail_a(const AcceptArgs a, int chunk,
   const long drow0 = (long)b * Kmax;
   const float invT = a.invT;
   const bool lead = cb == 0;  // the request's first block writes its results
-  // wave 0: the inputs of the first 64 acceptance decisions, ahead of the statistics
+  // wave 0: the inputs of the first 64 acceptance decisions.  The draft ids and coins
+  // are loaded first; the logits at the ids are loaded once the ids are in, after this
+  // wave's statistic partials have been requested (so its merges do not wait for them).
   int x0 = 0;
   float u0 = 0.f, zt0 = 0.f, zd0 = 0.f;
   if (wave == 0 && lane < Kb) {
     x0 = a.draft[drow0 + lane];
     u0 = a.u[(long)b * (Kmax + 1) + lane];
-    if (x0 >= 0 && x0 < a.V) {
+  }
+  auto load_at_drafts = [&]() {
+    if (wave == 0 && lane < Kb && x0 >= 0 && x0 < a.V) {
       zt0 = a.logits_t[(trow0 + lane) * (long)a.V + x0];
       zd0 = a.logits_d[(drow0 + lane) * (long)a.V + x0];
     }
-  }
+  };
   // row statistics: rows r = 0..Kb are target rows, r = Kb+1..2Kb draft rows 0..Kb-1
   const int nrows = 2 * Kb + 1;
   auto rowp = [&](int r) -> const StatPart * {
@@ -630,19 +636,26 @@ __global__ __launch_bounds__(TA_NT) void k_tail_a(const AcceptArgs a, int chunk,
       }
     }
   };
+  bool drafts_loaded = false;
   for (int r0 = wave; r0 < nrows; r0 += 2 * NW) {
     const int r1 = r0 + NW;
     if (a.nslots_t == a.nslots_d || (r0 <= Kb) == (r1 <= Kb)) {
       const int ns = r0 <= Kb ? a.nslots_t : a.nslots_d;
       StatPart s0, s1;
-      wave_merge_rows2<4>(rowp(r0), rowp(r1), ns, invT, s0, s1);
+      wave_merge_rows2<4>(rowp(r0), rowp(r1), ns, invT, s0, s1, [&]() {
+        if (!drafts_loaded) load_at_drafts();
+        drafts_loaded = true;
+      });
       finish_row(r0, s0);
       if (r1 < nrows) finish_row(r1, s1);
     } else {
+      if (!drafts_loaded) load_at_drafts();
+      drafts_loaded = true;
       finish_row(r0, wave_merge_row<8>(rowp(r0), r0 <= Kb ? a.nslots_t : a.nslots_d, invT, true));
       if (r1 < nrows) finish_row(r1, wave_merge_row<8>(rowp(r1), r1 <= Kb ? a.nslots_t : a.nslots_d, invT, true));
     }
   }
+  if (!drafts_loaded) load_at_drafts();  // a wave with no rows (only when Kb is small)
   __syncthreads();
   // acceptance, left to right: lane j of wave 0 handles draft position j+1
   if (wave == 0) {
