@@ -184,8 +184,49 @@ def test_greedy_drafts_from_target_accept_everything():
     assert float(out.tau.item()) == pytest.approx(np.mean(acc + 1))
 
 
+# Shapes of the small-batch tail (B * (K+1) <= 32) beyond the ones above: V a multiple
+# of 4 (16-byte logit loads) at reduced size, no drafts at all (K = 0: the one token is
+# drawn from p), and the scheduled mode with two requests (budget binding).
+TAIL_VEC = wl.Workload("tail_vec", 16, B=2, K=7, d=256, d_ff=512, V=8192, T=1.0, sigma=0.4)
+NO_DRAFTS = wl.Workload("no_drafts", 17, B=4, K=0, d=256, d_ff=512, V=5003, T=1.0, sigma=0.4)
+SCHED_TAIL = wl.Workload("sched_tail", 18, B=2, K=15, d=256, d_ff=512, V=8192, T=1.0, sigma=(0.3, 1.2),
+                         gain=(4.0, 32.0), threshold=0.3, budget=12)
+
+
+def test_sample_parity_small_tail_vec():
+    _run_sample(TAIL_VEC)
+
+
+def test_sample_without_drafts():
+    wk = NO_DRAFTS
+    data = wl.generate(wk)
+    W = oracle.Weights.from_bits(data)
+    coins = data["coins"].astype(np.float64)
+    draft = np.zeros((wk.B, 0), dtype=np.int64)
+    ref = oracle.verify_sample(W, oracle.from_bf16_bits(data["h"]), oracle.from_bf16_bits(data["h_draft"]), draft,
+                               coins, wk.T)
+    w = pt.dev_weights(data)
+    out = bd.spec_verify_sample(w, pt.dev_bf16(data["h"]), pt.dev_bf16(data["h_draft"]), _i32(draft),
+                                _f32(data["coins"]), wk.T, logits=True)
+    torch.cuda.synchronize()
+    assert int(out.dev_status.item()) == bd.SV_DEV_OK
+    lg = out.logits.cpu().numpy().astype(np.float64)
+    assert np.abs(lg - ref["logits_t"].reshape(-1, wk.V)).max() <= pt.LOGIT_TOL
+    acc, em = out.accepted_len.cpu().numpy(), out.emitted.cpu().numpy()
+    assert np.all(acc == 0)
+    pt.assert_decisions(ref, acc, em, lambda b: pt.first_diff_sample(ref, 0, em[b], b, coins, 0), "no drafts")
+    assert float(out.tau.item()) == pytest.approx(1.0)
+
+
 def test_scheduled_parity_small():
-    wk = wl.SMALL_SCHED
+    _run_scheduled(wl.SMALL_SCHED)
+
+
+def test_scheduled_parity_small_tail():
+    _run_scheduled(SCHED_TAIL)
+
+
+def _run_scheduled(wk):
     data = wl.generate(wk)
     W = oracle.Weights.from_bits(data)
     T = wk.T
