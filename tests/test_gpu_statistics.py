@@ -59,6 +59,55 @@ def test_statement1_chi_square_v8_gpu():
     assert float(out.tau.item()) == pytest.approx(tau, rel=1e-6)
 
 
+def test_statement1_chi_square_v8_small_tail():
+    """The same V = 8 check through the small-batch tail (B * (K+1) <= 32): 20,000 calls
+    of 6 requests each (120,000 trials), fresh draft tokens and coins per request.  Every
+    emitted position follows p (chi-square, alpha = 0.01 with a Bonferroni split), and
+    mean(A + 1) matches the closed form within 1% (its standard error here is ~0.3%)."""
+    w = wl.Workload("chi8", 20, B=1, K=4, d=64, d_ff=0, V=8, T=1.0, sigma=0.9)
+    data = wl.generate(w)
+    W = oracle.Weights.from_bits(data)
+    h64, hd64 = oracle.from_bf16_bits(data["h"])[0], oracle.from_bf16_bits(data["h_draft"])[0]
+    p = oracle.softmax_t(oracle.lm_logits(W.w_lm, h64), 1.0)
+    q = oracle.softmax_t(oracle.lm_logits(W.w_lm, hd64), 1.0)
+    K, V, Bc, calls = 4, 8, 6, 20_000
+    N = Bc * calls
+    rng = np.random.default_rng(2027)
+    cdf = np.cumsum(q, axis=1)
+    draft = np.stack([np.minimum(np.searchsorted(cdf[j], rng.random(N), side="right"), V - 1) for j in range(K)], axis=1)
+    coins = (rng.integers(0, 1 << 24, size=(N, K + 1)) * 2.0 ** -24).astype(np.float32)
+    dev = torch.device("cuda")
+    wd = pt.dev_weights(data)
+    h = pt.dev_bf16(data["h"]).expand(Bc, K + 1, 64).contiguous()
+    hd = pt.dev_bf16(data["h_draft"]).expand(Bc, K, 64).contiguous()
+    draft_d = torch.from_numpy(draft.astype(np.int32)).to(dev)
+    coins_d = torch.from_numpy(coins).to(dev)
+    out = bd.make_outputs(Bc, K, dev, mode=bd.SV_MODE_SAMPLE, V=V, d=64)
+    ws = bd.workspace(bd.SV_MODE_SAMPLE, Bc, K, wd, dev)
+    A_d = torch.empty(N, dtype=torch.int32, device=dev)
+    em_d = torch.empty(N, K + 1, dtype=torch.int32, device=dev)
+    for i in range(calls):
+        sl = slice(i * Bc, (i + 1) * Bc)
+        bd.spec_verify_sample(wd, h, hd, draft_d[sl], coins_d[sl], 1.0, out=out, ws=ws)
+        A_d[sl].copy_(out.accepted_len)
+        em_d[sl].copy_(out.emitted)
+    torch.cuda.synchronize()
+    assert int(out.dev_status.item()) == 0
+    A, em = A_d.cpu().numpy(), em_d.cpu().numpy()
+    crit1 = scipy.stats.chi2.ppf(0.99, V - 1)
+    crit_b = scipy.stats.chi2.ppf(1 - 0.01 / (K + 1), V - 1)
+    stats = []
+    for j in range(K + 1):
+        sel = A >= j
+        hist = np.bincount(em[sel, j], minlength=V)
+        n = hist.sum()
+        stats.append(float(((hist - n * p[j]) ** 2 / (n * p[j])).sum()))
+    assert stats[0] < crit1, stats
+    assert max(stats) < crit_b, stats
+    alphas = [oracle.acceptance_rate(p[j], q[j]) for j in range(K)]
+    assert float(np.mean(A + 1)) == pytest.approx(oracle.tau_closed_form(alphas), rel=0.01)
+
+
 def test_tiny_config_tau_gpu():
     """Tiny configuration (B=1, K=4, d=64, V=512, T=1), run as 10^5 independent verify steps
     (fresh h, noise, drafts and coins; one weight draw) in one call: the mean of A + 1
