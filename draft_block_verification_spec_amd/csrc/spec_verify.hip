@@ -42,8 +42,8 @@ struct Gemm {
   int splits = 1;
   int nslots = 0;  // statistics slots per row (EPI_LOGITS)
   size_t partial_floats = 0;
-  // EPI_LOGITS: columns [0, n_split) in whole rounds of `shape` tiles over the CUs, the
-  // rest in a second launch of `shape2` tiles (0: one launch)
+  // EPI_LOGITS / EPI_SWIGLU: output columns [0, n_split) in whole rounds of `shape` tiles
+  // over the CUs, the rest in a second launch of `shape2` tiles (0: one launch)
   int n_split = 0;
   TileShape shape2{256, 128, 64, 3};
 };
@@ -72,6 +72,29 @@ Gemm choose(int M, int N, int K, int epi) {
     g.splits = want < maxs ? want : maxs;
   }
   if (g.splits > 1) g.partial_floats = (size_t)g.splits * M * Ncols;
+  if (epi == EPI_SWIGLU && M > 192) {
+    // Whole rounds of 256 x 256 tiles, then the remaining output columns as one launch of
+    // 256 x 128 tiles, when that costs less than either shape alone (a 256 x 256 tile
+    // takes ~1.7-1.9x a 256 x 128 one): 1024 rows at d_ff = 12288 run 1 + 1 rounds
+    // (126 + 70 us) instead of 3 rounds of 256 x 128 tiles (204 us).
+    const long tm = (M + 255) / 256, cus = num_cus();
+    const long tiles256 = tm * ((2L * N + 255) / 256);
+    const long full = tiles256 / cus;
+    if (full >= 1 && tiles256 % cus > 0 && cus % tm == 0) {
+      const long n1 = full * (cus / tm) * 128;  // output columns of the whole rounds
+      if (n1 < N) {
+        const long r2 = (tm * ((2L * (N - n1) + 127) / 128) + cus - 1) / cus;
+        const long r128 = (tm * ((2L * N + 127) / 128) + cus - 1) / cus;
+        const long r256 = (tiles256 + cus - 1) / cus;
+        const long best = 10 * r128 < 17 * r256 ? 10 * r128 : 17 * r256;
+        if (17 * full + 10 * r2 < best) {
+          g.shape = TileShape{256, 256, 64, 2};
+          g.shape2 = TileShape{256, 128, 64, 3};
+          g.n_split = (int)n1;
+        }
+      }
+    }
+  }
   if (epi == EPI_LOGITS) {
     g.nslots = tiled_slots(N, g.shape.bn);
     // A last round of 256 x 256 tiles at most half full would cost a whole round: its
@@ -223,7 +246,7 @@ thread_local const char *g_last_hip_error = "no error";
 
 hipError_t run_gemm(const Gemm &g, GemmArgs a, int epi, hipStream_t st) {
   if (g.stream) return launch_gemm_stream(a, epi, g.grid, st);
-  if (g.n_split > 0) {  // EPI_LOGITS in two launches over disjoint column ranges
+  if (g.n_split > 0) {  // two launches over disjoint ranges of output columns
     GemmArgs a1 = a;
     a1.N = g.n_split;
     hipError_t e = launch_gemm_tiled(a1, epi, g.shape, 1, st);
@@ -231,9 +254,14 @@ hipError_t run_gemm(const Gemm &g, GemmArgs a, int epi, hipStream_t st) {
     GemmArgs a2 = a;
     a2.N = a.N - g.n_split;
     a2.w = a.w + (size_t)g.n_split * a.K;
-    if (a.logits) a2.logits = a.logits + g.n_split;
-    a2.parts = a.parts + tiled_slots(g.n_split, g.shape.bn);
-    a2.n_off = a.n_off + g.n_split;
+    if (epi == EPI_SWIGLU) {
+      a2.w2 = a.w2 + (size_t)g.n_split * a.K;
+      a2.out = a.out + g.n_split;
+    } else {
+      if (a.logits) a2.logits = a.logits + g.n_split;
+      a2.parts = a.parts + tiled_slots(g.n_split, g.shape.bn);
+      a2.n_off = a.n_off + g.n_split;
+    }
     a2.status_reset = nullptr;
     a2.counter_reset = nullptr;
     return launch_gemm_tiled(a2, epi, g.shape2, 1, st);

@@ -138,9 +138,10 @@ def _run_greedy(wk, rep=0, fp8=False):
 #  * 128 requests x 8 rows = 1024 rows, V = 24000: 94 column tiles of 256 x 4 row tiles =
 #    376 tiles = one round of 256 + 120, so columns [0, 16384) run as 256 x 256 tiles and
 #    the ragged rest (7616 columns, 240 tiles of 256 x 128) as a second launch whose
-#    argmax indices and statistic slots are offset.
+#    argmax indices and statistic slots are offset; with d_ff = 12288 gate/up splits the
+#    same way (outputs [0, 8192) on 256 x 256 tiles, the rest on 256 x 128).
 MLP160 = wl.Workload("mlp160", 14, B=20, K=7, d=256, d_ff=1536, V=5003, T=1.0, sigma=(0.3, 1.2))
-LM_SPLIT = wl.Workload("lm_split", 15, B=128, K=7, d=256, d_ff=512, V=24000, T=1.0, sigma=(0.3, 1.2))
+LM_SPLIT = wl.Workload("lm_split", 15, B=128, K=7, d=256, d_ff=12288, V=24000, T=1.0, sigma=(0.3, 1.2))
 
 
 def test_sample_parity_160_rows():
