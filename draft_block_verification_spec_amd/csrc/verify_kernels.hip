@@ -16,7 +16,7 @@ namespace sv {
 namespace {
 
 constexpr int NT = 256;  // threads per block for the small kernels
-constexpr int PER = 8;   // tokens per thread in the final scan of a sampling chunk (chunk <= NT * PER)
+constexpr int PER = 8;   // tokens per thread and chunk in the chunk-sum kernel (a chunk is at most NT * PER = 2048)
 
 __device__ void set_status(int32_t *st, int code) {
   if (st) atomicCAS(st, 0, code);
