@@ -33,7 +33,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps before each timed loop; the GPU clock needs ~0.1 s of work to settle")
     ap.add_argument("--config", default="block16", choices=["block16", "sweep", "sched", "sched_stress", "wide"])
     ap.add_argument("--batch", type=int, default=0, help="override B (sweep)")
     ap.add_argument("--no-extra", action="store_true")
