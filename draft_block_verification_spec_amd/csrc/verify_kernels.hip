@@ -576,8 +576,9 @@ __device__ void wave_merge_rows2(const StatPart *p0, const StatPart *p1, int nsl
 
 // ---- small-batch tail (B * (K+1) <= 32), two kernels, no inter-block signalling.
 // tail_a, blocks (pair of sampling chunks, request): every block merges its request's row
-// statistics (one wave per pair of rows; the draft ids, coins and logits at the drafts
-// are loaded first), decides acceptance left to right (Statement 1: u < p(x)/q(x)), and
+// statistics (one wave per pair of rows; the draft ids and coins are loaded first, the
+// logits at the draft ids right behind the statistic partials), decides acceptance left
+// to right (Wildberries page, "A bit of theory", Statement 1: u < p(x)/q(x)), and
 // sums the sampling weights of the draw at the first rejection A over its two chunks:
 // max(0, p - q) and p from target row A and draft row A (p alone for the bonus row
 // A = K_b).  So only the accepted candidate's two rows are read.  The request's first
