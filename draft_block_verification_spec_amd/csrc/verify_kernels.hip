@@ -267,16 +267,32 @@ __global__ __launch_bounds__(1024) void k_accept_greedy(const AcceptArgs a) {
   const int nw = blockDim.x >> 6;
   // draft tokens of the first 64 positions, loaded ahead of the statistics
   const int x0 = (wave == 0 && lane < K) ? a.draft[(long)b * K + lane] : -1;
-  for (int j = wave; j <= K; j += nw) {
-    const StatPart st = wave_merge_row<12>(a.parts_t + (trow0 + j) * a.nslots_t, a.nslots_t, 1.f, a.diag != nullptr);
-    if (lane == 0) {
-      amax[j] = st.i1;
-      if (!isfinite(st.b1)) bad = SV_DEV_NONFINITE;
-      if (a.diag) {
-        float *dg = a.diag + (trow0 + j) * SV_DIAG_COLS;
-        dg[0] = st.b1 + __logf(st.s); dg[1] = (float)st.i1; dg[2] = st.b1 - st.b2; dg[3] = st.b1;
-        dg[4] = NAN; dg[5] = NAN; dg[6] = NAN; dg[7] = 0.f;
-      }
+  auto finish_row = [&](int j, const StatPart &st) {
+    amax[j] = st.i1;
+    if (!isfinite(st.b1)) bad = SV_DEV_NONFINITE;
+    if (a.diag) {
+      float *dg = a.diag + (trow0 + j) * SV_DIAG_COLS;
+      dg[0] = st.b1 + __logf(st.s); dg[1] = (float)st.i1; dg[2] = st.b1 - st.b2; dg[3] = st.b1;
+      dg[4] = NAN; dg[5] = NAN; dg[6] = NAN; dg[7] = 0.f;
+    }
+  };
+  if (2 * (K + 1) <= nw) {
+    // two waves per row, each merging half of its partials (one round of loads for ~1200
+    // partials), the halves combined in a fixed order
+    __shared__ StatPart halves[2][8];
+    const int j = wave % (K + 1), h = wave / (K + 1);
+    if (h < 2) {
+      const int half = (a.nslots_t + 1) / 2;
+      const int s0 = h * half, n = min(a.nslots_t, s0 + half) - s0;
+      const StatPart st = wave_merge_row<12>(a.parts_t + (trow0 + j) * a.nslots_t + s0, n, 1.f, a.diag != nullptr);
+      if (lane == 0) halves[h][j] = st;
+    }
+    __syncthreads();
+    if (wave <= K && lane == 0) finish_row(wave, stat_merge(halves[0][wave], halves[1][wave], 1.f, a.diag != nullptr));
+  } else {
+    for (int j = wave; j <= K; j += nw) {
+      const StatPart st = wave_merge_row<12>(a.parts_t + (trow0 + j) * a.nslots_t, a.nslots_t, 1.f, a.diag != nullptr);
+      if (lane == 0) finish_row(j, st);
     }
   }
   __syncthreads();
@@ -1566,7 +1582,7 @@ hipError_t launch_accept_sample(const AcceptArgs &a, hipStream_t st) {
 
 hipError_t launch_accept_greedy(const AcceptArgs &a, hipStream_t st) {
   const size_t shm = sizeof(int) * (a.K + 2);
-  const int nw = min(16, max(1, a.K + 1));
+  const int nw = min(16, max(1, 2 * (a.K + 1)));  // two waves per row when K + 1 <= 8
   hipLaunchKernelGGL(k_accept_greedy, dim3(a.B), dim3(64 * nw), shm, st, a);
   return hipGetLastError();
 }
