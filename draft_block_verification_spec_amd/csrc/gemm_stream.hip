@@ -23,6 +23,7 @@
 //  * the 8 partial accumulators of a tile are summed in a fixed order through LDS
 //    (deterministic), then the epilogue runs: fp32 logits + running per-row
 //    statistics, SwiGLU with paired gate/up rows, or residual add, bf16 output.
+#include <atomic>
 #include <type_traits>
 
 #include "sv_device.h"
@@ -427,12 +428,17 @@ hipError_t launch_one(GemmArgs a, int grid, hipStream_t st) {
   a.buf_cols = 0;
   if (shm <= dyn_max && (EPI != EPI_LOGITS || a.logits)) {
     a.buf_cols = cols;
-    static bool attr_set = false;  // one instantiation per (MB, EPI, KM, F8)
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_stream<MB, EPI, KM, F8>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_max);
+    // the attribute belongs to the current device: set once per device and instantiation
+    static std::atomic<unsigned long long> attr_set{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const unsigned long long bit = 1ull << (dev & 63);
+    if (!(attr_set.load(std::memory_order_acquire) & bit)) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_stream<MB, EPI, KM, F8>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_max);
       if (e != hipSuccess) return e;
-      attr_set = true;
+      attr_set.fetch_or(bit, std::memory_order_release);
     }
   } else {
     shm = 0;
