@@ -363,7 +363,6 @@ __device__ __forceinline__ float wave_incl_scan(float v) {
 template <int NI>
 __device__ int wave_find(const float (&w)[NI], int n, int item0, float base, float incl, float lane_tot,
                          float target, float *run_before) {
-  const int lane = threadIdx.x & 63;
   float run = base + incl - lane_tot;
   int hit = -1, last = -1;
   float hit_run = 0.f, last_run = 0.f;
