@@ -53,14 +53,17 @@ __device__ __forceinline__ void vm_wait() {
 }
 __device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// The 192-row shape holds one workgroup per CU by its LDS alone; one wave per SIMD
-// gives its accumulators the whole register file.
-template <int BM, int BN>
-constexpr int waves_per_eu() { return (BM * BN >= 256 * 256 || BM == 192) ? 1 : 2; }
+// Waves per SIMD the kernel is compiled for: one where the slice pipeline's LDS already
+// holds the CU to one workgroup (the 192-row shape among them), and for 256 x 256 tiles,
+// whose accumulators need the whole register file; two otherwise.
+template <int BM, int BN, int BK, int NS>
+constexpr int waves_per_eu() {
+  return (BM * BN >= 256 * 256 || BM == 192 || (160 * 1024) / (NS * (BM + BN) * BK * 2) < 2) ? 1 : 2;
+}
 
 // PAIR: the weight rows of a tile are [32 gate | 32 up] groups of the same outputs.
 template <int BM, int BN, int BK, int NS, int EPI, bool PAIR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_eu<BM, BN>(), waves_per_eu<BM, BN>())))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_eu<BM, BN, BK, NS>(), waves_per_eu<BM, BN, BK, NS>())))
 void k_tiled(const GemmArgs a) {
   constexpr int RB = Slice<BK>::RB, CPR = Slice<BK>::CPR, RPI = Slice<BK>::RPI;
   constexpr int SA = BM * RB, SB = BN * RB, SS = SA + SB;  // bytes of one slice
@@ -386,7 +389,7 @@ template <int BM, int BN, int BK, int NS>
 constexpr int per_cu() {
   constexpr int lds = NS * (BM + BN) * BK * 2;
   constexpr int by_lds = (160 * 1024) / lds;
-  return by_lds < waves_per_eu<BM, BN>() ? by_lds : waves_per_eu<BM, BN>();
+  return by_lds < waves_per_eu<BM, BN, BK, NS>() ? by_lds : waves_per_eu<BM, BN, BK, NS>();
 }
 
 template <int BM, int BN, int BK, int NS>
