@@ -442,10 +442,11 @@ TileShape tiled_shape(int M, int N, int K, int epi) {
     if (M > 128 && M <= 192) return TileShape{192, 128, 64, 3};  // 160 rows: 121 us against 149 us
     return M <= 256 ? TileShape{128, 256, 64, 3} : TileShape{256, 128, 64, 3};
   }
-  // (a single 320 x 128 row tile at 288 rows measured 9% slower than three 128 x 256 ones)
+  // (a single 320 x 128 row tile at 288 rows measured 9% slower than three 128 x 256 ones;
+  // at 256 rows two 128 x 256 row tiles beat one 256 x 128 row tile by 4% of the step)
   if (M <= 64) return k128 ? TileShape{64, 128, 128, 3} : TileShape{64, 128, 64, 2};
   if (M <= 128) return TileShape{128, 128, 64, 4};
-  if (M <= 256) return TileShape{256, 128, 64, 3};
+  if (M <= 192) return TileShape{256, 128, 64, 3};
   if (M <= 384) return TileShape{128, 256, 64, 3};
   return TileShape{256, 256, 64, 2};
 }
