@@ -429,6 +429,8 @@ TileShape tiled_shape(int M, int N, int K, int epi) {
     // one row tile, at most a third empty (160 rows at d = 8192: 219 us against 239 us
     // for 256 x 256 tiles)
     if (M <= 192) return TileShape{192, 128, 64, 3};
+    // two 128-row tiles at 193-256 rows (256 rows: 0.7% of the step faster than 256 x 128)
+    if (M <= 256) return TileShape{128, 256, 64, 3};
     // 256-row tiles, one workgroup per CU either way: 256 x 256 when it needs enough fewer
     // rounds over the CUs than 256 x 128 (a 256 x 256 tile takes ~1.7x as long as a
     // 256 x 128 one), e.g. 512 rows: 192 tiles in one round against 384 tiles in two
