@@ -85,7 +85,11 @@ void k_tiled(const GemmArgs a) {
   int M = a.M;
   if (a.M_dev) M = min(M, *a.M_dev);
   const int Ncols = PAIR ? 2 * a.N : a.N;  // columns of the weight-row space
-  const int tiles_m = (a.M + BM - 1) / BM;
+  // Only row tiles that hold rows are walked: with a device-side row count below a.M the
+  // live tiles still spread over every workgroup (skipping the dead ones in place would
+  // leave all live tiles to the workgroups whose slot meets them, half the grid at two
+  // row tiles).
+  const int tiles_m = M > 0 ? (M + BM - 1) / BM : 0;
   const int total = tiles_m * ((Ncols + BN - 1) / BN);
   const int splits = gridDim.z, z = blockIdx.z;
   const int nkt_total = a.K / BK;

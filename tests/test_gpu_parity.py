@@ -227,6 +227,15 @@ def test_scheduled_parity_small_tail():
     _run_scheduled(SCHED_TAIL)
 
 
+# A binding budget above 128 rows: the verify GEMMs span two row tiles of 128.
+SCHED_200 = wl.Workload("sched_200", 19, B=24, K=15, d=256, d_ff=512, V=3001, T=1.0, sigma=(0.3, 1.2),
+                        gain=(4.0, 32.0), threshold=0.3, budget=200)
+
+
+def test_scheduled_parity_two_row_tiles():
+    _run_scheduled(SCHED_200)
+
+
 def _run_scheduled(wk):
     data = wl.generate(wk)
     W = oracle.Weights.from_bits(data)
