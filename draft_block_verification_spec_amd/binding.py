@@ -18,12 +18,14 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libspecverify.so")
 
-SV_OK, SV_EINVAL, SV_EWORKSPACE, SV_EHIP = 0, -1, -2, -3
+SV_OK, SV_EINVAL, SV_EWORKSPACE, SV_EHIP, SV_ESCRATCH = 0, -1, -2, -3, -4
+SV_STATIC_SCRATCH_BYTES = 32 << 20
 SV_DEV_OK, SV_DEV_BAD_TOKEN, SV_DEV_NONFINITE, SV_DEV_BAD_COMMIT, SV_DEV_BAD_TREE, SV_DEV_TIMEOUT = 0, 1, 2, 3, 4, 5
 SV_MODE_GREEDY, SV_MODE_SAMPLE, SV_MODE_SCHEDULED, SV_MODE_PROPOSE = 0, 1, 2, 3
 SV_DIAG_COLS = 8
 
-EXPORTS = ("sv_workspace_bytes", "spec_verify_greedy", "spec_verify_sample", "spec_verify_scheduled",
+EXPORTS = ("sv_workspace_bytes", "spec_verify_greedy", "spec_verify_sample", "spec_verify_sample_noalloc",
+           "spec_verify_scheduled",
            "spec_draft_propose", "spec_verify_tree", "spec_commit", "sv_version", "sv_strerror",
            "sv_last_hip_error")
 
@@ -78,6 +80,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.spec_verify_sample.restype = i32
     lib.spec_verify_sample.argtypes = [ctypes.POINTER(SvWeights), vp, vp, vp, vp, f32, i32, i32, vp, sz,
                                        ctypes.POINTER(SvOutputs), vp]
+    lib.spec_verify_sample_noalloc.restype = i32
+    lib.spec_verify_sample_noalloc.argtypes = [ctypes.POINTER(SvWeights), vp, vp, vp, vp, f32, i32, i32,
+                                               ctypes.POINTER(SvOutputs), vp]
     lib.spec_verify_scheduled.restype = i32
     lib.spec_verify_scheduled.argtypes = [ctypes.POINTER(SvWeights), vp, vp, vp, vp, f32, f32, i32, i32, i32, vp,
                                           sz, ctypes.POINTER(SvOutputs), vp]
@@ -254,6 +259,25 @@ def spec_verify_sample(w: Weights, h, h_draft, draft, u, T: float, *, out: Outpu
     rc = load().spec_verify_sample(ctypes.byref(w.c), _ptr(h), _ptr(h_draft), _ptr(draft), _ptr(u), float(T), B, K,
                                    _ptr(ws), ws.numel(), ctypes.byref(oc), _stream(stream))
     _raise(rc, "spec_verify_sample")
+    return out
+
+
+def spec_verify_sample_noalloc(w: Weights, h, h_draft, draft, u, T: float, *, out: Outputs | None = None,
+                               stream=None, diag=False, logits=False, hidden=False) -> Outputs:
+    """spec_verify_sample with the library's static per-GPU scratch as the workspace (no
+    workspace argument); raises on sizes beyond SV_STATIC_SCRATCH_BYTES."""
+    _check_dev(h, torch.bfloat16, "h")
+    _check_dev(h_draft, torch.bfloat16, "h_draft")
+    _check_dev(draft, torch.int32, "draft")
+    _check_dev(u, torch.float32, "u")
+    B, K1, _ = h.shape
+    K = K1 - 1
+    out = out or make_outputs(B, K, h.device, mode=SV_MODE_SAMPLE, V=w.V, d=w.d, diag=diag, logits=logits,
+                              hidden=hidden)
+    oc = out.c()
+    rc = load().spec_verify_sample_noalloc(ctypes.byref(w.c), _ptr(h), _ptr(h_draft), _ptr(draft), _ptr(u),
+                                           float(T), B, K, ctypes.byref(oc), _stream(stream))
+    _raise(rc, "spec_verify_sample_noalloc")
     return out
 
 

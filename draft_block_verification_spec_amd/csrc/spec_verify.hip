@@ -436,6 +436,49 @@ SV_API int spec_verify_sample(const sv_weights *w, const uint16_t *h, const uint
   return SV_OK;
 }
 
+// ---- the sampled verification without any allocation: the workspace is the file-scope
+// device array below (one copy per GPU, kept until the process ends)
+namespace sv {
+namespace {
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)SV_STATIC_SCRATCH_BYTES;
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES];  // device address of `scratch` on each device, once looked up
+}  // namespace
+}  // namespace sv
+
+static __device__ __align__(256) uint8_t scratch[sv::STATIC_SCRATCH_BYTES];
+
+SV_API int spec_verify_sample_noalloc(const sv_weights *w, const uint16_t *h, const uint16_t *h_draft,
+                                      const int32_t *draft, const float *u, float T, int B, int K, sv_outputs *out,
+                                      void *stream) {
+  // every argument is checked before the first device call
+  int rc = check_common(w, h, draft, B, K, nullptr, out);
+  if (rc) return rc;
+  if (!u || !(T > 0.f) || !isfinite(T)) return SV_EINVAL;
+  if (K > 0 && (!h_draft || !aligned16(h_draft))) return SV_EINVAL;
+  Plan p;
+  if (!make_plan(SV_MODE_SAMPLE, B, K, w, 0, p)) return SV_EINVAL;
+  if (p.total > STATIC_SCRATCH_BYTES) return SV_ESCRATCH;
+  int dev = 0;
+  SV_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= MAX_DEVICES) return SV_EINVAL;
+  void *ptr;
+  {
+    // The array's name is a host-side stand-in: its device address is looked up once per
+    // device, with that device current, and only that address is handed to the kernels.
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void *q = nullptr;
+      SV_CHECK(hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)));
+      if (!q) return SV_EHIP;
+      g_scratch_ptr[dev] = q;
+    }
+    ptr = g_scratch_ptr[dev];
+  }
+  return spec_verify_sample(w, h, h_draft, draft, u, T, B, K, ptr, STATIC_SCRATCH_BYTES, out, stream);
+}
+
 SV_API int spec_verify_scheduled(const sv_weights *w, const uint16_t *h, const uint16_t *h_draft,
                                  const int32_t *draft, const float *u, float T, float survival_threshold,
                                  int budget_rows, int B, int Kmax, void *ws, size_t ws_bytes, sv_outputs *out,
@@ -657,6 +700,7 @@ SV_API const char *sv_strerror(int code) {
     case SV_EINVAL: return "invalid argument";
     case SV_EWORKSPACE: return "workspace too small";
     case SV_EHIP: return "HIP runtime error";
+    case SV_ESCRATCH: return "sizes need more workspace than the library's static scratch holds";
     default: return "unknown error";
   }
 }

@@ -64,6 +64,7 @@ extern "C" {
 #define SV_EINVAL (-1)      /* bad sizes, NULL required pointer, misalignment, T <= 0, budget < B */
 #define SV_EWORKSPACE (-2)  /* ws_bytes smaller than sv_workspace_bytes() */
 #define SV_EHIP (-3)        /* a HIP launch or runtime call failed */
+#define SV_ESCRATCH (-4)    /* spec_verify_sample_noalloc: the sizes need more than SV_STATIC_SCRATCH_BYTES */
 
 #define SV_DEV_OK 0
 #define SV_DEV_BAD_TOKEN 1  /* a draft id outside [0, V) */
@@ -146,6 +147,24 @@ int spec_verify_greedy(const sv_weights *w, const uint16_t *h, const int32_t *dr
 int spec_verify_sample(const sv_weights *w, const uint16_t *h, const uint16_t *h_draft,
                        const int32_t *draft, const float *u, float T, int B, int K, void *ws,
                        size_t ws_bytes, sv_outputs *out, void *stream);
+
+/* Bytes of device scratch held by the library on each GPU it runs on (until the process ends). */
+#define SV_STATIC_SCRATCH_BYTES (32u << 20)
+
+/* spec_verify_sample for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same computation and
+ * the same kernels, with the workspace taken from a static device array of
+ * SV_STATIC_SCRATCH_BYTES bytes per GPU instead of the caller's `ws`.  The caller still
+ * passes inputs and outputs.  Calls whose sizes need more workspace than that
+ * (sv_workspace_bytes(SV_MODE_SAMPLE, B, K, w) > SV_STATIC_SCRATCH_BYTES) return
+ * SV_ESCRATCH and enqueue nothing; e.g. one 16-token block (B = 1, K = 15, d = 4096,
+ * V = 151936) needs about 18.6 MiB.  No HIP allocation or free is made; the first call on
+ * a device looks up the array's address there.  All calls on one GPU share its array, so
+ * calls that overlap on one GPU (different streams or threads without ordering) race:
+ * order them on one stream.  The array's contents on entry do not matter. */
+int spec_verify_sample_noalloc(const sv_weights *w, const uint16_t *h, const uint16_t *h_draft,
+                               const int32_t *draft, const float *u, float T, int B, int K, sv_outputs *out,
+                               void *stream);
 
 /* Confidence-scheduled verification at temperature T > 0.  Shapes as in
  * spec_verify_sample with K = Kmax.  The LM head first scores all B*Kmax draft rows;

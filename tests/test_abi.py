@@ -193,3 +193,19 @@ def test_commit_rejects_bad_sizes(lib, B, Kmax, acc):
     c = _cache()
     assert lib.spec_commit(ctypes.byref(c), acc, None, None, B, Kmax, None, None) == b.SV_EINVAL
     assert lib.spec_commit(None, 6 << 20, None, None, 8, 15, None, None) == b.SV_EINVAL
+
+
+def test_noalloc_entry_rejects_before_touching_the_device(lib):
+    """The allocation-free sampled call refuses sizes beyond its static scratch (and bad
+    arguments) before any device call, so this runs without a GPU."""
+    w, o = _w(), _outs()
+    P = 1 << 28
+    assert lib.sv_strerror(b.SV_ESCRATCH).startswith(b"sizes need more workspace")
+    need = lib.sv_workspace_bytes(b.SV_MODE_SAMPLE, 1, 15, ctypes.byref(w))
+    assert 0 < need <= b.SV_STATIC_SCRATCH_BYTES  # one 16-token block fits
+    big = lib.sv_workspace_bytes(b.SV_MODE_SAMPLE, 8, 7, ctypes.byref(w))
+    assert big > b.SV_STATIC_SCRATCH_BYTES
+    assert lib.spec_verify_sample_noalloc(ctypes.byref(w), P, P, P, P, 1.0, 8, 7, ctypes.byref(o), None) == b.SV_ESCRATCH
+    assert lib.spec_verify_sample_noalloc(ctypes.byref(w), P, P, P, P, 0.0, 1, 15, ctypes.byref(o), None) == b.SV_EINVAL
+    assert lib.spec_verify_sample_noalloc(ctypes.byref(w), None, P, P, P, 1.0, 1, 15, ctypes.byref(o),
+                                          None) == b.SV_EINVAL
