@@ -90,7 +90,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.spec_draft_propose.argtypes = [ctypes.POINTER(SvWeights), vp, vp, f32, i32, vp, sz, vp, vp, vp]
     lib.spec_verify_tree.restype = i32
     lib.spec_verify_tree.argtypes = [ctypes.POINTER(SvWeights), vp, vp, vp, vp, vp, f32, i32, i32, vp, sz,
-                                     ctypes.POINTER(SvOutputs), vp, vp]
+                                     ctypes.POINTER(SvOutputs), vp, i32, vp]
     lib.spec_commit.restype = i32
     lib.spec_commit.argtypes = [ctypes.POINTER(SvCache), vp, vp, vp, i32, i32, vp, vp]
     lib.sv_version.restype = ctypes.c_char_p
@@ -319,10 +319,11 @@ def spec_draft_propose(w: Weights, h_draft, coins, T: float, *, draft_out=None, 
 
 
 def spec_verify_tree(w: Weights, h, h_draft, tokens, parent, u, T: float, *, out: Outputs | None = None, ws=None,
-                     stream=None, diag=False, logits=False, hidden=False) -> Outputs:
+                     stream=None, diag=False, logits=False, hidden=False, wait_polls: int = -1) -> Outputs:
     """Tree verification of B trees of K+1 nodes: h [B, K+1, d]; h_draft [B, K, d] (T > 0);
     tokens / parent [B, K] (node j+1); u [B, K+1] (T > 0).  T == 0 is greedy.  The output
-    carries ``path`` [B, K+1] (node at each depth, -1 beyond the accepted depth)."""
+    carries ``path`` [B, K+1] (node at each depth, -1 beyond the accepted depth).  ``wait_polls``
+    bounds a workgroup's wait for the others of its request per meeting (< 0: the default)."""
     greedy = float(T) == 0.0
     _check_dev(h, torch.bfloat16, "h")
     _check_dev(tokens, torch.int32, "tokens")
@@ -340,7 +341,7 @@ def spec_verify_tree(w: Weights, h, h_draft, tokens, parent, u, T: float, *, out
     oc = out.c()
     rc = load().spec_verify_tree(ctypes.byref(w.c), _ptr(h), None if greedy else _ptr(h_draft), _ptr(tokens),
                                  _ptr(parent), None if greedy else _ptr(u), float(T), B, K, _ptr(ws), ws.numel(),
-                                 ctypes.byref(oc), _ptr(out.path), _stream(stream))
+                                 ctypes.byref(oc), _ptr(out.path), int(wait_polls), _stream(stream))
     _raise(rc, "spec_verify_tree")
     return out
 

@@ -2,7 +2,6 @@
 // the launch sequence of each verification mode.  Everything is enqueued on the
 // caller's stream; there is no host synchronisation and no allocation.
 #include <math.h>
-#include <cstdlib>
 #include <mutex>
 
 #include "sv_internal.h"
@@ -600,7 +599,7 @@ SV_API int spec_draft_propose(const sv_weights *w, const uint16_t *h_draft, cons
 
 SV_API int spec_verify_tree(const sv_weights *w, const uint16_t *h, const uint16_t *h_draft, const int32_t *tokens,
                             const int32_t *parent, const float *u, float T, int B, int K, void *ws, size_t ws_bytes,
-                            sv_outputs *out, int32_t *path, void *stream) {
+                            sv_outputs *out, int32_t *path, int wait_polls, void *stream) {
   int rc = check_common(w, h, tokens, B, K, ws, out);
   if (rc) return rc;
   if (K > 63 || (K > 0 && !parent) || !(T >= 0.f) || !isfinite(T)) return SV_EINVAL;
@@ -645,9 +644,9 @@ SV_API int spec_verify_tree(const sv_weights *w, const uint16_t *h, const uint16
     a.chunk_sums = at<float>(ws, p.o_tree);
     a.partials = a.chunk_sums + (size_t)B * tree_chunks(p.V);
     a.meet = sync + 1;
-    a.spin_limit = 1 << 16;  // a block waits for the others at most ~65 ms per pass
-    // test hook: SV_TREE_SPIN_LIMIT overrides the bound (0: every meeting times out)
-    if (const char *e = std::getenv("SV_TREE_SPIN_LIMIT")) a.spin_limit = std::atoi(e);
+    // a block waits for the others at most wait_polls polls per meeting (default 65,536,
+    // about 65 ms); 0 makes every meeting time out
+    a.spin_limit = wait_polls < 0 ? 1 << 16 : wait_polls;
   }
   SV_CHECK(launch_tree(a, st));
   return SV_OK;

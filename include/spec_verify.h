@@ -126,19 +126,29 @@ typedef struct sv_outputs {
                             pass); both NULL to skip.  For measurement only. */
 } sv_outputs;
 
-/* Bytes of device workspace a call with these sizes needs (0 on invalid sizes).
+/* Bytes of device workspace a call with these sizes needs (0 on invalid sizes).  The pages
+ * define no memory plan; this is the library's own (fp32 logit rows for the sampled modes,
+ * per-row statistic records, MLP activations).
  * mode: SV_MODE_*; K is Kmax in scheduled mode (the size covers any budget); in
  * propose mode B is the number of draft rows and K is ignored. */
 size_t sv_workspace_bytes(int mode, int B, int K, const sv_weights *w);
 
-/* Greedy verification (temperature 0).  h: [B, K+1, d] bf16 target hidden rows;
+/* Greedy verification (temperature 0).  Source: "Let's start over, Misha", "Why isn't the
+ * answer spoiled?" (at temperature 0 a draft token is kept when it is the target's argmax)
+ * and the Wildberries page, "Where speculative decoding came from" (the longest correct
+ * prefix is kept and the target's own token is put at the first error; one pass scores
+ * every position).  h: [B, K+1, d] bf16 target hidden rows;
  * draft: [B, K] int32.  A_b is the first j with draft[b, j] != argmax of target row
  * j (K if none); the emitted tokens are draft[b, 0..A_b-1] then the argmax of row
  * A_b.  Ties in the argmax go to the lowest index.  The diag records use T = 1. */
 int spec_verify_greedy(const sv_weights *w, const uint16_t *h, const int32_t *draft, int B, int K,
                        void *ws, size_t ws_bytes, sv_outputs *out, void *stream);
 
-/* Rejection-sampling verification at temperature T > 0.  h: [B, K+1, d];
+/* Rejection-sampling verification at temperature T > 0.  Source: the Wildberries page, "A
+ * bit of theory", Statement 1 (accept x with probability min(1, p(x)/q(x)), p and q after
+ * temperature; on rejection draw from the normalised max(0, p - q)), Statement 2 (the
+ * accepted length and tau), and "Let's start over, Misha", "How it works" (when every draft
+ * passes the same pass yields one more token from p).  h: [B, K+1, d];
  * h_draft: [B, K, d] draft hidden rows scored by the same LM head; draft: [B, K];
  * u: [B, K+1].  Draft token j+1 is accepted while u[b, j] < p_j(x)/q_j(x); at the
  * first rejection the emitted token is drawn from max(0, p_j - q_j) (falling back to
@@ -166,7 +176,11 @@ int spec_verify_sample_noalloc(const sv_weights *w, const uint16_t *h, const uin
                                const int32_t *draft, const float *u, float T, int B, int K, sv_outputs *out,
                                void *stream);
 
-/* Confidence-scheduled verification at temperature T > 0.  Shapes as in
+/* Confidence-scheduled verification at temperature T > 0.  Source: "DSpark: speculative
+ * decoding with confidence-scheduled verification and semi-autoregressive generation" (each
+ * request's verify length follows the estimated survival probability of its draft prefix,
+ * under the engine's capacity); the rule below is the library's reading of it (the page
+ * gives the idea, not the formula), then the sampled rule of spec_verify_sample.  Shapes as in
  * spec_verify_sample with K = Kmax.  The LM head first scores all B*Kmax draft rows;
  * c[b, k] = max_v q_{b,k}(v), survival s_b(k) = prod_{i<=k} c[b, i].  Positions with
  * s_b(k) >= survival_threshold are eligible; each request always verifies its own
@@ -180,8 +194,10 @@ int spec_verify_scheduled(const sv_weights *w, const uint16_t *h, const uint16_t
                           int budget_rows, int B, int Kmax, void *ws, size_t ws_bytes,
                           sv_outputs *out, void *stream);
 
-/* The drafter's step on the shared LM head (the call before verification in
- * MTP/EAGLE-style drafting).  h_draft: [rows, d]; coins: [rows] (unused when T == 0).
+/* The drafter's step on the shared LM head: the call before verification in MTP/EAGLE-style
+ * drafting ("Speculative decoding in vLLM and SGLang ...", "EAGLE and EAGLE-3": a light head
+ * over the target's hidden states proposes the next tokens; that it ends in the target's own
+ * LM head is this library's reading).  h_draft: [rows, d]; coins: [rows] (unused when T == 0).
  * draft_out[r] = token drawn from q = softmax(h_draft[r] W_lm^T / T) by inverse CDF
  * with coins[r], or the argmax when T == 0; conf_out[r] (may be NULL) = max_v q(v)
  * (1 when T == 0). */
@@ -214,12 +230,16 @@ int spec_draft_propose(const sv_weights *w, const uint16_t *h_draft, const float
  * the final token; path (may be NULL) [B, K+1] = node at each depth, -1 beyond A (the
  * tree path spec_commit takes).  A chain (parent[b, j] = j) gives exactly the results of
  * spec_verify_greedy / spec_verify_sample.  diag rows: target rows then (T > 0) draft
- * rows, records [0..3] as above, [4..6] NaN.  Requires K <= 63.  Workspace:
+ * rows, records [0..3] as above, [4..6] NaN.  At T > 0 the residual passes of a request may
+ * run on several workgroups that meet at a device-side counter; wait_polls bounds how often
+ * a workgroup polls for the others per meeting (< 0: 65,536, about 65 ms; 0 makes every
+ * meeting fail, which tests the time-out path): a request whose workgroups never meet gets
+ * SV_DEV_TIMEOUT and outputs -1 instead of a hang.  Requires K <= 63.  Workspace:
  * sv_workspace_bytes(SV_MODE_GREEDY, B, K, w) at T == 0, SV_MODE_SAMPLE at T > 0.  A bad
  * parent sets SV_DEV_BAD_TREE, a token outside [0, V) SV_DEV_BAD_TOKEN (request outputs -1). */
 int spec_verify_tree(const sv_weights *w, const uint16_t *h, const uint16_t *h_draft, const int32_t *tokens,
                      const int32_t *parent, const float *u, float T, int B, int K, void *ws, size_t ws_bytes,
-                     sv_outputs *out, int32_t *path, void *stream);
+                     sv_outputs *out, int32_t *path, int wait_polls, void *stream);
 
 /* Cached target state of B requests, for the commit after a verify call.
  *

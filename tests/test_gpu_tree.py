@@ -187,22 +187,20 @@ def test_tree_path_commits():
     assert np.array_equal(kv_d.cpu().numpy(), kv_e) and np.array_equal(rs_d.cpu().numpy(), st_e)
 
 
-def test_tree_meeting_timeout_is_reported(monkeypatch):
-    """With the blocks' wait bound forced to zero every meeting of a sampled tree fails:
+def test_tree_meeting_timeout_is_reported():
+    """With the blocks' wait bound set to zero polls every meeting of a sampled tree fails:
     the requests are flagged with SV_DEV_TIMEOUT and their outputs are -1 (no hang)."""
     wk = wl.SMALL.with_batch(3)
     data, W, parent, tokens, coins, ref = _case(wk, 3, "topk", wk.T)
     args = (pt.dev_weights(data), pt.dev_bf16(data["h"]), pt.dev_bf16(data["h_draft"]), _i32(tokens), _i32(parent),
             _f32(coins), wk.T)
-    monkeypatch.setenv("SV_TREE_SPIN_LIMIT", "0")
-    out = bd.spec_verify_tree(*args)
+    out = bd.spec_verify_tree(*args, wait_polls=0)
     torch.cuda.synchronize()
     acc = out.accepted_len.cpu().numpy()
     # a request whose walk needs no residual pass before its draw still meets once (the draw's pass)
     assert np.all(acc == -1)
     assert int(out.dev_status.item()) == bd.SV_DEV_TIMEOUT
     assert np.all(out.emitted.cpu().numpy() == -1)
-    monkeypatch.delenv("SV_TREE_SPIN_LIMIT")
     out = bd.spec_verify_tree(*args)
     torch.cuda.synchronize()
     assert int(out.dev_status.item()) == 0 and np.all(out.accepted_len.cpu().numpy() >= 0)
