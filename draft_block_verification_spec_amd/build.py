@@ -18,6 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libspecverify.so")
+PEAKS_LIB = os.path.join(PKG, "libsvpeaks.so")  # achievable-peak probes (measurement only)
+PEAKS_SRC = os.path.join(CSRC, "probe", "peaks.hip")
 ARCH = "gfx950"
 
 SOURCES = ["spec_verify.hip", "gemm_stream.hip", "gemm_tiled.hip", "verify_kernels.hip", "commit.hip"]
@@ -60,6 +62,9 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     outs.append(_run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]))
     os.replace(tmp, LIB)
+    tmp = PEAKS_LIB + ".tmp"
+    outs.append(_run([cc, *HIPCC_FLAGS, "-shared", PEAKS_SRC, "-o", tmp]))
+    os.replace(tmp, PEAKS_LIB)
     if verbose:
         for o in outs:
             if o.strip():

@@ -209,3 +209,20 @@ def test_noalloc_entry_rejects_before_touching_the_device(lib):
     assert lib.spec_verify_sample_noalloc(ctypes.byref(w), P, P, P, P, 0.0, 1, 15, ctypes.byref(o), None) == b.SV_EINVAL
     assert lib.spec_verify_sample_noalloc(ctypes.byref(w), None, P, P, P, 1.0, 1, 15, ctypes.byref(o),
                                           None) == b.SV_EINVAL
+
+
+def test_peak_probe_library_exports_its_header():
+    from draft_block_verification_spec_amd import peaks
+    if not os.path.exists(peaks.LIB_PATH):
+        from draft_block_verification_spec_amd import build
+        build.build()
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "sv_peaks.h")).read(), flags=re.S)
+    declared = set(re.findall(r"\b(sv_probe_\w+)\s*\(", src))
+    assert declared == set(peaks.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", peaks.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert {s for s in exported if s.startswith("sv_")} == declared
+    lib = peaks.load()
+    ms = ctypes.c_float()
+    assert lib.sv_probe_read(None, 1 << 20, 1 << 24, None, ctypes.byref(ms)) == -1  # rejected before any launch
+    assert lib.sv_probe_read(1 << 28, 100, 1 << 24, None, ctypes.byref(ms)) == -1

@@ -28,3 +28,11 @@ def test_bench_line():
     assert 0 < roof["frac"] < 1 and roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"])
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]
+    assert cpu["os_cpu_count"] >= 1
+    # tau over the rotated input sets, with its interval and the oracle's closed form beside it
+    assert d["input_sets"] == 16 and len(d["tau_sets"]) == 16
+    lo, hi = d["tau_ci95"]
+    assert lo <= d["tau"] <= hi
+    assert d["tau_closed_form"]["tau"] >= 1.0
+    peaks = d["measured_peaks"]
+    assert 1000 < peaks["hbm_read_GBps"] < 8000 and 100 < peaks["mfma_bf16_TFLOPs"] < 2500
