@@ -25,6 +25,95 @@ GAP_BAND = 1e-3
 CDF_BAND = 1e-4
 SURV_BAND = 1e-5
 
+# The bf16 MLP output y may round the other way than the fp64 oracle's y where its fp32
+# sums land within their rounding error of a bf16 rounding boundary (a flipped intermediate
+# a moves y as well).  The bar is derived per shape and weight format from a plain fp32
+# evaluation of the same sums on the CPU (numpy float32 products and sums): the GPU may flip
+# at most twice as many elements as that evaluation, plus three (counting noise on small
+# shapes).  For the 16-token block that evaluation flips 3-8e-3 of y with bf16 weights and
+# FP8 codes double its flips of a (6.9-7.3e-4 against 3.1-3.5e-4); the GPU flips ~1e-3.
+
+
+def fp32_flip_rate(W, h64) -> float:
+    """Share of y = bf16(h + a W_down^T), a = bf16(silu(h W_gate^T) * (h W_up^T)), that a plain
+    fp32 evaluation rounds differently from the fp64 oracle."""
+    h = np.asarray(h64, dtype=np.float64).reshape(-1, W.w_gate.shape[1])
+    y64 = oracle.target_hidden(h, W)
+    h32 = h.astype(np.float32)
+    g32 = h32 @ W.w_gate.astype(np.float32).T
+    u32 = h32 @ W.w_up.astype(np.float32).T
+    a32 = oracle.bf16_rne(oracle.silu(g32.astype(np.float64)) * u32)
+    y32 = oracle.bf16_rne(h + (a32.astype(np.float32) @ W.w_down.astype(np.float32).T).astype(np.float64))
+    return float(np.mean(y32 != y64))
+
+
+# Tallies over a test session: decisions compared, requests that differ, and the near-tie
+# class of each difference (every difference must have one); printed at the end of the run,
+# whose overall mismatch rate must stay below 0.1%.
+TALLY = {"requests": 0, "mismatches": 0, "decisions": 0, "in_band": 0}
+# near-tie classes of the first differing decision; the last two concern the final
+# inverse-CDF draw only (see first_diff_sample)
+CLASSES = {"ratio": 0, "argmax_gap": 0, "survival": 0, "cdf": 0, "final_from_logits": 0, "final_fp32_cdf": 0}
+# The final draw over V ~ 1.5e5 tokens: a token's probability (~7e-6) is far below the CDF
+# shift that one-ulp bf16 roundings of the MLP output put into the target logits, so the
+# GPU's final token can differ from the oracle's whenever the coin is not far from a token
+# boundary.  Where the GPU's logits are at hand the draw is checked exactly on them instead
+# (fp64 inverse CDF of the GPU's own rows): the GPU's token must be that draw, or the coin
+# within FP32_CDF_BAND of one of its boundaries (fp32 sums of the CDF).
+FP32_CDF_BAND = 1e-6
+FINAL_CLASSES = ("final_from_logits", "final_fp32_cdf")
+
+
+# (GPU flips, elements, plain fp32 evaluation's flip rate) per checked MLP output
+FLIPS: list = []
+
+
+def note(cls: str) -> None:
+    CLASSES[cls] += 1
+
+
+def count_bands(ref: dict, coins, kind: str) -> None:
+    """Count decisions of the oracle's run that fall inside a near-tie band (the raw
+    exception-class rate, whether or not the GPU differs there)."""
+    A = np.asarray(ref["accepted"])
+    if kind == "sample":
+        r = np.asarray(ref["ratio"], dtype=np.float64)
+        c = np.asarray(coins, dtype=np.float64)
+        for b in range(len(A)):
+            n = min(int(A[b]) + 1, r.shape[1]) if r.ndim == 2 else 0
+            for j in range(n):
+                if np.isfinite(r[b, j]):
+                    TALLY["decisions"] += 1
+                    TALLY["in_band"] += int(abs(c[b, j] - min(1.0, r[b, j])) < RATIO_BAND)
+            TALLY["decisions"] += 1
+            u = c[b, -1]
+            TALLY["in_band"] += int(min(abs(u - ref["cdf_lo"][b]), abs(u - ref["cdf_hi"][b])) < CDF_BAND)
+    else:
+        gap = np.asarray(ref["gap_t"])
+        for b in range(len(A)):
+            for j in range(int(A[b]) + 1):
+                TALLY["decisions"] += 1
+                TALLY["in_band"] += int(gap[b, j] < GAP_BAND)
+
+
+def check_hidden(out_hidden, ref_y, W, h64):
+    """bf16 MLP output y against the oracle: every element within one bf16 ulp + 1e-3 (a
+    flipped a moves y by |W_down| * ulp(a) before y's own rounding), and at most twice the
+    rounding flips of a plain fp32 evaluation of the same sums, plus three elements."""
+    rows = int(np.prod(np.shape(h64)[:-1]))
+    got = out_hidden.float().cpu().numpy().astype(np.float64).reshape(rows, -1)
+    ref = ref_y.reshape(rows, -1)
+    diff = np.abs(got - ref)
+    ulp = np.abs(ref) * 2.0 ** -7
+    assert np.all(diff <= ulp * 1.01 + 1e-3), f"MLP output differs by {diff.max()}"
+    n = diff.size
+    flips = int(np.sum(diff > 0))
+    ref_rate = fp32_flip_rate(W, h64)
+    FLIPS.append((flips, n, ref_rate))
+    bar = 2.0 * ref_rate * n + 3
+    assert flips <= bar, f"{flips} bf16 rounding flips of {n} (bar {bar:.0f}: twice a plain fp32 evaluation's, + 3)"
+    return flips / n
+
 
 def dev_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
@@ -57,21 +146,51 @@ def oracle_drafts(W: oracle.Weights, data: dict, T: float, rows=None) -> dict:
     return oracle.propose(W, hd, T, coins)
 
 
-def first_diff_sample(ref: dict, A_g: int, em_g: np.ndarray, b: int, coins: np.ndarray, K_b: int) -> str | None:
+def gpu_rows_draw(lg_t_row, lg_d_row, T: float, u: float):
+    """The final token drawn exactly (fp64) from the GPU's own logit rows: from max(0, p - q)
+    after a rejection (lg_d_row given; p if that is all zero), from p otherwise, by inverse
+    CDF over ascending token ids with coin u.  Returns (token, CDF below it, CDF through it)."""
+    p = oracle.softmax_t(np.asarray(lg_t_row, dtype=np.float64)[None], T)[0]
+    w = p
+    if lg_d_row is not None:
+        q = oracle.softmax_t(np.asarray(lg_d_row, dtype=np.float64)[None], T)[0]
+        r = np.maximum(p - q, 0.0)
+        w = r if r.sum() > 0 else p
+    v, lo, hi = oracle.inverse_cdf(w[None], np.array([u]))
+    return int(v[0]), float(lo[0]), float(hi[0])
+
+
+def first_diff_sample(ref: dict, A_g: int, em_g: np.ndarray, b: int, coins: np.ndarray, K_b: int,
+                      rows=None) -> str | None:
     """Classify the first decision where GPU and oracle differ for request b.
-    Returns None if it is an allowed near tie, else a description."""
+    Returns None if it is an allowed near tie, else a description.  ``rows(A)`` (optional)
+    gives the GPU's logit rows of the final draw at accepted length A: (target row,
+    draft row or None at the bonus position, T)."""
     A_o = int(ref["accepted"][b])
     if A_g != A_o:
         j = min(A_g, A_o)
         r = float(ref["ratio"][b, j])
         if abs(coins[b, j] - min(1.0, r)) < RATIO_BAND:
+            note("ratio")
             return None
         return f"acceptance differs at position {j}: u={coins[b, j]:.6f} ratio={r:.6f} (gpu A={A_g}, oracle A={A_o})"
     em_o = ref["emitted"][b]
     if np.array_equal(em_o[: A_o + 1], em_g[: A_o + 1]):
         return f"tail differs: {em_g} vs {em_o}"
     u = coins[b, -1]
+    if rows is not None:
+        lt, ld, T = rows(A_o)
+        v, lo, hi = gpu_rows_draw(lt, ld, T, float(u))
+        if int(em_g[A_o]) == v:
+            note("final_from_logits")
+            return None
+        if min(abs(u - lo), abs(u - hi)) < FP32_CDF_BAND:
+            note("final_fp32_cdf")
+            return None
+        return (f"final token {em_g[A_o]} is not the draw on the GPU's own logits ({v}; u={u:.8f}, "
+                f"cdf [{lo:.8f}, {hi:.8f}])")
     if min(abs(u - ref["cdf_lo"][b]), abs(u - ref["cdf_hi"][b])) < CDF_BAND:
+        note("cdf")
         return None
     return f"final token differs: gpu {em_g[A_o]} oracle {em_o[A_o]} (u={u:.6f}, cdf [{ref['cdf_lo'][b]:.6f}, {ref['cdf_hi'][b]:.6f}])"
 
@@ -94,11 +213,37 @@ def compare_requests(ref: dict, acc_g: np.ndarray, em_g: np.ndarray, classify) -
 
 
 def assert_decisions(ref, acc_g, em_g, classify, what=""):
+    """Every request whose decisions differ from the oracle's must differ first at a near tie
+    of a stated class.  Differences at an acceptance, argmax or schedule decision (or at the
+    final draw where no GPU logits are given) are counted against the 0.1% bar (per call:
+    fewer than 0.1% of B, or at most one for small B; over the session: below 0.1% of all
+    requests compared); final tokens that are the exact draw on the GPU's own logits are
+    counted and reported apart."""
+    before = {k: CLASSES[k] for k in FINAL_CLASSES}
     mism, bad = compare_requests(ref, acc_g, em_g, classify)
+    final = sum(CLASSES[k] - before[k] for k in FINAL_CLASSES)
     B = len(acc_g)
+    TALLY["requests"] += B
+    TALLY["mismatches"] += mism - final
+    TALLY["final_from_logits"] = TALLY.get("final_from_logits", 0) + final
     assert not bad, f"{what}: {len(bad)} unexplained mismatches, e.g. {bad[:3]}"
+    mism -= final
     if B >= 1000:
         assert mism < 0.001 * B, f"{what}: {mism} near-tie mismatches out of {B}"
     else:
         assert mism <= 1, f"{what}: {mism} near-tie mismatches out of {B}"
     return mism
+
+
+def summary() -> str:
+    t = TALLY
+    rate = t["mismatches"] / t["requests"] if t["requests"] else 0.0
+    band = t["in_band"] / t["decisions"] if t["decisions"] else 0.0
+    cls = ", ".join(f"{k} {v}" for k, v in CLASSES.items())
+    fin = t.get("final_from_logits", 0)
+    return (f"decision parity: {t['mismatches']} of {t['requests']} requests differ from the oracle at a counted "
+            f"near tie ({rate:.2e}); {fin} more differ only in the final token, which is the exact draw on the "
+            f"GPU's own logits ({fin / max(1, t['requests']):.2e}); first differing decision by class: {cls}; "
+            f"{t['in_band']} of {t['decisions']} oracle decisions lie in a near-tie band ({band:.2e})"
+            + ("; MLP output bf16 flips (GPU / plain fp32): "
+               + ", ".join(f"{f / n:.2e}/{r:.2e}" for f, n, r in FLIPS) if FLIPS else ""))

@@ -82,7 +82,9 @@ def test_fp8_rejects_batches_past_the_streaming_kernel():
 
 @pytest.mark.parametrize("T", [0.0, 1.0], ids=["greedy", "sample"])
 def test_fp8_tree_block16(T):
-    """Tree verification with FP8 weights: the 16-token block as a top-k tree."""
+    """Tree verification with FP8 weights: the 16-token block as a top-k tree.  Greedy: the
+    children of a node are its best draft tokens in rank order.  Sampled: every child is drawn
+    from its parent's q with its own coin (the rule is lossless for such children)."""
     wk = wl.BLOCK16
     data = wl.to_fp8(wl.generate(wk, 1))
     W = oracle.Weights.from_fp8(data)
@@ -93,10 +95,14 @@ def test_fp8_tree_block16(T):
     z_d = oracle.lm_logits(W.w_lm, hd64)
     coins = data["coins"].astype(np.float64)
     tok = np.zeros((wk.B, wk.K), np.int64)
-    for j in range(wk.K):  # child j+1 of node u: u's (rank)-th best draft token
-        u = int(parent[0, j])
-        r = int(np.sum(parent[0, :j] == u))
-        tok[0, j] = np.argsort(-z_d[0, u], kind="stable")[r]
+    if T == 0.0:
+        for j in range(wk.K):  # child j+1 of node u: u's (rank)-th best draft token
+            u = int(parent[0, j])
+            r = int(np.sum(parent[0, :j] == u))
+            tok[0, j] = np.argsort(-z_d[0, u], kind="stable")[r]
+    else:
+        q_par = oracle.softmax_t(z_d[0, parent[0]], T)  # [K, V]: q of each child's parent
+        tok[0] = oracle.inverse_cdf(q_par, data["draft_coins"][0].astype(np.float64))[0]
     if T == 0.0:
         ref = oracle.accept_tree_greedy(z_t, tok, parent)
     else:

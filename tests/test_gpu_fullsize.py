@@ -1,10 +1,9 @@
 """GPU parity at the full workload sizes, in the launch configuration the benchmark times.
 
-The oracle recomputes every output it can afford: all rows of the B=1 block, and a
-sample of the requests of the batched shapes (requests are independent, so a
-request's rows can be checked one by one).  The scheduled shapes are also checked
-through properties that hold at any size: the kept positions follow the survival
-rule applied to the GPU's own confidences, within the budget.
+The oracle recomputes every output it can afford: all rows of the B=1 block, every draft
+row and every request of the scheduled batches (their schedule is the oracle's own, from
+its own confidences), and a sample of the requests of the other batched shapes (requests
+are independent, so a request's rows can be checked one by one).
 """
 import numpy as np
 import pytest
@@ -14,6 +13,7 @@ import oracle
 from draft_block_verification_spec_amd import binding as bd
 from draft_block_verification_spec_amd import workload as wl
 from tests import parity as pt
+from tests.test_gpu_parity import _final_rows, _schedule_agrees
 
 pytestmark = pytest.mark.gpu
 
@@ -65,7 +65,10 @@ def test_block16_sample_full(rep):
     assert np.abs(dg[:K, 5] - ref["p_x"][0]).max() <= pt.PROB_TOL
     assert np.abs(dg[K + 1:, 5] - ref["q_x"][0]).max() <= pt.PROB_TOL
     acc, em = out.accepted_len.cpu().numpy(), out.emitted.cpu().numpy()
-    pt.assert_decisions(ref, acc, em, lambda b: pt.first_diff_sample(ref, int(acc[b]), em[b], b, coins, K),
+    pt.count_bands(ref, coins, "sample")
+    lg = out.logits.cpu().numpy()
+    rows = _final_rows(lg, wk.B, K, wk.T)
+    pt.assert_decisions(ref, acc, em, lambda b: pt.first_diff_sample(ref, int(acc[b]), em[b], b, coins, K, rows(b, K)),
                         "block16 sample")
 
 
@@ -84,8 +87,12 @@ def test_block16_greedy_full(rep):
 
     def classify(b):
         j = min(int(acc[b]), int(ref["accepted"][b]))
-        return None if gap[b, j] < pt.GAP_BAND else f"row {j} gap {gap[b, j]}"
+        if gap[b, j] < pt.GAP_BAND:
+            pt.note("argmax_gap")
+            return None
+        return f"row {j} gap {gap[b, j]}"
 
+    pt.count_bands(ref, None, "greedy")
     pt.assert_decisions(ref, acc, em, classify, "block16 greedy")
 
 
@@ -117,12 +124,19 @@ def test_sweep_greedy_sampled_requests(B):
 
         def classify(_b):
             j = min(int(acc[b]), int(ref["accepted"][0]))
-            return None if gap[0, j] < pt.GAP_BAND else f"request {b} row {j}"
+            if gap[0, j] < pt.GAP_BAND:
+                pt.note("argmax_gap")
+                return None
+            return f"request {b} row {j}"
 
+        pt.count_bands(ref, None, "greedy")
         pt.assert_decisions(ref, acc[b:b + 1], em[b:b + 1], classify, f"sweep B={B}")
 
 
 def _sched_check(wk):
+    """The whole scheduled batch against the oracle: every draft row's confidence and logits,
+    the oracle's own schedule (from its own confidences), and for every request the schedule
+    agrees on, its verified rows' logits and its decisions."""
     data, W, w = _setup(wk)
     B, K, V = wk.B, wk.K, wk.V
     hd_dev = pt.dev_bf16(data["h_draft"])
@@ -136,37 +150,29 @@ def _sched_check(wk):
     dg = out.diag.cpu().numpy().astype(np.float64)
     conf = dg[B * (K + 1):, 6].reshape(B, K)
     np.testing.assert_allclose(conf, conf_gpu.cpu().numpy(), atol=pt.PROB_TOL)
-    # the schedule is the survival rule applied to the GPU confidences
-    sch = oracle.survival_schedule(conf, wk.threshold, wk.budget)
-    s = sch["survival"]
-    if not np.array_equal(vl, sch["verify_len"]):
-        near = (np.abs(s - wk.threshold) < pt.SURV_BAND) | (np.abs(1024 * s - np.round(1024 * s)) < 1024 * pt.SURV_BAND)
-        assert near.any(), "schedule differs from the rule on the GPU's confidences"
+    coins = data["coins"].astype(np.float64)
+    ref = oracle.verify_scheduled(W, oracle.from_bf16_bits(data["h"]), oracle.from_bf16_bits(data["h_draft"]), draft,
+                                  coins, wk.T, wk.threshold, wk.budget)
+    np.testing.assert_allclose(conf, ref["conf"], atol=pt.PROB_TOL)
+    lg = out.logits.cpu().numpy()
+    _check_rows(lg[B * (K + 1):], ref["logits_d"].reshape(-1, V))
+    same = _schedule_agrees(vl, ref, wk)
     assert (vl + 1).sum() <= wk.budget
     assert np.all((vl >= 0) & (vl <= K))
-    lg = out.logits.cpu().numpy()
     acc, em = out.accepted_len.cpu().numpy(), out.emitted.cpu().numpy()
-    coins = data["coins"].astype(np.float64)
-    rng = np.random.default_rng(7)
-    sample = np.unique(np.concatenate([[0, B - 1], rng.choice(B, size=4, replace=False), [int(np.argmax(vl))]]))
-    for b in sample:
+    lt = lg[: B * (K + 1)].reshape(B, K + 1, V)
+    for b in np.nonzero(same)[0]:
         kb = int(vl[b])
-        hd64 = oracle.from_bf16_bits(data["h_draft"][b:b + 1])
-        zd = oracle.lm_logits(W.w_lm, hd64)[0]
-        np.testing.assert_allclose(conf[b], oracle.softmax_t(zd, wk.T).max(-1), atol=pt.PROB_TOL)
-        _check_rows(lg[B * (K + 1) + b * K: B * (K + 1) + (b + 1) * K], zd)
-        cb = np.concatenate([coins[b, :kb], coins[b, K:]])[None]
-        ref = oracle.verify_sample(W, oracle.from_bf16_bits(data["h"][b:b + 1, : kb + 1]),
-                                   hd64[:, :kb], draft[b:b + 1, :kb], cb, wk.T)
-        _check_rows(lg[b * (K + 1): b * (K + 1) + kb + 1], ref["logits_t"][0])
-        em_b = em[b, : kb + 1]
-        A = int(acc[b])
-
-        def classify(_b):
-            return pt.first_diff_sample(ref, A, em_b, 0, cb, kb)
-
-        pt.assert_decisions(ref, acc[b:b + 1], em_b[None], classify, f"{wk.name} request {b}")
+        _check_rows(lt[b, : kb + 1], ref["logits_t"][b, : kb + 1])
         assert np.all(em[b, kb + 1:] == -1)
+    sel = np.nonzero(same)[0]
+    sub = {k: (v[sel] if isinstance(v, np.ndarray) and v.shape[:1] == (B,) else v) for k, v in ref.items()}
+    pt.count_bands(sub, coins[sel], "sample")
+    rows = _final_rows(lg, B, K, wk.T)
+    pt.assert_decisions(sub, acc[sel], em[sel],
+                        lambda i: pt.first_diff_sample(sub, int(acc[sel[i]]), em[sel[i]], i, coins[sel], int(vl[sel[i]]),
+                                                       rows(sel[i], int(vl[sel[i]]))),
+                        f"{wk.name} (all {len(sel)} requests the schedule agrees on)")
     return vl
 
 
@@ -201,5 +207,7 @@ def test_wide_sample_sampled_requests():
         _check_rows(lg[b * (K + 1):(b + 1) * (K + 1)], ref["logits_t"][0])
         _check_rows(lg[B * (K + 1) + b * K: B * (K + 1) + (b + 1) * K], ref["logits_d"][0])
         A = int(acc[b])
-        pt.assert_decisions(ref, acc[sl], em[sl], lambda _b: pt.first_diff_sample(ref, A, em[b], 0, coins[sl], K),
+        pt.count_bands(ref, coins[sl], "sample")
+        rows = _final_rows(lg, B, K, wk.T)(b, K)
+        pt.assert_decisions(ref, acc[sl], em[sl], lambda _b: pt.first_diff_sample(ref, A, em[b], 0, coins[sl], K, rows),
                             f"wide request {b}")

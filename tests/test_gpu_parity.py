@@ -24,20 +24,6 @@ def _f32(x):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
 
 
-def _check_hidden(out_hidden, ref_y, rows):
-    got = out_hidden.float().cpu().numpy().astype(np.float64).reshape(rows, -1)
-    ref = ref_y.reshape(rows, -1)
-    diff = np.abs(got - ref)
-    # A one-ulp flip of an intermediate `a` moves y by |W_down| * ulp(a) ~ 1e-4 before y's own
-    # rounding, so y may differ by one of its ulps plus that amount, and only rarely: the fp32
-    # sums over K terms carry a relative error of about sqrt(K) * 2**-24 (6.6e-6 at K = 12288),
-    # and a value within that distance of a bf16 rounding boundary (ulp 2**-8 relative) rounds
-    # the other way with probability ~ 2 * 6.6e-6 / 2**-8 = 3.4e-3.
-    ulp = np.abs(ref) * 2.0 ** -7
-    assert np.all(diff <= ulp * 1.01 + 1e-3), f"MLP output differs by {diff.max()}"
-    assert np.mean(diff > 0) < 5e-3, f"too many bf16 rounding flips: {np.mean(diff > 0)}"
-
-
 def _weights(wk, rep, fp8):
     """Inputs, oracle weights and device weights (bf16, or FP8 codes + row scales)."""
     data = wl.generate(wk, rep)
@@ -45,6 +31,14 @@ def _weights(wk, rep, fp8):
         data = wl.to_fp8(data)
         return data, oracle.Weights.from_fp8(data), pt.dev_fp8_weights(data)
     return data, oracle.Weights.from_bits(data), pt.dev_weights(data)
+
+
+def _final_rows(lg, B, K, T):
+    """rows(b, K_b)(A): the GPU's logit rows of request b's final draw at accepted length A,
+    out of the logits in call order (target rows [B*(K+1)], then draft rows [B*K])."""
+    def rows(b, K_b):
+        return lambda A: (lg[b * (K + 1) + A], lg[B * (K + 1) + b * K + A] if A < K_b else None, T)
+    return rows
 
 
 def _run_sample(wk, rep=0, check_hidden=True, fp8=False):
@@ -66,7 +60,7 @@ def _run_sample(wk, rep=0, check_hidden=True, fp8=False):
     err = np.abs(lg - ref_lg).max()
     assert err <= pt.LOGIT_TOL, f"logit error {err}"
     if check_hidden and wk.d_ff > 0:
-        _check_hidden(out.hidden, ref["y"], B * (K + 1))
+        pt.check_hidden(out.hidden, ref["y"], W, h64)
     # p(x) on target rows j < K and q(x) on draft rows
     dg = out.diag.cpu().numpy().astype(np.float64)
     dt = dg[: B * (K + 1)].reshape(B, K + 1, -1)
@@ -79,7 +73,10 @@ def _run_sample(wk, rep=0, check_hidden=True, fp8=False):
     # decisions
     acc = out.accepted_len.cpu().numpy()
     em = out.emitted.cpu().numpy()
-    mism = pt.assert_decisions(ref, acc, em, lambda b: pt.first_diff_sample(ref, int(acc[b]), em[b], b, coins, K),
+    pt.count_bands(ref, coins, "sample")
+    rows = _final_rows(lg, B, K, T)
+    mism = pt.assert_decisions(ref, acc, em,
+                               lambda b: pt.first_diff_sample(ref, int(acc[b]), em[b], b, coins, K, rows(b, K)),
                                f"sample {wk.name}")
     tau = float(out.tau.item())
     assert tau == pytest.approx(np.mean(acc + 1), rel=1e-6)
@@ -108,6 +105,8 @@ def _run_greedy(wk, rep=0, fp8=False):
     torch.cuda.synchronize()
     B, K, V = wk.B, wk.K, wk.V
     assert int(out.dev_status.item()) == bd.SV_DEV_OK
+    if wk.d_ff > 0:
+        pt.check_hidden(out.hidden, ref["y"], W, oracle.from_bf16_bits(data["h"]))
     lg = out.logits.cpu().numpy().astype(np.float64)
     err = np.abs(lg - ref["logits_t"].reshape(-1, V)).max()
     assert err <= pt.LOGIT_TOL, f"logit error {err}"
@@ -122,8 +121,12 @@ def _run_greedy(wk, rep=0, fp8=False):
     def classify(b):
         A_o, A_g = int(ref["accepted"][b]), int(acc[b])
         j = min(A_o, A_g)
-        return None if gap[b, j] < pt.GAP_BAND else f"greedy decision differs at row {j} (gap {gap[b, j]:.2e})"
+        if gap[b, j] < pt.GAP_BAND:
+            pt.note("argmax_gap")
+            return None
+        return f"greedy decision differs at row {j} (gap {gap[b, j]:.2e})"
 
+    pt.count_bands(ref, None, "greedy")
     pt.assert_decisions(ref, acc, em, classify, f"greedy {wk.name}")
     # every emitted token is the target argmax of its row (the greedy invariant, on GPU output)
     for b in range(B):
@@ -149,13 +152,11 @@ def test_sample_parity_160_rows():
 
 
 def test_greedy_parity_160_rows():
-    ref, out = _run_greedy(MLP160)
-    _check_hidden(out.hidden, ref["y"], MLP160.M_t)
+    _run_greedy(MLP160)
 
 
 def test_greedy_parity_lm_head_in_two_launches():
-    ref, out = _run_greedy(LM_SPLIT)
-    _check_hidden(out.hidden, ref["y"], LM_SPLIT.M_t)
+    _run_greedy(LM_SPLIT)
 
 
 @pytest.mark.parametrize("name", ["small", "small_wide", "small_batch", "tiny"])
@@ -215,7 +216,9 @@ def test_sample_without_drafts():
     assert np.abs(lg - ref["logits_t"].reshape(-1, wk.V)).max() <= pt.LOGIT_TOL
     acc, em = out.accepted_len.cpu().numpy(), out.emitted.cpu().numpy()
     assert np.all(acc == 0)
-    pt.assert_decisions(ref, acc, em, lambda b: pt.first_diff_sample(ref, 0, em[b], b, coins, 0), "no drafts")
+    rows = _final_rows(lg, wk.B, 0, wk.T)
+    pt.assert_decisions(ref, acc, em, lambda b: pt.first_diff_sample(ref, 0, em[b], b, coins, 0, rows(b, 0)),
+                        "no drafts")
     assert float(out.tau.item()) == pytest.approx(1.0)
 
 
@@ -236,7 +239,19 @@ def test_scheduled_parity_two_row_tiles():
     _run_scheduled(SCHED_200)
 
 
-def _run_scheduled(wk):
+# A budget that does not bind: the verify GEMMs are planned for 512 rows (two row tiles)
+# while about 70 rows are verified, so only the first row tile is live and the down
+# projection takes its split-K path.
+SCHED_LOOSE = wl.Workload("sched_loose", 22, B=64, K=15, d=256, d_ff=512, V=3001, T=1.0, sigma=(0.3, 1.2),
+                          gain=(1.0, 2.5), threshold=0.3, budget=512)
+
+
+def test_scheduled_parity_budget_not_binding():
+    vl = _run_scheduled(SCHED_LOOSE, expect_bound=False)
+    assert 64 < (vl + 1).sum() <= 192, (vl + 1).sum()
+
+
+def _run_scheduled(wk, expect_bound=True):
     data = wl.generate(wk)
     W = oracle.Weights.from_bits(data)
     T = wk.T
@@ -244,7 +259,7 @@ def _run_scheduled(wk):
     coins = data["coins"].astype(np.float64)
     ref = oracle.verify_scheduled(W, oracle.from_bf16_bits(data["h"]), oracle.from_bf16_bits(data["h_draft"]), draft,
                                   coins, T, wk.threshold, wk.budget)
-    assert ref["budget_bound"], "the stress shape is meant to make the budget bind"
+    assert bool(ref["budget_bound"]) == expect_bound, "budget binding not as the shape intends"
     w = pt.dev_weights(data)
     out = bd.spec_verify_scheduled(w, pt.dev_bf16(data["h"]), pt.dev_bf16(data["h_draft"]), _i32(draft),
                                    _f32(data["coins"]), T, wk.threshold, wk.budget, diag=True, logits=True)
@@ -257,24 +272,50 @@ def _run_scheduled(wk):
     lg = out.logits.cpu().numpy().astype(np.float64)
     np.testing.assert_allclose(lg[B * (K + 1):], ref["logits_d"].reshape(-1, V), atol=pt.LOGIT_TOL, rtol=0)
     vl = out.verify_len.cpu().numpy()
-    s = ref["survival"]
-    near = (np.abs(s - wk.threshold) < pt.SURV_BAND) | (np.abs(1024 * s - np.round(1024 * s)) < 1024 * pt.SURV_BAND)
-    if not np.array_equal(vl, ref["verify_len"]):
-        assert near.any(), f"schedule differs without a near tie: {vl} vs {ref['verify_len']}"
-        pytest.skip("schedule differs on a near tie; decisions not comparable")
+    same = _schedule_agrees(vl, ref, wk)
     assert (vl + 1).sum() <= wk.budget
-    # verified target rows' logits (scattered back to their unpacked rows)
+    # every request the schedule agrees on: its verified target rows' logits (scattered back
+    # to their unpacked rows) and its decisions
     lt = lg[: B * (K + 1)].reshape(B, K + 1, V)
-    for b in range(B):
+    for b in np.nonzero(same)[0]:
         kb = int(vl[b])
         err = np.abs(lt[b, : kb + 1] - ref["logits_t"][b, : kb + 1]).max()
         assert err <= pt.LOGIT_TOL
     acc = out.accepted_len.cpu().numpy()
     em = out.emitted.cpu().numpy()
-    pt.assert_decisions(ref, acc, em, lambda b: pt.first_diff_sample(ref, int(acc[b]), em[b], b, coins, int(vl[b])),
+    sel = np.nonzero(same)[0]
+    sub = {k: (v[sel] if isinstance(v, np.ndarray) and v.shape[:1] == (B,) else v) for k, v in ref.items()}
+    pt.count_bands(sub, coins[sel], "sample")
+    rows = _final_rows(lg, B, K, T)
+    pt.assert_decisions(sub, acc[sel], em[sel],
+                        lambda i: pt.first_diff_sample(sub, int(acc[sel[i]]), em[sel[i]], i, coins[sel], int(vl[sel[i]]),
+                                                       rows(sel[i], int(vl[sel[i]]))),
                         "scheduled")
     c = out.counters.cpu().numpy()
     assert c[1] == vl.sum() and c[2] == (acc + 1).sum()
+    return vl
+
+
+def _schedule_agrees(vl, ref, wk):
+    """Requests whose verify length equals the oracle's.  Where they differ, the survival
+    products must lie within SURV_BAND of the threshold or of a 1/1024 key boundary (reading
+    R11): a request whose own survival is near the threshold, or any request when the budget
+    cut falls on a near-tie key (it can move positions between requests)."""
+    same = vl == ref["verify_len"]
+    if same.all():
+        return same
+    s = ref["survival"]
+    near_thr = np.abs(s - wk.threshold) < pt.SURV_BAND
+    near_key = np.abs(1024 * s - np.round(1024 * s)) < 1024 * pt.SURV_BAND
+    for b in np.nonzero(~same)[0]:
+        assert near_thr[b].any() or (ref["budget_bound"] and near_key.any()), \
+            f"request {b}: verify length {vl[b]} vs {ref['verify_len'][b]} without a near tie"
+        pt.note("survival")
+    TALLY_SCHED.append(int((~same).sum()))
+    return same
+
+
+TALLY_SCHED: list = []
 
 
 def test_propose_parity():
