@@ -75,7 +75,8 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
   if (a.counter_reset && blockIdx.x == 0 && blockIdx.z == 0)
     for (int i = threadIdx.x; i < max(1, a.counter_reset_n); i += blockDim.x) a.counter_reset[i] = 0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int M = a.M_dev ? min(a.M, *a.M_dev) : a.M;
+  const int M = live_rows(a);
+  if (M < 0) return;  // another launch of the same product does the work
   const int N = a.N;
   const int nks = a.K >> 5;
   const int nch = (nks + CHUNK_KS - 1) / CHUNK_KS;

@@ -61,164 +61,13 @@ constexpr int waves_per_eu() {
   return (BM * BN >= 256 * 256 || BM == 192 || (160 * 1024) / (NS * (BM + BN) * BK * 2) < 2) ? 1 : 2;
 }
 
-// PAIR: the weight rows of a tile are [32 gate | 32 up] groups of the same outputs.
-template <int BM, int BN, int BK, int NS, int EPI, bool PAIR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_eu<BM, BN, BK, NS>(), waves_per_eu<BM, BN, BK, NS>())))
-void k_tiled(const GemmArgs a) {
-  constexpr int RB = Slice<BK>::RB, CPR = Slice<BK>::CPR, RPI = Slice<BK>::RPI;
-  constexpr int SA = BM * RB, SB = BN * RB, SS = SA + SB;  // bytes of one slice
-  constexpr int IA = BM / RPI / 4, IB = BN / RPI / 4;      // 1 KB loads per wave per slice
+// The epilogue of one BM x BN tile, run by the four MFMA waves (2 x 2, wave (wm, wn) owns
+// rows wm*BM/2.. and columns wn*BN/2..) straight from their accumulators.
+template <int BM, int BN, int EPI, bool PAIR>
+__device__ __forceinline__ void tile_epilogue(const GemmArgs &a, f32x16 (&acc)[BM / 64][BN / 64], int m0, int n0,
+                                              int tni, int wm, int wn, int lane, int M, int Ncols, int z) {
   constexpr int WTM = BM / 2, WTN = BN / 2, TM = WTM / 32, TN = WTN / 32;
-  constexpr int KS = BK / 16;
-  static_assert(IA >= 1 && IB >= 1, "tile too small");
-  static_assert(NS >= 2 && (NS - 1) * (IA + IB) < 64, "slice pipeline depth");
-  static_assert(KS % 2 == 0, "fragment sets alternate within a slice");
-  static_assert(!PAIR || (WTN % 64) == 0, "paired tiles need gate/up block pairs");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * SS];
-
-  if (a.status_reset && blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0) *a.status_reset = 0;
-  if (a.counter_reset && blockIdx.x == 0 && blockIdx.z == 0)
-    for (int i = threadIdx.x; i < max(1, a.counter_reset_n); i += blockDim.x) a.counter_reset[i] = 0;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-  int M = a.M;
-  if (a.M_dev) M = min(M, *a.M_dev);
-  const int Ncols = PAIR ? 2 * a.N : a.N;  // columns of the weight-row space
-  // Only row tiles that hold rows are walked: with a device-side row count below a.M the
-  // live tiles still spread over every workgroup (skipping the dead ones in place would
-  // leave all live tiles to the workgroups whose slot meets them, half the grid at two
-  // row tiles).
-  const int tiles_m = M > 0 ? (M + BM - 1) / BM : 0;
-  const int total = tiles_m * ((Ncols + BN - 1) / BN);
-  const int splits = gridDim.z, z = blockIdx.z;
-  const int nkt_total = a.K / BK;
-  const int per = (nkt_total + splits - 1) / splits;
-  const int kt0 = z * per;
-  const int kt1 = min(nkt_total, kt0 + per);
-  const int nkt = kt1 > kt0 ? kt1 - kt0 : 0;
-  // Tiles: workgroup w takes tiles r*G + slot(w), r = 0, 1, ... (one round when the grid
-  // covers every tile).  With G a multiple of 8, workgroup w runs on XCD w % 8 and
-  // slot(w) = (w % 8) * G/8 + w / 8, so consecutive tiles - the row tiles of one weight
-  // tile - run on one XCD at the same time and read that weight tile through its L2.
-  // A persistent grid (one workgroup per CU slot) keeps those row tiles in step round
-  // after round; the hardware dispatcher would start them at scattered times.
-  const int G = gridDim.x;
-  const int slot = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
-  for (int lin = slot; lin < total; lin += G) {
-  const int tmi = lin % tiles_m, tni = lin / tiles_m;
-  const int m0 = tmi * BM, n0 = tni * BN;
-  if (m0 >= M) continue;
-  if (lin != slot) {  // every wave's reads of the previous tile's slices are done
-    lgkm_wait0();
-    __builtin_amdgcn_s_barrier();
-  }
-
-  // Per-lane global sources of the slice loads.  Load j of this wave fills LDS bytes
-  // [(wave + 4 j) KB, +1 KB) of the operand: rows (wave + 4 j) * RPI + lane / CPR, at
-  // swizzled chunk lane % CPR.  Rows past M (or N) read a clamped valid row; their
-  // results are never stored.
-  const uint16_t *ga[IA];
-  const uint16_t *gb[IB];
-  const int mlast = max(M, 1) - 1;
-#pragma unroll
-  for (int j = 0; j < IA; ++j) {
-    const int r = (wave + 4 * j) * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ Slice<BK>::swz(r);
-    const int m = min(m0 + r, mlast);
-    ga[j] = (m < a.m1 ? a.x1 + (long)m * a.ldx1 : a.x2 + (long)(m - a.m1) * a.ldx2) + c * 8;
-  }
-#pragma unroll
-  for (int j = 0; j < IB; ++j) {
-    const int r = (wave + 4 * j) * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ Slice<BK>::swz(r);
-    if constexpr (PAIR) {
-      const int p = r >> 6, half = (r >> 5) & 1, rr = r & 31;
-      const int n = min((n0 >> 1) + p * 32 + rr, a.N - 1);
-      gb[j] = (half ? a.w2 : a.w) + (long)n * a.K + c * 8;
-    } else {
-      const int n = min(n0 + r, a.N - 1);
-      gb[j] = a.w + (long)n * a.K + c * 8;
-    }
-  }
-  // element offset of slice t of this split; past the end it re-reads the last slice
-  auto kofs = [&](int t) -> long { return (long)(kt0 + min(t, nkt - 1)) * BK; };
-  auto issue_one = [&](long ko, uint32_t soff, int g) {
-    uint8_t *sb = smem + soff;
-    if (g < IA) dma16(ga[g] + ko, sb + (wave + 4 * g) * 1024);
-    else dma16(gb[g - IA] + ko, sb + SA + (wave + 4 * (g - IA)) * 1024);
-  };
-
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
   const int l32 = lane & 31, hi = lane >> 5;
-  // lane l reads row l%32 of a 32-row block at logical chunk 2 kk + l/32 of k step kk
-  int off[KS];
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) off[kk] = l32 * RB + (((kk * 2 + hi) ^ Slice<BK>::swz(l32)) << 4);
-  bf16x8 af[2][TM], bfr[2][TN];
-  auto lfrag_one = [&](int set, uint32_t soff, int kk, int g) {
-    const uint8_t *sb = smem + soff;
-    if (g < TM) af[set][g] = *reinterpret_cast<const bf16x8 *>(sb + (wm * WTM + g * 32) * RB + off[kk]);
-    else bfr[set][g - TM] = *reinterpret_cast<const bf16x8 *>(sb + SA + (wn * WTN + (g - TM) * 32) * RB + off[kk]);
-  };
-  // One k step: TM*TN MFMAs on fragment set `cur`; after MFMA q comes the LDS read of
-  // fragment q of the next step and, at a slice boundary, global->LDS load q.
-  auto step = [&](int cur, uint32_t rsoff, int rkk, bool ld, long ko, uint32_t lsoff) {
-#pragma unroll
-    for (int q = 0; q < TM * TN; ++q) {
-      const int i = q / TN, j = q % TN;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
-      if (ld && q < IA + IB) issue_one(ko, lsoff, q);
-      if (q < TM + TN) lfrag_one(cur ^ 1, rsoff, rkk, q);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (ld) {  // loads left over when a slice needs more loads than the step has MFMAs
-#pragma unroll
-      for (int g = TM * TN; g < IA + IB; ++g) issue_one(ko, lsoff, g);
-    }
-#pragma unroll
-    for (int g = TM * TN; g < TM + TN; ++g) lfrag_one(cur ^ 1, rsoff, rkk, g);
-  };
-
-  if (nkt > 0) {
-    // prologue: slices 0 .. NS-1 in flight, wait for slice 0
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-#pragma unroll
-      for (int g = 0; g < IA + IB; ++g) issue_one(kofs(s), s * SS, g);
-    }
-    vm_wait<(NS - 1) * (IA + IB)>();
-    __builtin_amdgcn_s_barrier();
-#pragma unroll
-    for (int g = 0; g < TM + TN; ++g) lfrag_one(0, 0, 0, g);
-
-    uint32_t scur = 0;
-    for (int t = 0; t < nkt; ++t) {
-      const uint32_t snext = scur + SS == NS * SS ? 0 : scur + SS;
-#pragma unroll
-      for (int kk = 0; kk + 1 < KS; ++kk) step(kk & 1, scur, kk + 1, false, 0, 0);
-      // Slice boundary: every wave has finished reading slice t (its LDS reads are
-      // complete), slice t+1 has landed.  Refill slice t's buffer with slice t+NS and
-      // start reading slice t+1.  After the last slice this reads a stale buffer that
-      // no MFMA consumes.
-      lgkm_wait0();
-      vm_wait<(NS - 2) * (IA + IB)>();
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      step((KS - 1) & 1, snext, 0, true, kofs(t + NS), scur);
-      scur = snext;
-    }
-    // no load may still be writing LDS when the workgroup leaves
-    vm_wait<0>();
-  }
-
   // ---- epilogue.  Lane l of block (i, j) holds column l%32 and, for register r,
   // row (r/4)*8 + (l/32)*4 + r%4 of the 32x32 block.
   const int rsub = hi * 4;
@@ -354,14 +203,175 @@ void k_tiled(const GemmArgs a) {
       if ((lane & 1) == 0 && m < M) a.parts[(long)m * a.nslots + pslot] = st;
     }
   }
+}
+
+// PAIR: the weight rows of a tile are [32 gate | 32 up] groups of the same outputs.
+template <int BM, int BN, int BK, int NS, int EPI, bool PAIR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(waves_per_eu<BM, BN, BK, NS>(), waves_per_eu<BM, BN, BK, NS>())))
+void k_tiled(const GemmArgs a) {
+  constexpr int RB = Slice<BK>::RB, CPR = Slice<BK>::CPR, RPI = Slice<BK>::RPI;
+  constexpr int SA = BM * RB, SB = BN * RB, SS = SA + SB;  // bytes of one slice
+  constexpr int IA = BM / RPI / 4, IB = BN / RPI / 4;      // 1 KB loads per wave per slice
+  constexpr int WTM = BM / 2, WTN = BN / 2, TM = WTM / 32, TN = WTN / 32;
+  constexpr int KS = BK / 16;
+  static_assert(IA >= 1 && IB >= 1, "tile too small");
+  static_assert(NS >= 2 && (NS - 1) * (IA + IB) < 64, "slice pipeline depth");
+  static_assert(KS % 2 == 0, "fragment sets alternate within a slice");
+  static_assert(!PAIR || (WTN % 64) == 0, "paired tiles need gate/up block pairs");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * SS];
+
+  if (a.status_reset && blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0) *a.status_reset = 0;
+  if (a.counter_reset && blockIdx.x == 0 && blockIdx.z == 0)
+    for (int i = threadIdx.x; i < max(1, a.counter_reset_n); i += blockDim.x) a.counter_reset[i] = 0;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int M = live_rows(a);
+  if (M < 0) return;  // another launch of the same product does the work
+  const int Ncols = PAIR ? 2 * a.N : a.N;  // columns of the weight-row space
+  // Only row tiles that hold rows are walked: with a device-side row count below a.M the
+  // live tiles still spread over every workgroup (skipping the dead ones in place would
+  // leave all live tiles to the workgroups whose slot meets them, half the grid at two
+  // row tiles).
+  const int tiles_m = M > 0 ? (M + BM - 1) / BM : 0;
+  const int total = tiles_m * ((Ncols + BN - 1) / BN);
+  const int splits = gridDim.z, z = blockIdx.z;
+  const int nkt_total = a.K / BK;
+  const int per = (nkt_total + splits - 1) / splits;
+  const int kt0 = z * per;
+  const int kt1 = min(nkt_total, kt0 + per);
+  const int nkt = kt1 > kt0 ? kt1 - kt0 : 0;
+  // Tiles: workgroup w takes tiles r*G + slot(w), r = 0, 1, ... (one round when the grid
+  // covers every tile).  With G a multiple of 8, workgroup w runs on XCD w % 8 and
+  // slot(w) = (w % 8) * G/8 + w / 8, so consecutive tiles - the row tiles of one weight
+  // tile - run on one XCD at the same time and read that weight tile through its L2.
+  // A persistent grid (one workgroup per CU slot) keeps those row tiles in step round
+  // after round; the hardware dispatcher would start them at scattered times.
+  const int G = gridDim.x;
+  const int slot = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  for (int lin = slot; lin < total; lin += G) {
+  const int tmi = lin % tiles_m, tni = lin / tiles_m;
+  const int m0 = tmi * BM, n0 = tni * BN;
+  if (m0 >= M) continue;
+  if (lin != slot) {  // every wave's reads of the previous tile's slices are done
+    lgkm_wait0();
+    __builtin_amdgcn_s_barrier();
+  }
+
+  // Per-lane global sources of the slice loads.  Load j of this wave fills LDS bytes
+  // [(wave + 4 j) KB, +1 KB) of the operand: rows (wave + 4 j) * RPI + lane / CPR, at
+  // swizzled chunk lane % CPR.  Rows past M (or N) read a clamped valid row; their
+  // results are never stored.
+  const uint16_t *ga[IA];
+  const uint16_t *gb[IB];
+  const int mlast = max(M, 1) - 1;
+#pragma unroll
+  for (int j = 0; j < IA; ++j) {
+    const int r = (wave + 4 * j) * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ Slice<BK>::swz(r);
+    const int m = min(m0 + r, mlast);
+    ga[j] = (m < a.m1 ? a.x1 + (long)m * a.ldx1 : a.x2 + (long)(m - a.m1) * a.ldx2) + c * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < IB; ++j) {
+    const int r = (wave + 4 * j) * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ Slice<BK>::swz(r);
+    if constexpr (PAIR) {
+      const int p = r >> 6, half = (r >> 5) & 1, rr = r & 31;
+      const int n = min((n0 >> 1) + p * 32 + rr, a.N - 1);
+      gb[j] = (half ? a.w2 : a.w) + (long)n * a.K + c * 8;
+    } else {
+      const int n = min(n0 + r, a.N - 1);
+      gb[j] = a.w + (long)n * a.K + c * 8;
+    }
+  }
+  // element offset of slice t of this split; past the end it re-reads the last slice
+  auto kofs = [&](int t) -> long { return (long)(kt0 + min(t, nkt - 1)) * BK; };
+  auto issue_one = [&](long ko, uint32_t soff, int g) {
+    uint8_t *sb = smem + soff;
+    if (g < IA) dma16(ga[g] + ko, sb + (wave + 4 * g) * 1024);
+    else dma16(gb[g - IA] + ko, sb + SA + (wave + 4 * (g - IA)) * 1024);
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int l32 = lane & 31, hi = lane >> 5;
+  // lane l reads row l%32 of a 32-row block at logical chunk 2 kk + l/32 of k step kk
+  int off[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) off[kk] = l32 * RB + (((kk * 2 + hi) ^ Slice<BK>::swz(l32)) << 4);
+  bf16x8 af[2][TM], bfr[2][TN];
+  auto lfrag_one = [&](int set, uint32_t soff, int kk, int g) {
+    const uint8_t *sb = smem + soff;
+    if (g < TM) af[set][g] = *reinterpret_cast<const bf16x8 *>(sb + (wm * WTM + g * 32) * RB + off[kk]);
+    else bfr[set][g - TM] = *reinterpret_cast<const bf16x8 *>(sb + SA + (wn * WTN + (g - TM) * 32) * RB + off[kk]);
+  };
+  // One k step: TM*TN MFMAs on fragment set `cur`; after MFMA q comes the LDS read of
+  // fragment q of the next step and, at a slice boundary, global->LDS load q.
+  auto step = [&](int cur, uint32_t rsoff, int rkk, bool ld, long ko, uint32_t lsoff) {
+#pragma unroll
+    for (int q = 0; q < TM * TN; ++q) {
+      const int i = q / TN, j = q % TN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
+      if (ld && q < IA + IB) issue_one(ko, lsoff, q);
+      if (q < TM + TN) lfrag_one(cur ^ 1, rsoff, rkk, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (ld) {  // loads left over when a slice needs more loads than the step has MFMAs
+#pragma unroll
+      for (int g = TM * TN; g < IA + IB; ++g) issue_one(ko, lsoff, g);
+    }
+#pragma unroll
+    for (int g = TM * TN; g < TM + TN; ++g) lfrag_one(cur ^ 1, rsoff, rkk, g);
+  };
+
+  if (nkt > 0) {
+    // prologue: slices 0 .. NS-1 in flight, wait for slice 0
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+#pragma unroll
+      for (int g = 0; g < IA + IB; ++g) issue_one(kofs(s), s * SS, g);
+    }
+    vm_wait<(NS - 1) * (IA + IB)>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int g = 0; g < TM + TN; ++g) lfrag_one(0, 0, 0, g);
+
+    uint32_t scur = 0;
+    for (int t = 0; t < nkt; ++t) {
+      const uint32_t snext = scur + SS == NS * SS ? 0 : scur + SS;
+#pragma unroll
+      for (int kk = 0; kk + 1 < KS; ++kk) step(kk & 1, scur, kk + 1, false, 0, 0);
+      // Slice boundary: every wave has finished reading slice t (its LDS reads are
+      // complete), slice t+1 has landed.  Refill slice t's buffer with slice t+NS and
+      // start reading slice t+1.  After the last slice this reads a stale buffer that
+      // no MFMA consumes.
+      lgkm_wait0();
+      vm_wait<(NS - 2) * (IA + IB)>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      step((KS - 1) & 1, snext, 0, true, kofs(t + NS), scur);
+      scur = snext;
+    }
+    // no load may still be writing LDS when the workgroup leaves
+    vm_wait<0>();
+  }
+
+  tile_epilogue<BM, BN, EPI, PAIR>(a, acc, m0, n0, tni, wm, wn, lane, M, Ncols, z);
   }  // tiles
 }
 
 // Fixed-order reduction of split-K partials followed by the elementwise epilogue.
 template <int EPI>
 __global__ __launch_bounds__(256) void k_splitk_reduce(const GemmArgs a, int splits, int bn) {
-  int M = a.M;
-  if (a.M_dev) M = min(M, *a.M_dev);
+  const int M = live_rows(a);
+  if (M < 0) return;
   const long total = (long)M * a.N;
   const int Ncols = (EPI == EPI_SWIGLU) ? 2 * a.N : a.N;
   const long stride = (long)a.M * Ncols;
@@ -475,7 +485,7 @@ int tiled_per_cu(const TileShape &sh) {
 }
 
 hipError_t launch_gemm_tiled(const GemmArgs &a, int epi, const TileShape &sh, int splits, hipStream_t st) {
-  if (a.K % sh.bk != 0) return hipErrorInvalidValue;
+  if (a.K % sh.bk != 0 || a.K < sh.bk) return hipErrorInvalidValue;
 #define SV_LAUNCH(BM, BN, BK, NS) \
   if (sh.bm == BM && sh.bn == BN && sh.bk == BK && sh.ns == NS) return launch_shape<BM, BN, BK, NS>(a, epi, splits, st);
   SV_TILE_SHAPES(SV_LAUNCH)

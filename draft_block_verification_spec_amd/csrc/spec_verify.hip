@@ -120,6 +120,10 @@ struct Plan {
   int mode = 0, B = 0, K = 0, d = 0, d_ff = 0, V = 0;
   int M_t = 0, M_lm = 0, rows_d = 0, budget = 0;
   Gemm gu, dn, lm, s1;
+  // scheduled mode: plans for at most m_split verified rows (gu_lo, dn_lo, lm_lo), run
+  // beside the budget-sized plans; the device-side row count picks the one that works
+  int m_split = 0;
+  Gemm gu_lo, dn_lo, lm_lo;
   size_t o_a = 0, o_y = 0, o_part = 0, o_parts = 0, o_parts_d = 0, o_logits = 0, o_logits_d = 0,
          o_jobs = 0, o_sums = 0, o_conf = 0, o_vlen = 0, o_rowoff = 0, o_rowmap = 0, o_mtot = 0,
          o_hp = 0, o_sync = 0, o_lse = 0, o_tree = 0, total = 0;
@@ -147,6 +151,34 @@ bool fp8_ok(const Gemm &g, int N) {
   if (!g.stream || g.grid < 1) return false;
   const int ntiles = (N + 15) / 16;
   return 16 * ((ntiles + g.grid - 1) / g.grid) <= 2048;
+}
+
+// Scheduled mode: the verified rows are known only on the device, and the budget-sized
+// plans (256-row tiles at a 512-row budget) run far below their rate when few rows pass
+// the threshold.  Plans for at most SMALL_ROWS rows are kept beside them when the
+// budget-sized LM head uses taller tiles; both are launched and the device-side count
+// lets exactly one of each pair work.  Both LM-head plans write the same statistics
+// slots (same column tiles).
+constexpr int SMALL_ROWS = 128;
+bool plan_small_rows(Plan &p, int V) {
+  if (p.budget <= SMALL_ROWS || p.lm.stream || p.lm.n_split > 0 || p.lm.shape.bm <= SMALL_ROWS) return false;
+  Gemm lo = choose(SMALL_ROWS, V, p.d, EPI_LOGITS);
+  if (lo.stream) return false;
+  if (lo.shape.bn != p.lm.shape.bn) {
+    if (p.lm.shape.bn == 256) lo.shape = TileShape{128, 256, 64, 3};
+    else if (p.lm.shape.bn == 128) lo.shape = TileShape{128, 128, 64, 4};
+    else return false;
+    lo.nslots = tiled_slots(V, lo.shape.bn);
+  }
+  if (lo.n_split > 0 || lo.nslots != p.lm.nslots) return false;
+  if (p.d_ff > 0) {
+    p.gu_lo = choose(SMALL_ROWS, p.d_ff, p.d, EPI_SWIGLU);
+    p.dn_lo = choose(SMALL_ROWS, p.d, p.d_ff, EPI_RESID);
+    if (p.gu_lo.stream || p.dn_lo.stream || p.gu.stream || p.dn.stream) return false;
+  }
+  p.lm_lo = lo;
+  p.m_split = SMALL_ROWS;
+  return true;
 }
 
 bool make_plan(int mode, int B, int K, const sv_weights *w, int budget, Plan &p) {
@@ -190,8 +222,12 @@ bool make_plan(int mode, int B, int K, const sv_weights *w, int budget, Plan &p)
     p.o_a = take(2 * (size_t)M_mlp * w->d_ff);
     p.o_y = take(2 * (size_t)M_mlp * d);
   }
-  if (part_floats) p.o_part = take(sizeof(float) * part_floats);
   p.lm = choose(p.M_lm, V, d, EPI_LOGITS);
+  if (mode == SV_MODE_SCHEDULED && w->wtype == SV_WEIGHTS_BF16 && plan_small_rows(p, V)) {
+    if (p.gu_lo.partial_floats > part_floats) part_floats = p.gu_lo.partial_floats;
+    if (p.dn_lo.partial_floats > part_floats) part_floats = p.dn_lo.partial_floats;
+  }
+  if (part_floats) p.o_part = take(sizeof(float) * part_floats);
   p.o_parts = take(sizeof(StatPart) * (size_t)p.M_lm * p.lm.nslots);
   const int NJ = B * (K + 1);
   if (mode != SV_MODE_GREEDY) {
@@ -302,25 +338,33 @@ void set_w(GemmArgs &g, const void *wt, const float *sc, const void *wt2, const 
 }
 void set_lm(GemmArgs &g, const sv_weights *w) { set_w(g, w->w_lm, w->s_lm, nullptr, nullptr, w->wtype); }
 
-hipError_t run_mlp(const Plan &p, const sv_weights *w, const uint16_t *h, int M, const int *M_dev, uint16_t *y,
-                   void *ws, int32_t *status_reset, hipStream_t st) {
+// With a device-side row count M_dev, the pair of launches does its work only when
+// m_lo < *M_dev <= m_hi (m_hi = 0: no upper limit).
+hipError_t run_mlp_plans(const Plan &p, const Gemm &gu, const Gemm &dnp, const sv_weights *w, const uint16_t *h,
+                         int M, const int *M_dev, int m_lo, int m_hi, uint16_t *y, void *ws, int32_t *status_reset,
+                         hipStream_t st) {
   uint16_t *abuf = at<uint16_t>(ws, p.o_a);
   GemmArgs g = base_args();
   g.x1 = h; g.ldx1 = p.d; g.m1 = M; g.x2 = h; g.ldx2 = p.d;
-  g.M = M; g.M_dev = M_dev; g.N = p.d_ff; g.K = p.d;
+  g.M = M; g.M_dev = M_dev; g.m_lo = m_lo; g.m_hi = m_hi; g.N = p.d_ff; g.K = p.d;
   set_w(g, w->w_gate, w->s_gate, w->w_up, w->s_up, w->wtype);
   g.out = abuf; g.ldo = p.d_ff;
-  g.partial = p.gu.splits > 1 ? at<float>(ws, p.o_part) : nullptr;
+  g.partial = gu.splits > 1 ? at<float>(ws, p.o_part) : nullptr;
   g.status_reset = status_reset;
-  hipError_t e = run_gemm(p.gu, g, EPI_SWIGLU, st);
+  hipError_t e = run_gemm(gu, g, EPI_SWIGLU, st);
   if (e != hipSuccess) return e;
   GemmArgs dn = base_args();
   dn.x1 = abuf; dn.ldx1 = p.d_ff; dn.m1 = M; dn.x2 = abuf; dn.ldx2 = p.d_ff;
-  dn.M = M; dn.M_dev = M_dev; dn.N = p.d; dn.K = p.d_ff;
+  dn.M = M; dn.M_dev = M_dev; dn.m_lo = m_lo; dn.m_hi = m_hi; dn.N = p.d; dn.K = p.d_ff;
   set_w(dn, w->w_down, w->s_down, nullptr, nullptr, w->wtype);
   dn.out = y; dn.ldo = p.d; dn.resid = h; dn.ldr = p.d;
-  dn.partial = p.dn.splits > 1 ? at<float>(ws, p.o_part) : nullptr;
-  return run_gemm(p.dn, dn, EPI_RESID, st);
+  dn.partial = dnp.splits > 1 ? at<float>(ws, p.o_part) : nullptr;
+  return run_gemm(dnp, dn, EPI_RESID, st);
+}
+
+hipError_t run_mlp(const Plan &p, const sv_weights *w, const uint16_t *h, int M, const int *M_dev, uint16_t *y,
+                   void *ws, int32_t *status_reset, hipStream_t st) {
+  return run_mlp_plans(p, p.gu, p.dn, w, h, M, M_dev, 0, 0, y, ws, status_reset, st);
 }
 
 int check_common(const sv_weights *w, const uint16_t *h, const int32_t *draft, int B, int K, void *ws,
@@ -526,11 +570,14 @@ SV_API int spec_verify_scheduled(const sv_weights *w, const uint16_t *h, const u
   reset = nullptr;
   SV_CHECK(launch_schedule(sa, st));
   SV_CHECK(launch_gather_rows(h, hp, rowmap, mtot, p.budget, p.d, st));
-  // S3-S5 on the packed target rows
+  // S3-S5 on the packed target rows: with small-row plans, each product is launched for
+  // at most m_split rows and for more, and the device-side count m_total picks one
+  const int ms = p.m_split;
   const uint16_t *y = hp;
   if (p.d_ff > 0) {
     uint16_t *ybuf = at<uint16_t>(ws, p.o_y);
-    SV_CHECK(run_mlp(p, w, hp, p.budget, mtot, ybuf, ws, nullptr, st));
+    if (ms > 0) SV_CHECK(run_mlp_plans(p, p.gu_lo, p.dn_lo, w, hp, ms, mtot, 0, ms, ybuf, ws, nullptr, st));
+    SV_CHECK(run_mlp_plans(p, p.gu, p.dn, w, hp, p.budget, mtot, ms, 0, ybuf, ws, nullptr, st));
     y = ybuf;
   }
   float *logits_t = at<float>(ws, p.o_logits);
@@ -541,6 +588,12 @@ SV_API int spec_verify_scheduled(const sv_weights *w, const uint16_t *h, const u
   g.parts = at<StatPart>(ws, p.o_parts); g.nslots = p.lm.nslots;
   g.invT = invT; g.want_s = 1;
   int32_t *sync = at<int32_t>(ws, p.o_sync);
+  if (ms > 0) {
+    GemmArgs gl = g;
+    gl.M = ms; gl.m1 = ms; gl.m_hi = ms;
+    SV_CHECK(run_gemm(p.lm_lo, gl, EPI_LOGITS, st));
+    g.m_lo = ms;
+  }
   SV_CHECK(run_gemm(p.lm, g, EPI_LOGITS, st));
   // S6-S9
   AcceptArgs a = {};

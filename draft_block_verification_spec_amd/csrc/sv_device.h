@@ -16,6 +16,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Rows of a launch: a.M, or the device-side count when one is given.  A launch gated
+// to a range of device-side counts (m_lo < count <= m_hi) gets -1 outside it.
+__device__ __forceinline__ int live_rows(const GemmArgs &a) {
+  if (!a.M_dev) return a.M;
+  const int md = *a.M_dev;
+  if (md <= a.m_lo || (a.m_hi > 0 && md > a.m_hi)) return -1;
+  return min(a.M, md);
+}
+
+
 __device__ __forceinline__ u32x4 ld_nt(const uint16_t *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }

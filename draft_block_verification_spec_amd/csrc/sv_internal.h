@@ -41,6 +41,9 @@ struct GemmArgs {
   int m1;
   int M;             // rows (upper bound when M_dev is given)
   const int *M_dev;  // optional device-side row count (scheduled mode)
+  // With M_dev: the launch does its work only when m_lo < *M_dev and, if m_hi > 0,
+  // *M_dev <= m_hi (a plan for few rows and one for many, both launched, one working)
+  int m_lo, m_hi;
   int N;             // output columns (for SWIGLU: columns of a)
   int K;             // reduction length, multiple of 64
   const uint16_t *w;   // [N, K] (SWIGLU: gate rows)

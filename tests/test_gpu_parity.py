@@ -4,6 +4,8 @@ Reduced shapes span several GEMM tiles and ragged tails (V = 5003, 12347, 4099, 
 M not a multiple of 16) and are compared element by element; the full-size shapes
 are in test_gpu_fullsize.py.
 """
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -239,16 +241,44 @@ def test_scheduled_parity_two_row_tiles():
     _run_scheduled(SCHED_200)
 
 
-# A budget that does not bind: the verify GEMMs are planned for 512 rows (two row tiles)
-# while about 70 rows are verified, so only the first row tile is live and the down
-# projection takes its split-K path.
+# A budget that does not bind: the verify GEMMs are planned for 512 rows (two row tiles
+# of 256) while 142 rows are verified, so only the first row tile is live, the down
+# projection takes its split-K path, and of each pair of launches (plans for at most 128
+# rows and for the budget) the budget-sized one works.
 SCHED_LOOSE = wl.Workload("sched_loose", 22, B=64, K=15, d=256, d_ff=512, V=3001, T=1.0, sigma=(0.3, 1.2),
                           gain=(1.0, 2.5), threshold=0.3, budget=512)
 
 
 def test_scheduled_parity_budget_not_binding():
     vl = _run_scheduled(SCHED_LOOSE, expect_bound=False)
-    assert 64 < (vl + 1).sum() <= 192, (vl + 1).sum()
+    assert 128 < (vl + 1).sum() <= 192, (vl + 1).sum()
+
+
+# The same batch with a higher threshold: 105 rows verified, so the launches planned for
+# at most 128 rows (128 x 256 LM-head tiles) do the work and the budget-sized ones return.
+SCHED_FEW = replace(SCHED_LOOSE, name="sched_few", threshold=0.5)
+
+
+def test_scheduled_parity_few_rows_small_plans():
+    vl = _run_scheduled(SCHED_FEW, expect_bound=False)
+    assert 64 < (vl + 1).sum() <= 128, (vl + 1).sum()
+
+
+# A 160-row budget: the budget-sized LM head uses 256 x 128 tiles and the small plan
+# 128 x 128 ones (the same statistics slots).  Binding (160 rows: the budget-sized
+# launches work) and not binding (105 rows: the small ones work).
+SCHED_160 = replace(SCHED_200, name="sched_160", budget=160)
+SCHED_160_FEW = replace(SCHED_LOOSE, name="sched_160_few", threshold=0.5, budget=160)
+
+
+def test_scheduled_parity_budget_160_binding():
+    vl = _run_scheduled(SCHED_160)
+    assert (vl + 1).sum() == 160
+
+
+def test_scheduled_parity_budget_160_few_rows():
+    vl = _run_scheduled(SCHED_160_FEW, expect_bound=False)
+    assert 64 < (vl + 1).sum() <= 128, (vl + 1).sum()
 
 
 def _run_scheduled(wk, expect_bound=True):
