@@ -74,3 +74,39 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+
+
+# A build of the library whose host code carries AddressSanitizer and
+# UndefinedBehaviorSanitizer (the device code is built as usual, without them), and the
+# C++ program that runs the host-side ABI checks against it; the checks never reach the
+# device, so no GPU is needed.  Every sanitizer flag applies to the host pass only.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
+HOST_CHECKS_SRC = os.path.join(ROOT, "tests", "abi_host_checks.cpp")
+
+
+def build_host_checks(out_dir: str) -> str:
+    """Build the host-sanitized library and the check program into out_dir; return the
+    program's path."""
+    os.makedirs(out_dir, exist_ok=True)
+    cc = hipcc()
+    base = [f"--offload-arch={ARCH}", "-O1", "-g", "-std=c++17", "-fPIC", "-fvisibility=hidden",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}", *SANITIZE]
+    objs, cmds = [], []
+    for s in SOURCES:
+        o = os.path.join(out_dir, s.replace(".hip", ".o"))
+        objs.append(o)
+        cmds.append([cc, *base, "-c", os.path.join(CSRC, s), "-o", o])
+    with ThreadPoolExecutor(len(cmds)) as ex:
+        list(ex.map(_run, cmds))
+    lib = os.path.join(out_dir, "libspecverify.so")
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *SANITIZE, *objs, "-o", lib])
+    exe = os.path.join(out_dir, "abi_host_checks")
+    clangxx = os.path.join(os.path.dirname(os.path.realpath(cc)), "..", "lib", "llvm", "bin", "clang++")
+    if not os.path.exists(clangxx):
+        clangxx = "/opt/rocm/lib/llvm/bin/clang++"
+    _run([clangxx, "-O1", "-g", "-std=c++17", *SANITIZE, f"-I{INCLUDE}", HOST_CHECKS_SRC, "-o", exe,
+          f"-L{out_dir}", "-lspecverify", f"-Wl,-rpath,{out_dir}"])
+    return exe
+
