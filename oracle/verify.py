@@ -160,8 +160,9 @@ def row_stats(z, T: float = 1.0, tokens=None) -> dict:
     m = s.max(axis=-1)
     lse = m + np.log(np.exp(s - m[..., None]).sum(axis=-1))
     top2 = -np.sort(-z, axis=-1)[..., :2]
-    out = {"lse": lse, "argmax": z.argmax(axis=-1), "gap": top2[..., 0] - top2[..., 1],
-           "zmax": top2[..., 0]}
+    # one token: no second logit, so the margin is unbounded (no near tie can occur)
+    gap = top2[..., 0] - top2[..., 1] if z.shape[-1] > 1 else np.full(z.shape[:-1], np.inf)
+    out = {"lse": lse, "argmax": z.argmax(axis=-1), "gap": gap, "zmax": top2[..., 0]}
     if tokens is not None:
         out["z_x"] = np.take_along_axis(z, np.asarray(tokens)[..., None], axis=-1)[..., 0]
     return out

@@ -428,3 +428,24 @@ def test_scheduled_zero_length_request_samples_first_row():
     v, _, _ = oracle.inverse_cdf(p1, coins[0, Kmax])
     assert r["emitted"][0, 0] == v
     assert np.all(r["emitted"][0, 1:] == -1)
+
+
+def test_one_token_vocabulary_accepts_everything():
+    """V = 1: p = q = 1 at every position, so every draft passes (u < 1), the bonus token
+    is token 0, tau = K + 1, and the greedy margin (top-1 minus top-2) has no second
+    logit: it is unbounded, never a near tie (reading R6)."""
+    rng = np.random.default_rng(5)
+    B, K, d = 3, 4, 8
+    W = oracle.Weights(rng.normal(size=(1, d)))
+    h = rng.normal(size=(B, K + 1, d))
+    hd = rng.normal(size=(B, K, d))
+    draft = np.zeros((B, K), dtype=np.int64)
+    coins = rng.random((B, K + 1))
+    s = oracle.verify_sample(W, h, hd, draft, coins, 1.0)
+    assert np.all(s["accepted"] == K) and np.all(s["emitted"] == 0) and s["tau"] == K + 1
+    g = oracle.verify_greedy(W, h, draft)
+    assert np.all(g["accepted"] == K) and np.all(g["emitted"] == 0)
+    assert np.all(np.isinf(oracle.row_stats(h @ W.w_lm.T)["gap"]))
+    # two tokens: the margin is the plain difference of the two logits
+    z = rng.normal(size=(4, 2))
+    np.testing.assert_array_equal(oracle.row_stats(z)["gap"], np.abs(z[:, 0] - z[:, 1]))
