@@ -77,6 +77,7 @@ __global__ __launch_bounds__(512) void k_stream(const GemmArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int M = live_rows(a);
   if (M < 0) return;  // another launch of the same product does the work
+  if (a.nslots_out && blockIdx.x == 0 && threadIdx.x == 0) *a.nslots_out = a.nslots_plan;
   const int N = a.N;
   const int nks = a.K >> 5;
   const int nch = (nks + CHUNK_KS - 1) / CHUNK_KS;

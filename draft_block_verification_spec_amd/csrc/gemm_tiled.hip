@@ -228,6 +228,7 @@ void k_tiled(const GemmArgs a) {
   const int wm = wave >> 1, wn = wave & 1;
   const int M = live_rows(a);
   if (M < 0) return;  // another launch of the same product does the work
+  if (a.nslots_out && blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0) *a.nslots_out = a.nslots_plan;
   const int Ncols = PAIR ? 2 * a.N : a.N;  // columns of the weight-row space
   // Only row tiles that hold rows are walked: with a device-side row count below a.M the
   // live tiles still spread over every workgroup (skipping the dead ones in place would

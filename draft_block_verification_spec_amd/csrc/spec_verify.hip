@@ -126,7 +126,7 @@ struct Plan {
   Gemm gu_lo, dn_lo, lm_lo;
   size_t o_a = 0, o_y = 0, o_part = 0, o_parts = 0, o_parts_d = 0, o_logits = 0, o_logits_d = 0,
          o_jobs = 0, o_sums = 0, o_conf = 0, o_vlen = 0, o_rowoff = 0, o_rowmap = 0, o_mtot = 0,
-         o_hp = 0, o_sync = 0, o_lse = 0, o_tree = 0, total = 0;
+         o_hp = 0, o_sync = 0, o_lse = 0, o_tree = 0, o_nslots = 0, total = 0;
   bool small_tail = false;  // B*(K+1) <= 32: acceptance in every chunk block, then the draw
 };
 
@@ -157,20 +157,39 @@ bool fp8_ok(const Gemm &g, int N) {
 // plans (256-row tiles at a 512-row budget) run far below their rate when few rows pass
 // the threshold.  Plans for at most SMALL_ROWS rows are kept beside them when the
 // budget-sized LM head uses taller tiles; both are launched and the device-side count
-// lets exactly one of each pair work.  Both LM-head plans write the same statistics
-// slots (same column tiles).
+// lets exactly one of each pair work.  The LM-head launch that works writes its plan's
+// statistics slot count for the acceptance kernel, so the two plans may tile the
+// columns differently.
 constexpr int SMALL_ROWS = 128;
-bool plan_small_rows(Plan &p, int V) {
-  if (p.budget <= SMALL_ROWS || p.lm.stream || p.lm.n_split > 0 || p.lm.shape.bm <= SMALL_ROWS) return false;
-  Gemm lo = choose(SMALL_ROWS, V, p.d, EPI_LOGITS);
-  if (lo.stream) return false;
-  if (lo.shape.bn != p.lm.shape.bn) {
-    if (p.lm.shape.bn == 256) lo.shape = TileShape{128, 256, 64, 3};
-    else if (p.lm.shape.bn == 128) lo.shape = TileShape{128, 128, 64, 4};
-    else return false;
-    lo.nslots = tiled_slots(V, lo.shape.bn);
+
+// LM head for at most SMALL_ROWS rows: whole rounds of 128 x 256 tiles over the CUs, the
+// remaining columns as 128 x 128 tiles in a second launch (a last round of 256-column
+// tiles a third full would cost nearly a whole round).
+Gemm small_lm_plan(int V, int d) {
+  Gemm g = choose(SMALL_ROWS, V, d, EPI_LOGITS);
+  if (g.stream) return g;
+  const TileShape wide{128, 256, 64, 3}, narrow{128, 128, 64, 4};
+  const long slots = (long)tiled_per_cu(wide) * num_cus();
+  const long tiles = (V + 255) / 256;
+  const long full = slots > 0 ? tiles / slots : 0;
+  g.shape = wide;
+  g.n_split = 0;
+  g.nslots = tiled_slots(V, 256);
+  if (full >= 1 && tiles % slots > 0) {
+    const long n1 = full * slots * 256;
+    if (n1 < V) {
+      g.n_split = (int)n1;
+      g.shape2 = narrow;
+      g.nslots = tiled_slots((int)n1, 256) + tiled_slots(V - (int)n1, 128);
+    }
   }
-  if (lo.n_split > 0 || lo.nslots != p.lm.nslots) return false;
+  return g;
+}
+
+bool plan_small_rows(Plan &p, int V) {
+  if (p.budget <= SMALL_ROWS || p.lm.stream || p.lm.shape.bm <= SMALL_ROWS) return false;
+  const Gemm lo = small_lm_plan(V, p.d);
+  if (lo.stream) return false;
   if (p.d_ff > 0) {
     p.gu_lo = choose(SMALL_ROWS, p.d_ff, p.d, EPI_SWIGLU);
     p.dn_lo = choose(SMALL_ROWS, p.d, p.d_ff, EPI_RESID);
@@ -228,7 +247,8 @@ bool make_plan(int mode, int B, int K, const sv_weights *w, int budget, Plan &p)
     if (p.dn_lo.partial_floats > part_floats) part_floats = p.dn_lo.partial_floats;
   }
   if (part_floats) p.o_part = take(sizeof(float) * part_floats);
-  p.o_parts = take(sizeof(StatPart) * (size_t)p.M_lm * p.lm.nslots);
+  const int nslots_max = p.m_split > 0 && p.lm_lo.nslots > p.lm.nslots ? p.lm_lo.nslots : p.lm.nslots;
+  p.o_parts = take(sizeof(StatPart) * (size_t)p.M_lm * nslots_max);
   const int NJ = B * (K + 1);
   if (mode != SV_MODE_GREEDY) {
     p.small_tail = NJ <= SMALL_TAIL_JOBS;
@@ -251,6 +271,7 @@ bool make_plan(int mode, int B, int K, const sv_weights *w, int budget, Plan &p)
     p.o_rowoff = take(sizeof(int32_t) * (size_t)(B + 1));
     p.o_rowmap = take(sizeof(int32_t) * (size_t)p.budget);
     p.o_mtot = take(sizeof(int32_t));
+    p.o_nslots = take(sizeof(int32_t));
     p.o_hp = take(2 * (size_t)p.budget * d);
   }
   p.total = off;
@@ -299,6 +320,7 @@ hipError_t run_gemm(const Gemm &g, GemmArgs a, int epi, hipStream_t st) {
     }
     a2.status_reset = nullptr;
     a2.counter_reset = nullptr;
+    a2.nslots_out = nullptr;
     return launch_gemm_tiled(a2, epi, g.shape2, 1, st);
   }
   if (g.splits > 1) {
@@ -588,17 +610,23 @@ SV_API int spec_verify_scheduled(const sv_weights *w, const uint16_t *h, const u
   g.parts = at<StatPart>(ws, p.o_parts); g.nslots = p.lm.nslots;
   g.invT = invT; g.want_s = 1;
   int32_t *sync = at<int32_t>(ws, p.o_sync);
+  int32_t *nslots_dev = nullptr;
   if (ms > 0) {
+    // each plan's launch that works reports its slot count to the acceptance kernel
+    nslots_dev = at<int32_t>(ws, p.o_nslots);
     GemmArgs gl = g;
     gl.M = ms; gl.m1 = ms; gl.m_hi = ms;
+    gl.nslots = p.lm_lo.nslots;
+    gl.nslots_out = nslots_dev; gl.nslots_plan = p.lm_lo.nslots;
     SV_CHECK(run_gemm(p.lm_lo, gl, EPI_LOGITS, st));
     g.m_lo = ms;
+    g.nslots_out = nslots_dev; g.nslots_plan = p.lm.nslots;
   }
   SV_CHECK(run_gemm(p.lm, g, EPI_LOGITS, st));
   // S6-S9
   AcceptArgs a = {};
   a.B = B; a.K = Kmax; a.V = p.V; a.invT = invT;
-  a.parts_t = g.parts; a.nslots_t = p.lm.nslots;
+  a.parts_t = g.parts; a.nslots_t = p.lm.nslots; a.nslots_t_dev = nslots_dev;
   a.parts_d = parts_d; a.nslots_d = p.s1.nslots;
   a.logits_t = logits_t; a.logits_d = logits_d;
   a.draft = draft; a.u = u; a.verify_len = vlen; a.row_off = rowoff;

@@ -44,6 +44,10 @@ struct GemmArgs {
   // With M_dev: the launch does its work only when m_lo < *M_dev and, if m_hi > 0,
   // *M_dev <= m_hi (a plan for few rows and one for many, both launched, one working)
   int m_lo, m_hi;
+  // EPI_LOGITS: when set, the launch that does the work writes nslots_plan (the statistics
+  // slots per row of the whole product, all launches of its plan) here
+  int32_t *nslots_out;
+  int nslots_plan;
   int N;             // output columns (for SWIGLU: columns of a)
   int K;             // reduction length, multiple of 64
   const uint16_t *w;   // [N, K] (SWIGLU: gate rows)
@@ -120,6 +124,7 @@ struct AcceptArgs {
   float invT;
   const StatPart *parts_t;  // target-row partials [rows][nslots_t]
   int nslots_t;
+  const int32_t *nslots_t_dev;  // when set, nslots_t as written by the LM-head launch that ran
   const StatPart *parts_d;  // draft-row partials [B*K][nslots_d]
   int nslots_d;
   const float *logits_t;  // target logits (packed rows in scheduled mode), row stride V

@@ -143,6 +143,7 @@ __global__ __launch_bounds__(1024) void k_accept_sample(const AcceptArgs a) {
   const int Kb = a.verify_len ? a.verify_len[b] : Kmax;
   const long trow0 = a.row_off ? a.row_off[b] : (long)b * (Kmax + 1);
   const long drow0 = (long)b * Kmax;
+  const int nslots_t = a.nslots_t_dev ? *a.nslots_t_dev : a.nslots_t;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float *lse_t = sm;                  // [Kmax+1]
   float *lse_d = sm + (Kmax + 1);     // [Kmax]
@@ -172,8 +173,8 @@ __global__ __launch_bounds__(1024) void k_accept_sample(const AcceptArgs a) {
   for (int r = wave; r < nrows; r += nw) {
     const bool is_t = r <= Kb;
     const int j = is_t ? r : r - Kb - 1;
-    const StatPart *pp = is_t ? a.parts_t + (trow0 + j) * a.nslots_t : a.parts_d + (drow0 + j) * a.nslots_d;
-    const StatPart st = wave_merge_row<12>(pp, is_t ? a.nslots_t : a.nslots_d, a.invT, true);
+    const StatPart *pp = is_t ? a.parts_t + (trow0 + j) * nslots_t : a.parts_d + (drow0 + j) * a.nslots_d;
+    const StatPart st = wave_merge_row<12>(pp, is_t ? nslots_t : a.nslots_d, a.invT, true);
     const float lse = st.b1 * a.invT + __logf(st.s);
     if (lane == 0) {
       if (is_t) lse_t[j] = lse; else lse_d[j] = lse;
