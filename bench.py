@@ -15,7 +15,7 @@ The headline workload is the 16-token block (B=1, K=15, d=4096, d_ff=12288, V=15
 T=1 sampled); `value` is verified positions per second (B*(K+1) target rows per step).
 Rank 0 prints one JSON line.  Extra points (greedy at B=1; FP8 weights; the greedy batch
 sweep at B=1, 8, 32, 128 with K=7; the confidence-scheduled step, literal and
-budget-binding; the block as a candidate tree; commit; the wide model) are reported under
+budget-binding; the block as a candidate tree; the drafter step; commit; the wide model) are reported under
 "extra", each with its own roofline.  The fp64 oracle is timed on the host cores for the
 headline and for the B=128, scheduled and wide points (`cpu_baseline`), and gives the
 closed-form expected tau of the sampled points' input sets beside the measured one.
@@ -346,6 +346,11 @@ def main():
             extra.append(bench_tree(bd, torch, wl, wk, sets, w_main, dev, to_bf16, to_i32, to_f32, mt, timed,
                                     tau_stats, args, peaks_m))
             log(f"block16 tree {mt}: {extra[-1]['ms_per_step']:.3f} ms/step, tau {extra[-1]['tau']:.2f}")
+        # the drafter step that makes the block's drafts: 15 draft rows through the shared head
+        for mp in ("sample", "greedy"):
+            extra.append(bench_propose(bd, torch, wk, sets, w_main, dev, to_bf16, to_f32, mp, args.steps,
+                                       args.warmup, peaks_m))
+            log(f"drafter step {mp}: {extra[-1]['ms_per_call'] * 1e3:.1f} us/call")
         # commit after verification: the scheduled batch (B = 64, Kmax = 15) with tree-shaped
         # blocks on a hybrid target (8 attention layers x 2 KiB entries, 1 MiB recurrent state)
         extra.append(bench_commit(bd, torch, wl, dev, to_i32, args.steps, args.warmup, peaks_m))
@@ -426,6 +431,49 @@ def bench_tree(bd, torch, wl, wk, sets, w, dev, to_bf16, to_i32, to_f32, mode, t
     pt.update({k: ts[k] for k in ("tau", "tau_ci95", "tau_sets", "input_sets")})
     pt["roofline"] = roofline(b_lm, 2.0 * rows_lm * d * V, lm, peaks_m, f"LM-head GEMM over {rows_lm} rows")
     return pt
+
+
+def bench_propose(bd, torch, wk, sets, w, dev, to_bf16, to_f32, mode, steps, warmup, peaks_m):
+    """spec_draft_propose on the block's K draft rows (the drafter step that makes the
+    drafts): the shared LM head over K rows, then a draw from q at T (sampled) or the argmax
+    (greedy).  Algorithmic bytes: W_lm once plus the K activation rows.  The input sets
+    rotate through the calls; each call is timed with its own events."""
+    K, V, d = wk.K, wk.V, wk.d
+    rows = wk.B * K
+    T = wk.T if mode == "sample" else 0.0
+    ws = bd.workspace(bd.SV_MODE_PROPOSE, rows, 0, w, dev)
+    xo = torch.empty(rows, dtype=torch.int32, device=dev)
+    co = torch.empty(rows, dtype=torch.float32, device=dev)
+    ins = [(to_bf16(dc["h_draft"]).reshape(rows, d).contiguous(),
+            to_f32(dc["draft_coins"]).reshape(-1).contiguous() if T > 0 else None) for dc in sets]
+
+    def call(i):
+        hd, cn = ins[i % len(ins)]
+        bd.spec_draft_propose(w, hd, cn, T, draft_out=xo, conf_out=co, ws=ws)
+    t0 = time.time()
+    n = 0
+    while time.time() - t0 < 0.3:  # clock settle, as for the other points
+        for _ in range(16):
+            call(n)
+            n += 1
+        torch.cuda.synchronize()
+    for i in range(warmup):
+        call(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (e0, e1) in enumerate(evs):
+        e0.record()
+        call(i)
+        e1.record()
+    torch.cuda.synchronize()
+    per = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    ms = float(per.mean())
+    by = 2.0 * V * d + 2.0 * rows * d
+    return {"workload": f"drafter step ({mode}): {rows} draft rows of block16 through the shared LM head, "
+                        f"V={V} d={d}" + (f" T={T}" if T > 0 else ""),
+            "ms_per_call": ms, "call_ms_spread": {"median": float(np.median(per)), "min": float(per.min()),
+                                                  "max": float(per.max())},
+            "bytes_per_call": by,
+            "roofline": roofline(by, 2.0 * rows * d * V, ms, peaks_m, "whole call (LM head over the draft rows + draw)")}
 
 
 def bench_commit(bd, torch, wl, dev, to_i32, steps, warmup, peaks_m):
