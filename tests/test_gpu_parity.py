@@ -421,3 +421,44 @@ def test_deterministic_and_optional_outputs():
     assert torch.equal(o1.emitted, o2.emitted) and torch.equal(o1.emitted, o3.emitted)
     assert torch.equal(o1.accepted_len, o3.accepted_len)
     assert torch.equal(o1.diag.nan_to_num(), o2.diag.nan_to_num())
+
+
+def test_scheduled_workspace_reuse_across_plans():
+    """One workspace and one set of outputs for calls that alternate between the two
+    plans of the verify pass (105 rows verified: the plans for at most 128 rows work;
+    142 rows: the budget-sized ones): every call is bit-identical to the same call on a
+    fresh workspace, so nothing a previous call left behind (statistics slots, the slot
+    count the LM head reports, partials) leaks into the next."""
+    data = wl.generate(SCHED_LOOSE)
+    W = oracle.Weights.from_bits(data)
+    w = pt.dev_weights(data)
+    T = SCHED_LOOSE.T
+    draft = _i32(pt.oracle_drafts(W, data, T)["draft"])
+    h, hd, u = pt.dev_bf16(data["h"]), pt.dev_bf16(data["h_draft"]), _f32(data["coins"])
+    B, K = SCHED_LOOSE.B, SCHED_LOOSE.K
+    ws = bd.workspace(bd.SV_MODE_SCHEDULED, B, K, w, h.device)
+    out = bd.make_outputs(B, K, h.device, mode=bd.SV_MODE_SCHEDULED, V=SCHED_LOOSE.V, d=SCHED_LOOSE.d, diag=True,
+                          logits=True)
+    for thr in (0.5, 0.3, 0.5, 0.3):
+        fresh = bd.spec_verify_scheduled(w, h, hd, draft, u, T, thr, SCHED_LOOSE.budget, diag=True, logits=True)
+        bd.spec_verify_scheduled(w, h, hd, draft, u, T, thr, SCHED_LOOSE.budget, out=out, ws=ws)
+        torch.cuda.synchronize()
+        assert int(out.dev_status.item()) == bd.SV_DEV_OK
+        vl = out.verify_len.cpu().numpy()
+        rows = int((vl + 1).sum())
+        assert (64 < rows <= 128) if thr == 0.5 else (rows > 128), rows
+        assert torch.equal(out.verify_len, fresh.verify_len)
+        assert torch.equal(out.accepted_len, fresh.accepted_len)
+        assert torch.equal(out.emitted, fresh.emitted)
+        assert torch.equal(out.counters, fresh.counters)
+        # every draft row is written by each call; target rows up to each request's
+        # verified length (the rest of the reused outputs keep an earlier call's values)
+        nt = B * (K + 1)
+        assert torch.equal(out.diag[nt:].nan_to_num(), fresh.diag[nt:].nan_to_num())
+        assert torch.equal(out.logits[nt:], fresh.logits[nt:])
+        dt_o, dt_f = out.diag[:nt].view(B, K + 1, -1), fresh.diag[:nt].view(B, K + 1, -1)
+        lt_o, lt_f = out.logits[:nt].view(B, K + 1, -1), fresh.logits[:nt].view(B, K + 1, -1)
+        for b in range(B):
+            k = int(vl[b]) + 1
+            assert torch.equal(dt_o[b, :k].nan_to_num(), dt_f[b, :k].nan_to_num())
+            assert torch.equal(lt_o[b, :k], lt_f[b, :k])
