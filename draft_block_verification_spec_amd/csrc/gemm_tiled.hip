@@ -3,8 +3,8 @@
 // Once B*(K+1) rows share each weight read the verification pass stops being
 // bound by HBM and becomes compute-bound (Wildberries page, "A bit of theory",
 // Statement 3: under load the step time grows with B*(K+1)).  Each 256-thread
-// workgroup (2 x 2 waves) owns a BM x BN output tile and walks k in 64-wide
-// slices.  Both operand slices travel from global memory straight into LDS with
+// workgroup (2 x 2 waves, or 1 x 4 for 160-row tiles) owns a BM x BN output tile and
+// walks k in 64-wide slices.  Both operand slices travel from global memory straight into LDS with
 // global_load_lds_dwordx4 (no staging registers), NS slices deep, so the loads of
 // future slices run under the MFMAs of the current one.  Inside a row the sixteen-
 // byte chunks are XOR-swizzled so the 128-bit operand reads of
@@ -53,6 +53,16 @@ __device__ __forceinline__ void vm_wait() {
 }
 __device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// The four waves of a workgroup as a grid over the tile: 2 x 2 when the rows split into
+// two 32-row-aligned halves, otherwise 1 x 4 (all rows, a quarter of the columns each),
+// which lets a row tile hold 32 * odd rows (160 rows: 288 rows in two row tiles).
+template <int BM, int BN>
+struct WaveGrid {
+  static constexpr int WN = BM % 64 == 0 ? 2 : 4, WM = 4 / WN;
+  static constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles of whole 32 x 32 blocks");
+};
+
 // Waves per SIMD the kernel is compiled for: one where the slice pipeline's LDS already
 // holds the CU to one workgroup (the 192-row shape among them), and for 256 x 256 tiles,
 // whose accumulators need the whole register file; two otherwise.
@@ -61,12 +71,14 @@ constexpr int waves_per_eu() {
   return (BM * BN >= 256 * 256 || BM == 192 || (160 * 1024) / (NS * (BM + BN) * BK * 2) < 2) ? 1 : 2;
 }
 
-// The epilogue of one BM x BN tile, run by the four MFMA waves (2 x 2, wave (wm, wn) owns
-// rows wm*BM/2.. and columns wn*BN/2..) straight from their accumulators.
+// The epilogue of one BM x BN tile, run by the four MFMA waves (wave (wm, wn) of the
+// wave grid owns rows wm*WTM.. and columns wn*WTN..) straight from their accumulators.
 template <int BM, int BN, int EPI, bool PAIR>
-__device__ __forceinline__ void tile_epilogue(const GemmArgs &a, f32x16 (&acc)[BM / 64][BN / 64], int m0, int n0,
-                                              int tni, int wm, int wn, int lane, int M, int Ncols, int z) {
-  constexpr int WTM = BM / 2, WTN = BN / 2, TM = WTM / 32, TN = WTN / 32;
+__device__ __forceinline__ void tile_epilogue(const GemmArgs &a,
+                                              f32x16 (&acc)[WaveGrid<BM, BN>::TM][WaveGrid<BM, BN>::TN], int m0,
+                                              int n0, int tni, int wm, int wn, int lane, int M, int Ncols, int z) {
+  using WG = WaveGrid<BM, BN>;
+  constexpr int WTM = WG::WTM, WTN = WG::WTN, TM = WG::TM, TN = WG::TN;
   const int l32 = lane & 31, hi = lane >> 5;
   // ---- epilogue.  Lane l of block (i, j) holds column l%32 and, for register r,
   // row (r/4)*8 + (l/32)*4 + r%4 of the 32x32 block.
@@ -126,7 +138,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs &a, f32x16 (&acc)[B
     // statistics over all of the wave's columns.
     const bool ws = a.want_s != 0;
     const float invT = a.invT;
-    const int pslot = tni * 2 + wn;
+    const int pslot = tni * WG::WN + wn;
     const int nb = n0 + wn * WTN + l32;
     if (a.logits) {
       // row bases are wave-uniform; the lane part (row half, column) is an offset
@@ -212,7 +224,8 @@ void k_tiled(const GemmArgs a) {
   constexpr int RB = Slice<BK>::RB, CPR = Slice<BK>::CPR, RPI = Slice<BK>::RPI;
   constexpr int SA = BM * RB, SB = BN * RB, SS = SA + SB;  // bytes of one slice
   constexpr int IA = BM / RPI / 4, IB = BN / RPI / 4;      // 1 KB loads per wave per slice
-  constexpr int WTM = BM / 2, WTN = BN / 2, TM = WTM / 32, TN = WTN / 32;
+  using WG = WaveGrid<BM, BN>;
+  constexpr int WTM = WG::WTM, WTN = WG::WTN, TM = WG::TM, TN = WG::TN;
   constexpr int KS = BK / 16;
   static_assert(IA >= 1 && IB >= 1, "tile too small");
   static_assert(NS >= 2 && (NS - 1) * (IA + IB) < 64, "slice pipeline depth");
@@ -225,7 +238,7 @@ void k_tiled(const GemmArgs a) {
     for (int i = threadIdx.x; i < max(1, a.counter_reset_n); i += blockDim.x) a.counter_reset[i] = 0;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WG::WN, wn = wave % WG::WN;
   const int M = live_rows(a);
   if (M < 0) return;  // another launch of the same product does the work
   if (a.nslots_out && blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0) *a.nslots_out = a.nslots_plan;
@@ -432,7 +445,7 @@ hipError_t launch_shape(const GemmArgs &a, int epi, int splits, hipStream_t st) 
 
 }  // namespace
 
-int tiled_slots(int N, int bn) { return ((N + bn - 1) / bn) * 2; }
+int tiled_slots(int N, const TileShape &sh) { return ((N + sh.bn - 1) / sh.bn) * (sh.bm % 64 == 0 ? 2 : 4); }
 
 // Shapes measured best on MI355X for the row counts of the verification step (LM head,
 // gate/up, down at d = 4096 and 8192): the fewer the rows, the more of each slice is
@@ -441,6 +454,15 @@ TileShape tiled_shape(int M, int N, int K, int epi) {
   const bool k128 = K % 128 == 0;
   if (epi == EPI_SWIGLU) {
     if (M <= 128) return TileShape{128, 128, 64, 4};
+    // 129-160 rows: 160 x 256 tiles move 52 KiB per slice against 40 KiB for 192 x 128
+    // ones but cover twice the columns; taken when that needs fewer slice-rounds over the
+    // CUs (d_ff = 28672: one round against two, step 0.80 -> 0.77 ms; d_ff = 12288: one
+    // round either way, 192 x 128 keeps 192 CUs busy instead of 96)
+    if (M <= 160) {
+      const long cus = num_cus();
+      const long r160 = ((2L * N + 255) / 256 + cus - 1) / cus, r192 = ((2L * N + 127) / 128 + cus - 1) / cus;
+      if (13 * r160 < 10 * r192) return TileShape{160, 256, 64, 3};
+    }
     // one row tile, at most a third empty (160 rows at d = 8192: 219 us against 239 us
     // for 256 x 256 tiles)
     if (M <= 192) return TileShape{192, 128, 64, 3};
@@ -461,9 +483,15 @@ TileShape tiled_shape(int M, int N, int K, int epi) {
   }
   // (a single 320 x 128 row tile at 288 rows measured 9% slower than three 128 x 256 ones;
   // at 256 rows two 128 x 256 row tiles beat one 256 x 128 row tile by 4% of the step)
+  // 129-160 and 257-320 rows: one or two row tiles of 160 x 256 (160 rows: LM head
+  // 0.55 -> 0.44 ms for the d = 8192 model, 364 -> 358 us at d = 4096; 288 rows: 0.86 ->
+  // 0.76 ms against three 128 x 256 row tiles)
   if (M <= 64) return k128 ? TileShape{64, 128, 128, 3} : TileShape{64, 128, 64, 2};
   if (M <= 128) return TileShape{128, 128, 64, 4};
+  if (M <= 160) return TileShape{160, 256, 64, 3};
   if (M <= 192) return TileShape{256, 128, 64, 3};
+  if (M <= 256) return TileShape{128, 256, 64, 3};
+  if (M <= 320) return TileShape{160, 256, 64, 3};
   if (M <= 384) return TileShape{128, 256, 64, 3};
   return TileShape{256, 256, 64, 2};
 }
@@ -475,6 +503,7 @@ TileShape tiled_shape(int M, int N, int K, int epi) {
   X(192, 128, 64, 3)      \
   X(256, 128, 64, 3)      \
   X(128, 256, 64, 3)      \
+  X(160, 256, 64, 3)      \
   X(256, 256, 64, 2)
 
 int tiled_per_cu(const TileShape &sh) {

@@ -95,7 +95,7 @@ Gemm choose(int M, int N, int K, int epi) {
     }
   }
   if (epi == EPI_LOGITS) {
-    g.nslots = tiled_slots(N, g.shape.bn);
+    g.nslots = tiled_slots(N, g.shape);
     // A last round of 256 x 256 tiles at most half full would cost a whole round: its
     // columns go to a second launch of 256 x 128 tiles that fits in one round (half the
     // work per tile).  Measured at 1024 rows: 9.28 rounds -> 9 + one half-size round.
@@ -108,7 +108,7 @@ Gemm choose(int M, int N, int K, int epi) {
         const long tiles2 = tm * ((N - n1 + 127) / 128);
         if (n1 < N && nt * tm == tiles && tiles2 <= (long)tiled_per_cu(g.shape2) * num_cus()) {
           g.n_split = (int)n1;
-          g.nslots = tiled_slots((int)n1, 256) + tiled_slots(N - (int)n1, 128);
+          g.nslots = tiled_slots((int)n1, g.shape) + tiled_slots(N - (int)n1, g.shape2);
         }
       }
     }
@@ -174,13 +174,13 @@ Gemm small_lm_plan(int V, int d) {
   const long full = slots > 0 ? tiles / slots : 0;
   g.shape = wide;
   g.n_split = 0;
-  g.nslots = tiled_slots(V, 256);
+  g.nslots = tiled_slots(V, wide);
   if (full >= 1 && tiles % slots > 0) {
     const long n1 = full * slots * 256;
     if (n1 < V) {
       g.n_split = (int)n1;
       g.shape2 = narrow;
-      g.nslots = tiled_slots((int)n1, 256) + tiled_slots(V - (int)n1, 128);
+      g.nslots = tiled_slots((int)n1, wide) + tiled_slots(V - (int)n1, narrow);
     }
   }
   return g;
@@ -315,7 +315,7 @@ hipError_t run_gemm(const Gemm &g, GemmArgs a, int epi, hipStream_t st) {
       a2.out = a.out + g.n_split;
     } else {
       if (a.logits) a2.logits = a.logits + g.n_split;
-      a2.parts = a.parts + tiled_slots(g.n_split, g.shape.bn);
+      a2.parts = a.parts + tiled_slots(g.n_split, g.shape);
       a2.n_off = a.n_off + g.n_split;
     }
     a2.status_reset = nullptr;

@@ -107,7 +107,9 @@ TileShape tiled_shape(int M, int N, int K, int epi);
 // Workgroups of a shape resident per CU (LDS and waves per SIMD).
 int tiled_per_cu(const TileShape &sh);
 hipError_t launch_gemm_tiled(const GemmArgs &a, int epi, const TileShape &sh, int splits, hipStream_t st);
-int tiled_slots(int N, int bn);
+// Statistics slots per row of an EPI_LOGITS launch over N columns (one per column tile
+// and wave column).
+int tiled_slots(int N, const TileShape &sh);
 hipError_t launch_splitk_reduce(const GemmArgs &a, int epi, int splits, int bn, hipStream_t st);
 
 // End-of-call bookkeeping (tau and counters), run by the last block of the last kernel.

@@ -211,3 +211,33 @@ def test_wide_sample_sampled_requests():
         rows = _final_rows(lg, B, K, wk.T)(b, K)
         pt.assert_decisions(ref, acc[sl], em[sl], lambda _b: pt.first_diff_sample(ref, A, em[b], 0, coins[sl], K, rows),
                             f"wide request {b}")
+
+
+def test_wide_greedy_sampled_requests():
+    """The wide model greedy: 160 rows, so gate/up and the LM head run on 160 x 256 tiles
+    (waves side by side); logits of sampled requests and every decision checked."""
+    wk = wl.WIDE
+    data, W, w = _setup(wk)
+    B, K = wk.B, wk.K
+    x_gpu, _ = bd.spec_draft_propose(w, pt.dev_bf16(data["h_draft"]), None, 0.0)
+    out = bd.spec_verify_greedy(w, pt.dev_bf16(data["h"]), x_gpu.contiguous(), diag=True, logits=True)
+    torch.cuda.synchronize()
+    assert int(out.dev_status.item()) == 0
+    draft = x_gpu.cpu().numpy().astype(np.int64)
+    lg = out.logits.cpu().numpy()
+    acc, em = out.accepted_len.cpu().numpy(), out.emitted.cpu().numpy()
+    for b in (0, 17, B - 1):
+        sl = slice(b, b + 1)
+        ref = oracle.verify_greedy(W, oracle.from_bf16_bits(data["h"][sl]), draft[sl])
+        _check_rows(lg[b * (K + 1):(b + 1) * (K + 1)], ref["logits_t"][0])
+        gap = ref["gap_t"]
+
+        def classify(_b, b=b, ref=ref, gap=gap):
+            j = min(int(acc[b]), int(ref["accepted"][0]))
+            if gap[0, j] < pt.GAP_BAND:
+                pt.note("argmax_gap")
+                return None
+            return f"wide greedy request {b} row {j}"
+
+        pt.count_bands(ref, None, "greedy")
+        pt.assert_decisions(ref, acc[sl], em[sl], classify, f"wide greedy request {b}")

@@ -63,15 +63,17 @@ def _run_sample(wk, rep=0, check_hidden=True, fp8=False):
     assert err <= pt.LOGIT_TOL, f"logit error {err}"
     if check_hidden and wk.d_ff > 0:
         pt.check_hidden(out.hidden, ref["y"], W, h64)
-    # p(x) on target rows j < K and q(x) on draft rows
+    # p(x) on target rows j < K, q(x) and the confidence on draft rows
     dg = out.diag.cpu().numpy().astype(np.float64)
     dt = dg[: B * (K + 1)].reshape(B, K + 1, -1)
     dd = dg[B * (K + 1):].reshape(B, K, -1)
-    assert np.abs(dt[:, :K, 5] - ref["p_x"]).max() <= pt.PROB_TOL
-    assert np.abs(dd[:, :, 5] - ref["q_x"]).max() <= pt.PROB_TOL
-    assert np.abs(dt[:, :, 0] - ref["lse_t"]).max() <= 1e-3
-    assert np.abs(dd[:, :, 0] - ref["lse_d"]).max() <= 1e-3
-    np.testing.assert_allclose(dd[:, :, 6], ref["conf"], atol=pt.PROB_TOL)
+    rt = (np.arange(B)[:, None] * (K + 1) + np.arange(K)[None, :]).ravel()
+    rd = B * (K + 1) + np.arange(B * K)
+    pt.check_probs(dt[:, :K, 5], lg[rt], ref_lg[rt], draft, ref["p_x"], T, "p(x)")
+    pt.check_probs(dd[:, :, 5], lg[rd], ref_lg[rd], draft, ref["q_x"], T, "q(x)")
+    pt.check_probs(dd[:, :, 6], lg[rd], ref_lg[rd], None, ref["conf"], T, "confidence")
+    pt.check_lse(dt[:, :, 0], lg[: B * (K + 1)], ref_lg[: B * (K + 1)], ref["lse_t"], T, "target lse")
+    pt.check_lse(dd[:, :, 0], lg[rd], ref_lg[rd], ref["lse_d"], T, "draft lse")
     # decisions
     acc = out.accepted_len.cpu().numpy()
     em = out.emitted.cpu().numpy()
@@ -139,7 +141,8 @@ def _run_greedy(wk, rep=0, fp8=False):
 
 # Two reduced shapes aimed at tiling paths of the larger-batch GEMMs:
 #  * 20 requests x 8 rows = 160 target rows: gate/up and down run on 192-row tiles (one row
-#    tile per column tile), the 300-row sampled LM head on 128 x 256 tiles;
+#    tile per column tile), the 300-row sampled LM head on two row tiles of 160 x 256
+#    (waves side by side, four statistics slots per column tile);
 #  * 128 requests x 8 rows = 1024 rows, V = 24000: 94 column tiles of 256 x 4 row tiles =
 #    376 tiles = one round of 256 + 120, so columns [0, 16384) run as 256 x 256 tiles and
 #    the ragged rest (7616 columns, 240 tiles of 256 x 128) as a second launch whose
@@ -159,6 +162,37 @@ def test_greedy_parity_160_rows():
 
 def test_greedy_parity_lm_head_in_two_launches():
     _run_greedy(LM_SPLIT)
+
+
+# The LM head at 257-320 rows runs on two row tiles of 160: sampled at 288 rows (the wide
+# model's shape: 32 requests, 4 drafts) and 258 rows (86 requests, one draft: the second
+# row tile 98 rows live); greedy at 320 rows (both row tiles full) and 288 rows.
+LM160 = [wl.Workload("lm160_288", 23, B=32, K=4, d=512, d_ff=1536, V=12347, T=0.7, sigma=0.6),
+         wl.Workload("lm160_320", 24, B=40, K=7, d=256, d_ff=512, V=5003, T=1.0, sigma=(0.3, 1.2)),
+         wl.Workload("lm160_258", 25, B=86, K=1, d=256, d_ff=512, V=4099, T=1.0, sigma=0.4)]
+
+
+# 160 rows with d_ff = 16896: gate/up on 160 x 256 tiles (one round of 132 tiles against
+# two rounds of 264 192 x 128 ones), the LM head on one 160-row tile.
+MLP160_FF = wl.Workload("mlp160_ff", 26, B=20, K=7, d=256, d_ff=16896, V=5003, T=1.0, sigma=(0.3, 1.2))
+
+
+def test_greedy_parity_160_rows_wide_ff():
+    _run_greedy(MLP160_FF)
+
+
+def test_sample_parity_160_rows_wide_ff():
+    _run_sample(MLP160_FF)
+
+
+@pytest.mark.parametrize("wk", [LM160[0], LM160[2]], ids=lambda w: w.name)
+def test_sample_parity_lm_head_160_row_tiles(wk):
+    _run_sample(wk)
+
+
+@pytest.mark.parametrize("B", [40, 36], ids=["320-rows", "288-rows"])
+def test_greedy_parity_lm_head_160_row_tiles(B):
+    _run_greedy(LM160[1].with_batch(B))
 
 
 @pytest.mark.parametrize("name", ["small", "small_wide", "small_batch", "tiny"])
@@ -281,6 +315,16 @@ def test_scheduled_parity_budget_160_few_rows():
     assert 64 < (vl + 1).sum() <= 128, (vl + 1).sum()
 
 
+# A binding 300-row budget: the budget-sized verify LM head runs on two row tiles of 160
+# (four statistics slots per column tile), the small plan beside it on 128-row tiles.
+SCHED_300 = replace(SCHED_200, name="sched_300", budget=300)
+
+
+def test_scheduled_parity_budget_300_binding():
+    vl = _run_scheduled(SCHED_300)
+    assert (vl + 1).sum() == 300
+
+
 def _run_scheduled(wk, expect_bound=True):
     data = wl.generate(wk)
     W = oracle.Weights.from_bits(data)
@@ -298,9 +342,10 @@ def _run_scheduled(wk, expect_bound=True):
     assert int(out.dev_status.item()) == bd.SV_DEV_OK
     dg = out.diag.cpu().numpy().astype(np.float64)
     dd = dg[B * (K + 1):].reshape(B, K, -1)
-    np.testing.assert_allclose(dd[:, :, 6], ref["conf"], atol=pt.PROB_TOL)
     lg = out.logits.cpu().numpy().astype(np.float64)
-    np.testing.assert_allclose(lg[B * (K + 1):], ref["logits_d"].reshape(-1, V), atol=pt.LOGIT_TOL, rtol=0)
+    ref_ld = ref["logits_d"].reshape(-1, V)
+    np.testing.assert_allclose(lg[B * (K + 1):], ref_ld, atol=pt.LOGIT_TOL, rtol=0)
+    pt.check_probs(dd[:, :, 6], lg[B * (K + 1):], ref_ld, None, ref["conf"], T, "confidence")
     vl = out.verify_len.cpu().numpy()
     same = _schedule_agrees(vl, ref, wk)
     assert (vl + 1).sum() <= wk.budget
