@@ -478,6 +478,12 @@ TileShape tiled_shape(int M, int N, int K, int epi) {
   }
   if (epi == EPI_RESID) {
     if (M <= 64) return k128 ? TileShape{64, 128, 128, 3} : TileShape{64, 128, 64, 2};
+    // 129-160 rows: 160 x 256 tiles when their split-K workgroups still fill the CUs
+    // (the wide model's 8192 outputs: 32 tiles x 8 splits), else one 192-row tile
+    if (M > 128 && M <= 160) {
+      const int maxs = K / 64 / 4 < 8 ? K / 64 / 4 : 8;
+      if ((long)((N + 255) / 256) * maxs >= num_cus()) return TileShape{160, 256, 64, 3};
+    }
     if (M > 128 && M <= 192) return TileShape{192, 128, 64, 3};  // 160 rows: 121 us against 149 us
     return M <= 256 ? TileShape{128, 256, 64, 3} : TileShape{256, 128, 64, 3};
   }
