@@ -429,14 +429,26 @@ hipError_t launch_shape(const GemmArgs &a, int epi, int splits, hipStream_t st) 
   const int slots = (per_cu<BM, BN, BK, NS>() * num_cus()) & ~7;
   if (splits == 1 && slots > 0 && tiles > slots) gx = slots;
   dim3 grd(gx, 1, splits), blk(256);
+  // paired gate/up tiles need whole 64-row (gate | up) groups per wave column
+  constexpr bool pair_ok = WaveGrid<BM, BN>::WTN % 64 == 0;
   if (splits > 1) {
-    if (epi == EPI_SWIGLU) hipLaunchKernelGGL((k_tiled<BM, BN, BK, NS, EPI_RAW, true>), grd, blk, 0, st, a);
-    else hipLaunchKernelGGL((k_tiled<BM, BN, BK, NS, EPI_RAW, false>), grd, blk, 0, st, a);
+    if constexpr (pair_ok) {
+      if (epi == EPI_SWIGLU) {
+        hipLaunchKernelGGL((k_tiled<BM, BN, BK, NS, EPI_RAW, true>), grd, blk, 0, st, a);
+        return hipGetLastError();
+      }
+    } else {
+      if (epi == EPI_SWIGLU) return hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL((k_tiled<BM, BN, BK, NS, EPI_RAW, false>), grd, blk, 0, st, a);
     return hipGetLastError();
   }
   switch (epi) {
     case EPI_LOGITS: hipLaunchKernelGGL((k_tiled<BM, BN, BK, NS, EPI_LOGITS, false>), grd, blk, 0, st, a); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((k_tiled<BM, BN, BK, NS, EPI_SWIGLU, true>), grd, blk, 0, st, a); break;
+    case EPI_SWIGLU:
+      if constexpr (pair_ok) hipLaunchKernelGGL((k_tiled<BM, BN, BK, NS, EPI_SWIGLU, true>), grd, blk, 0, st, a);
+      else return hipErrorInvalidValue;
+      break;
     case EPI_RESID: hipLaunchKernelGGL((k_tiled<BM, BN, BK, NS, EPI_RESID, false>), grd, blk, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
@@ -491,11 +503,12 @@ TileShape tiled_shape(int M, int N, int K, int epi) {
   // at 256 rows two 128 x 256 row tiles beat one 256 x 128 row tile by 4% of the step)
   // 129-160 and 257-320 rows: one or two row tiles of 160 x 256 (160 rows: LM head
   // 0.55 -> 0.44 ms for the d = 8192 model, 364 -> 358 us at d = 4096; 288 rows: 0.86 ->
-  // 0.76 ms against three 128 x 256 row tiles)
+  // 0.76 ms against three 128 x 256 row tiles); 161-192 rows: one 192 x 192 row tile
+  // (192 rows: 367 -> 358 us against 256 x 128 tiles)
   if (M <= 64) return k128 ? TileShape{64, 128, 128, 3} : TileShape{64, 128, 64, 2};
   if (M <= 128) return TileShape{128, 128, 64, 4};
   if (M <= 160) return TileShape{160, 256, 64, 3};
-  if (M <= 192) return TileShape{256, 128, 64, 3};
+  if (M <= 192) return TileShape{192, 192, 64, 3};
   if (M <= 256) return TileShape{128, 256, 64, 3};
   if (M <= 320) return TileShape{160, 256, 64, 3};
   if (M <= 384) return TileShape{128, 256, 64, 3};
@@ -510,6 +523,7 @@ TileShape tiled_shape(int M, int N, int K, int epi) {
   X(256, 128, 64, 3)      \
   X(128, 256, 64, 3)      \
   X(160, 256, 64, 3)      \
+  X(192, 192, 64, 3)      \
   X(256, 256, 64, 2)
 
 int tiled_per_cu(const TileShape &sh) {

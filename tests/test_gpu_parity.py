@@ -195,6 +195,17 @@ def test_greedy_parity_lm_head_160_row_tiles(B):
     _run_greedy(LM160[1].with_batch(B))
 
 
+# The LM head at 161-192 rows runs on 192 x 192 tiles (three 32-column blocks per wave):
+# greedy at 168 and 192 rows, sampled at 180 rows (20 requests, 4 drafts).
+@pytest.mark.parametrize("B", [21, 24], ids=["168-rows", "192-rows"])
+def test_greedy_parity_lm_head_192_tiles(B):
+    _run_greedy(LM160[1].with_batch(B))
+
+
+def test_sample_parity_lm_head_192_tiles():
+    _run_sample(LM160[0].with_batch(20))
+
+
 @pytest.mark.parametrize("name", ["small", "small_wide", "small_batch", "tiny"])
 def test_greedy_parity(name):
     wk = wl.PRESETS[name]
@@ -298,9 +309,9 @@ def test_scheduled_parity_few_rows_small_plans():
     assert 64 < (vl + 1).sum() <= 128, (vl + 1).sum()
 
 
-# A 160-row budget: the budget-sized LM head uses 256 x 128 tiles and the small plan
-# 128 x 128 ones (the same statistics slots).  Binding (160 rows: the budget-sized
-# launches work) and not binding (105 rows: the small ones work).
+# A 160-row budget: the budget-sized LM head uses 160 x 256 tiles (four statistics slots
+# per column tile) and the small plan 128 x 256 ones (two).  Binding (160 rows: the
+# budget-sized launches work) and not binding (105 rows: the small ones work).
 SCHED_160 = replace(SCHED_200, name="sched_160", budget=160)
 SCHED_160_FEW = replace(SCHED_LOOSE, name="sched_160_few", threshold=0.5, budget=160)
 
@@ -323,6 +334,15 @@ SCHED_300 = replace(SCHED_200, name="sched_300", budget=300)
 def test_scheduled_parity_budget_300_binding():
     vl = _run_scheduled(SCHED_300)
     assert (vl + 1).sum() == 300
+
+
+# A binding 192-row budget: the budget-sized verify LM head on one row tile of 192 x 192.
+SCHED_192 = replace(SCHED_200, name="sched_192", budget=192)
+
+
+def test_scheduled_parity_budget_192_binding():
+    vl = _run_scheduled(SCHED_192)
+    assert (vl + 1).sum() == 192
 
 
 def _run_scheduled(wk, expect_bound=True):
