@@ -141,6 +141,8 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs &a,
     const int pslot = tni * WG::WN + wn;
     const int nb = n0 + wn * WTN + l32;
     if (a.logits) {
+      // Nontemporal stores: the logits are read once, by a later kernel, and would
+      // otherwise share L2 with the weight tiles (sampled steps 1-3% faster).
       // row bases are wave-uniform; the lane part (row half, column) is an offset
       const long lane_off = (long)rsub * a.ldl + nb;
 #pragma unroll
@@ -152,7 +154,7 @@ __device__ __forceinline__ void tile_epilogue(const GemmArgs &a,
           if (mrow + rsub < M) {
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-              if (nb + j * 32 < a.N) rowbase[lane_off + j * 32] = acc[i][j][r];
+              if (nb + j * 32 < a.N) __builtin_nontemporal_store(acc[i][j][r], rowbase + lane_off + j * 32);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
