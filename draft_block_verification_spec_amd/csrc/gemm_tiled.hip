@@ -3,10 +3,10 @@
 // Once B*(K+1) rows share each weight read the verification pass stops being
 // bound by HBM and becomes compute-bound (Wildberries page, "A bit of theory",
 // Statement 3: under load the step time grows with B*(K+1)).  Each 256-thread
-// workgroup (2 x 2 waves, or 1 x 4 for 160-row tiles) owns a BM x BN output tile and
-// walks k in 64-wide slices.  Both operand slices travel from global memory straight into LDS with
-// global_load_lds_dwordx4 (no staging registers), NS slices deep, so the loads of
-// future slices run under the MFMAs of the current one.  Inside a row the sixteen-
+// workgroup (2 x 2 waves, or 1 x 4 for 160-row tiles) owns a BM x BN output tile
+// and walks k in 64-wide slices.  Both operand slices travel from global memory
+// straight into LDS with global_load_lds_dwordx4 (no staging registers), NS slices
+// deep, so the loads of future slices run under the MFMAs of the current one.  Inside a row the sixteen-
 // byte chunks are XOR-swizzled so the 128-bit operand reads of
 // v_mfma_f32_32x32x16_bf16 hit distinct banks.  The LDS reads of the next k step,
 // and at slice boundaries the global->LDS loads of a future slice, are interleaved
@@ -500,7 +500,8 @@ TileShape tiled_shape(int M, int N, int K, int epi) {
   if (epi == EPI_RESID) {
     if (M <= 64) return k128 ? TileShape{64, 128, 128, 3} : TileShape{64, 128, 64, 2};
     // 129-160 rows: 160 x 256 tiles when their split-K workgroups still fill the CUs
-    // (the wide model's 8192 outputs: 32 tiles x 8 splits), else one 192-row tile
+    // (the wide model's 8192 outputs: 32 tiles x 8 splits), else one 192-row tile.  The
+    // split bound is the one the planner applies: at most 8, and at least 4 slices each.
     if (M > 128 && M <= 160) {
       const int maxs = K / 64 / 4 < 8 ? K / 64 / 4 : 8;
       if ((long)((N + 255) / 256) * maxs >= num_cus()) return TileShape{160, 256, 64, 3};
