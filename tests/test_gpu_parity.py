@@ -181,6 +181,16 @@ def test_greedy_parity_160_rows_wide_ff():
     _run_greedy(MLP160_FF)
 
 
+# 160 rows with d = 8192, d_ff = 2048: the down projection on 160 x 256 tiles with 8
+# K-splits (32 column tiles x 8 = 256 workgroups) and the fixed-order reduce; the MLP
+# output is compared element by element.
+MLP160_D8K = wl.Workload("mlp160_d8k", 27, B=20, K=7, d=8192, d_ff=2048, V=5003, T=1.0, sigma=(0.3, 1.2))
+
+
+def test_greedy_parity_160_rows_down_split_k():
+    _run_greedy(MLP160_D8K)
+
+
 def test_sample_parity_160_rows_wide_ff():
     _run_sample(MLP160_FF)
 
