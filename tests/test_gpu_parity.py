@@ -423,8 +423,11 @@ def _schedule_agrees(vl, ref, wk):
 TALLY_SCHED: list = []
 
 
-def test_propose_parity():
-    wk = wl.SMALL_WIDE
+# The drafter step over 20 draft rows (streaming kernel) and over 140, 168 and 280 rows
+# (LM head on 160 x 256, 192 x 192 and two row tiles of 160 x 256).
+@pytest.mark.parametrize("wk", [wl.SMALL_WIDE, wl.SMALL_BATCH.with_batch(20), wl.SMALL_BATCH.with_batch(24),
+                                wl.SMALL_BATCH.with_batch(40)], ids=lambda w: f"{w.name}-b{w.B}")
+def test_propose_parity(wk):
     data = wl.generate(wk)
     W = oracle.Weights.from_bits(data)
     w = pt.dev_weights(data)
