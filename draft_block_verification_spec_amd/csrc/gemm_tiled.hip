@@ -514,12 +514,16 @@ TileShape tiled_shape(int M, int N, int K, int epi) {
   // 129-160 and 257-320 rows: one or two row tiles of 160 x 256 (160 rows: LM head
   // 0.55 -> 0.44 ms for the d = 8192 model, 364 -> 358 us at d = 4096; 288 rows: 0.86 ->
   // 0.76 ms against three 128 x 256 row tiles); 161-192 rows: one 192 x 192 row tile
-  // (192 rows: 367 -> 358 us against 256 x 128 tiles)
+  // (192 rows: 367 -> 358 us against 256 x 128 tiles).  193-256 rows: one 256 x 256 row
+  // tile, which moves 2 bytes into LDS per weight byte against 3 for two 128 x 256 row
+  // tiles (the rate into LDS is what these kernels are held to); with the ragged columns
+  // on 256 x 128 tiles (the planner's split) the V = 151936 head at 256 rows went from
+  // 378 to 351 us, at 224 rows from 376 to 349 us.
   if (M <= 64) return k128 ? TileShape{64, 128, 128, 3} : TileShape{64, 128, 64, 2};
   if (M <= 128) return TileShape{128, 128, 64, 4};
   if (M <= 160) return TileShape{160, 256, 64, 3};
   if (M <= 192) return TileShape{192, 192, 64, 3};
-  if (M <= 256) return TileShape{128, 256, 64, 3};
+  if (M <= 256) return TileShape{256, 256, 64, 2};
   if (M <= 320) return TileShape{160, 256, 64, 3};
   if (M <= 384) return TileShape{128, 256, 64, 3};
   return TileShape{256, 256, 64, 2};

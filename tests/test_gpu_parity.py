@@ -216,6 +216,22 @@ def test_sample_parity_lm_head_192_tiles():
     _run_sample(LM160[0].with_batch(20))
 
 
+# The LM head at 193-256 rows runs on one 256 x 256 row tile: greedy at 256 rows with
+# V = 70000 (274 column tiles: one round of 256 on 256 x 256 tiles, the ragged 4464
+# columns as a second launch of 256 x 128 tiles), at 200 rows with V = 48000 (one partial
+# round, no split); sampled at 240 rows (16 requests: 128 target + 112 draft rows).
+LM256 = wl.Workload("lm256", 28, B=32, K=7, d=256, d_ff=512, V=70000, T=1.0, sigma=(0.3, 1.2))
+
+
+@pytest.mark.parametrize("B,V", [(32, 70000), (25, 48000)], ids=["256-rows-split", "200-rows"])
+def test_greedy_parity_lm_head_256_tiles(B, V):
+    _run_greedy(replace(LM256, V=V).with_batch(B))
+
+
+def test_sample_parity_lm_head_256_tiles():
+    _run_sample(LM256.with_batch(16))
+
+
 @pytest.mark.parametrize("name", ["small", "small_wide", "small_batch", "tiny"])
 def test_greedy_parity(name):
     wk = wl.PRESETS[name]
