@@ -15,12 +15,13 @@ import oracle
 from draft_block_verification_spec_amd import binding as bd
 from draft_block_verification_spec_amd import workload as wl
 from tests import parity as pt
-from tests.test_gpu_parity import _run_greedy, _run_sample
+from tests.test_gpu_parity import ODD, _run_greedy, _run_sample
 
 pytestmark = pytest.mark.gpu
 
-# reduced shapes with at most 16 target rows (MLP) and 32 LM-head rows
-SMALL8 = [wl.SMALL.with_batch(2), wl.SMALL_WIDE.with_batch(3), wl.TINY.with_batch(3)]
+# reduced shapes with at most 16 target rows (MLP) and 32 LM-head rows; the last has
+# d = 192 and d_ff = 576 (6 and 18 k-steps of 32 on the general path) and an odd V
+SMALL8 = [wl.SMALL.with_batch(2), wl.SMALL_WIDE.with_batch(3), wl.TINY.with_batch(3), ODD.with_batch(2)]
 
 
 @pytest.mark.parametrize("wk", SMALL8, ids=lambda w: f"{w.name}-B{w.B}")

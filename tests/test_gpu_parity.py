@@ -232,6 +232,23 @@ def test_sample_parity_lm_head_256_tiles():
     _run_sample(LM256.with_batch(16))
 
 
+# Sizes that are not multiples of 128: d = 192 and d_ff = 576 put the 64-row LM head and
+# down projection on 64-wide slices (64 x 128, two stages), the 16-row weight-streaming
+# kernels on their general-K path (6 and 18 k-steps of 32, the rest of a 4096-wide chunk
+# masked), and V = 3001 (odd) on the scalar paths of the sampling tails.
+ODD = wl.Workload("odd_dims", 33, B=8, K=7, d=192, d_ff=576, V=3001, T=1.0, sigma=(0.3, 1.2))
+
+
+@pytest.mark.parametrize("B", [8, 2], ids=["64-rows", "16-rows"])
+def test_greedy_parity_odd_dims(B):
+    _run_greedy(ODD.with_batch(B))
+
+
+@pytest.mark.parametrize("B", [8, 2], ids=["120-rows", "30-rows"])
+def test_sample_parity_odd_dims(B):
+    _run_sample(ODD.with_batch(B))
+
+
 @pytest.mark.parametrize("name", ["small", "small_wide", "small_batch", "tiny"])
 def test_greedy_parity(name):
     wk = wl.PRESETS[name]
