@@ -220,6 +220,24 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _used_on(stream, *tensors) -> None:
+    """Buffers allocated here (on torch's current stream) for a call enqueued on another
+    stream are recorded as used there, so torch's caching allocator does not hand their
+    memory out again before that stream has passed the call."""
+    if stream is None:
+        return
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(_stream(stream))
+    if s.cuda_stream == torch.cuda.current_stream().cuda_stream:
+        return
+    for t in tensors:
+        if isinstance(t, torch.Tensor):
+            t.record_stream(s)
+
+
+def _tensors(out: "Outputs") -> list:
+    return [v for v in vars(out).values() if isinstance(v, torch.Tensor)]
+
+
 def _raise(rc: int, what: str):
     if rc != SV_OK:
         msg = load().sv_strerror(rc).decode()
@@ -234,6 +252,7 @@ def spec_verify_greedy(w: Weights, h, draft, *, out: Outputs | None = None, ws=N
     _check_dev(draft, torch.int32, "draft")
     B, K1, _ = h.shape
     K = K1 - 1
+    mine = ([] if out is not None else ["out"]) + ([] if ws is not None else ["ws"])
     out = out or make_outputs(B, K, h.device, mode=SV_MODE_GREEDY, V=w.V, d=w.d, diag=diag, logits=logits,
                               hidden=hidden)
     ws = ws if ws is not None else workspace(SV_MODE_GREEDY, B, K, w, h.device)
@@ -241,6 +260,7 @@ def spec_verify_greedy(w: Weights, h, draft, *, out: Outputs | None = None, ws=N
     rc = load().spec_verify_greedy(ctypes.byref(w.c), _ptr(h), _ptr(draft), B, K, _ptr(ws), ws.numel(),
                                    ctypes.byref(oc), _stream(stream))
     _raise(rc, "spec_verify_greedy")
+    _used_on(stream, *(_tensors(out) if "out" in mine else []), *([ws] if "ws" in mine else []))
     return out
 
 
@@ -252,6 +272,7 @@ def spec_verify_sample(w: Weights, h, h_draft, draft, u, T: float, *, out: Outpu
     _check_dev(u, torch.float32, "u")
     B, K1, _ = h.shape
     K = K1 - 1
+    mine = ([] if out is not None else ["out"]) + ([] if ws is not None else ["ws"])
     out = out or make_outputs(B, K, h.device, mode=SV_MODE_SAMPLE, V=w.V, d=w.d, diag=diag, logits=logits,
                               hidden=hidden)
     ws = ws if ws is not None else workspace(SV_MODE_SAMPLE, B, K, w, h.device)
@@ -259,6 +280,7 @@ def spec_verify_sample(w: Weights, h, h_draft, draft, u, T: float, *, out: Outpu
     rc = load().spec_verify_sample(ctypes.byref(w.c), _ptr(h), _ptr(h_draft), _ptr(draft), _ptr(u), float(T), B, K,
                                    _ptr(ws), ws.numel(), ctypes.byref(oc), _stream(stream))
     _raise(rc, "spec_verify_sample")
+    _used_on(stream, *(_tensors(out) if "out" in mine else []), *([ws] if "ws" in mine else []))
     return out
 
 
@@ -272,12 +294,15 @@ def spec_verify_sample_noalloc(w: Weights, h, h_draft, draft, u, T: float, *, ou
     _check_dev(u, torch.float32, "u")
     B, K1, _ = h.shape
     K = K1 - 1
+    mine = out is None
     out = out or make_outputs(B, K, h.device, mode=SV_MODE_SAMPLE, V=w.V, d=w.d, diag=diag, logits=logits,
                               hidden=hidden)
     oc = out.c()
     rc = load().spec_verify_sample_noalloc(ctypes.byref(w.c), _ptr(h), _ptr(h_draft), _ptr(draft), _ptr(u),
                                            float(T), B, K, ctypes.byref(oc), _stream(stream))
     _raise(rc, "spec_verify_sample_noalloc")
+    if mine:
+        _used_on(stream, *_tensors(out))
     return out
 
 
@@ -290,6 +315,7 @@ def spec_verify_scheduled(w: Weights, h, h_draft, draft, u, T: float, survival_t
     _check_dev(u, torch.float32, "u")
     B, K1, _ = h.shape
     K = K1 - 1
+    mine = ([] if out is not None else ["out"]) + ([] if ws is not None else ["ws"])
     out = out or make_outputs(B, K, h.device, mode=SV_MODE_SCHEDULED, V=w.V, d=w.d, diag=diag, logits=logits,
                               hidden=hidden)
     ws = ws if ws is not None else workspace(SV_MODE_SCHEDULED, B, K, w, h.device)
@@ -298,6 +324,7 @@ def spec_verify_scheduled(w: Weights, h, h_draft, draft, u, T: float, survival_t
                                       float(survival_threshold), int(budget_rows), B, K, _ptr(ws), ws.numel(),
                                       ctypes.byref(oc), _stream(stream))
     _raise(rc, "spec_verify_scheduled")
+    _used_on(stream, *(_tensors(out) if "out" in mine else []), *([ws] if "ws" in mine else []))
     return out
 
 
@@ -309,12 +336,14 @@ def spec_draft_propose(w: Weights, h_draft, coins, T: float, *, draft_out=None, 
     if coins is not None:
         _check_dev(coins, torch.float32, "coins")
     dev = h_draft.device
+    mine = [t is None for t in (draft_out, conf_out, ws)]
     draft_out = draft_out if draft_out is not None else torch.empty(rows, dtype=torch.int32, device=dev)
     conf_out = conf_out if conf_out is not None else torch.empty(rows, dtype=torch.float32, device=dev)
     ws = ws if ws is not None else workspace(SV_MODE_PROPOSE, rows, 0, w, dev)
     rc = load().spec_draft_propose(ctypes.byref(w.c), _ptr(h_draft), _ptr(coins), float(T), rows, _ptr(ws),
                                    ws.numel(), _ptr(draft_out), _ptr(conf_out), _stream(stream))
     _raise(rc, "spec_draft_propose")
+    _used_on(stream, *[t for t, m in zip((draft_out, conf_out, ws), mine) if m])
     return draft_out.view(h_draft.shape[:-1]), conf_out.view(h_draft.shape[:-1])
 
 
@@ -334,15 +363,19 @@ def spec_verify_tree(w: Weights, h, h_draft, tokens, parent, u, T: float, *, out
     B, K1, _ = h.shape
     K = K1 - 1
     mode = SV_MODE_GREEDY if greedy else SV_MODE_SAMPLE
+    mine = ([] if out is not None else ["out"]) + ([] if ws is not None else ["ws"])
     out = out or make_outputs(B, K, h.device, mode=mode, V=w.V, d=w.d, diag=diag, logits=logits, hidden=hidden)
     if out.path is None:
         out.path = torch.empty(B, K + 1, dtype=torch.int32, device=h.device)
+        mine.append("path")
     ws = ws if ws is not None else workspace(mode, B, K, w, h.device)
     oc = out.c()
     rc = load().spec_verify_tree(ctypes.byref(w.c), _ptr(h), None if greedy else _ptr(h_draft), _ptr(tokens),
                                  _ptr(parent), None if greedy else _ptr(u), float(T), B, K, _ptr(ws), ws.numel(),
                                  ctypes.byref(oc), _ptr(out.path), int(wait_polls), _stream(stream))
     _raise(rc, "spec_verify_tree")
+    _used_on(stream, *(_tensors(out) if "out" in mine else [out.path] if "path" in mine else []),
+             *([ws] if "ws" in mine else []))
     return out
 
 
