@@ -117,6 +117,69 @@ def _check_dev(t, dtype, name):
         raise SpecVerifyError(f"{name} must be contiguous")
 
 
+def _shape(t, shape, name):
+    """The C ABI takes bare pointers: a tensor of the wrong size would send the kernels
+    past its end, so every shape is checked here, before the call."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise SpecVerifyError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _room(t, n, dtype, name):
+    """An output the kernels write n elements of (any shape, contiguous)."""
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise SpecVerifyError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous() or t.numel() < n:
+        raise SpecVerifyError(f"{name} must be contiguous with at least {n} elements, got {t.numel()}")
+
+
+def _check_weight_shapes(w_lm, w_gate, w_up, w_down, s_lm=None, s_gate=None, s_up=None, s_down=None):
+    if w_lm.dim() != 2:
+        raise SpecVerifyError(f"w_lm must be [V, d], got {tuple(w_lm.shape)}")
+    V, d = w_lm.shape
+    if (w_gate is None) != (w_up is None) or (w_gate is None) != (w_down is None):
+        raise SpecVerifyError("w_gate, w_up and w_down go together")
+    if w_gate is not None:
+        if w_gate.dim() != 2:
+            raise SpecVerifyError(f"w_gate must be [d_ff, d], got {tuple(w_gate.shape)}")
+        d_ff = w_gate.shape[0]
+        _shape(w_gate, (d_ff, d), "w_gate")
+        _shape(w_up, (d_ff, d), "w_up")
+        _shape(w_down, (d, d_ff), "w_down")
+        _shape(s_gate, (d_ff,), "s_gate")
+        _shape(s_up, (d_ff,), "s_up")
+        _shape(s_down, (d,), "s_down")
+    _shape(s_lm, (V,), "s_lm")
+
+
+def _check_call_shapes(w, h, *, draft=None, h_draft=None, u=None, out=None, mode=None):
+    """h [B, K+1, d] with the weights' d; draft [B, K]; h_draft [B, K, d]; u [B, K+1]; and
+    room in every output the call writes.  Returns (B, K)."""
+    if h.dim() != 3 or h.shape[-1] != w.d:
+        raise SpecVerifyError(f"h must be [B, K+1, {w.d}], got {tuple(h.shape)}")
+    B, K = h.shape[0], h.shape[1] - 1
+    _shape(draft, (B, K), "draft")
+    _shape(h_draft, (B, K, w.d), "h_draft")
+    _shape(u, (B, K + 1), "u")
+    if out is not None:
+        rows_t = B * (K + 1)
+        rows = rows_t + (0 if mode == SV_MODE_GREEDY else B * K)
+        i32, f32 = torch.int32, torch.float32
+        _room(out.accepted_len, B, i32, "accepted_len")
+        _room(out.emitted, rows_t, i32, "emitted")
+        _room(out.tau, 1, f32, "tau")
+        _room(out.counters, 3, torch.int64, "counters")
+        _room(out.dev_status, 1, i32, "dev_status")
+        _room(out.diag, rows * SV_DIAG_COLS, f32, "diag")
+        _room(out.logits, rows * w.V, f32, "logits")
+        _room(out.hidden, rows_t * w.d, torch.bfloat16, "hidden")
+        if mode == SV_MODE_SCHEDULED:
+            _room(out.verify_len, B, i32, "verify_len")
+        _room(out.path, rows_t, i32, "path")
+    return B, K
+
+
 @dataclass
 class Weights:
     """Device weights, row-major [out, in], and the C struct that points at them.
@@ -143,6 +206,8 @@ class Weights:
                 if getattr(self, n) is None:
                     raise SpecVerifyError(f"{n}: FP8 weights need their row scales")
                 _check_dev(getattr(self, n), torch.float32, n)
+        _check_weight_shapes(self.w_lm, self.w_gate, self.w_up, self.w_down, self.s_lm if fp8 else None,
+                             self.s_gate if fp8 else None, self.s_up if fp8 else None, self.s_down if fp8 else None)
         V, d = self.w_lm.shape
         d_ff = 0 if self.w_gate is None else self.w_gate.shape[0]
         self.c = SvWeights(_ptr(self.w_gate), _ptr(self.w_up), _ptr(self.w_down), _ptr(self.w_lm), d, d_ff, V,
@@ -250,8 +315,7 @@ def spec_verify_greedy(w: Weights, h, draft, *, out: Outputs | None = None, ws=N
                        logits=False, hidden=False) -> Outputs:
     _check_dev(h, torch.bfloat16, "h")
     _check_dev(draft, torch.int32, "draft")
-    B, K1, _ = h.shape
-    K = K1 - 1
+    B, K = _check_call_shapes(w, h, draft=draft, out=out, mode=SV_MODE_GREEDY)
     mine = ([] if out is not None else ["out"]) + ([] if ws is not None else ["ws"])
     out = out or make_outputs(B, K, h.device, mode=SV_MODE_GREEDY, V=w.V, d=w.d, diag=diag, logits=logits,
                               hidden=hidden)
@@ -270,8 +334,7 @@ def spec_verify_sample(w: Weights, h, h_draft, draft, u, T: float, *, out: Outpu
     _check_dev(h_draft, torch.bfloat16, "h_draft")
     _check_dev(draft, torch.int32, "draft")
     _check_dev(u, torch.float32, "u")
-    B, K1, _ = h.shape
-    K = K1 - 1
+    B, K = _check_call_shapes(w, h, draft=draft, h_draft=h_draft, u=u, out=out, mode=SV_MODE_SAMPLE)
     mine = ([] if out is not None else ["out"]) + ([] if ws is not None else ["ws"])
     out = out or make_outputs(B, K, h.device, mode=SV_MODE_SAMPLE, V=w.V, d=w.d, diag=diag, logits=logits,
                               hidden=hidden)
@@ -292,8 +355,7 @@ def spec_verify_sample_noalloc(w: Weights, h, h_draft, draft, u, T: float, *, ou
     _check_dev(h_draft, torch.bfloat16, "h_draft")
     _check_dev(draft, torch.int32, "draft")
     _check_dev(u, torch.float32, "u")
-    B, K1, _ = h.shape
-    K = K1 - 1
+    B, K = _check_call_shapes(w, h, draft=draft, h_draft=h_draft, u=u, out=out, mode=SV_MODE_SAMPLE)
     mine = out is None
     out = out or make_outputs(B, K, h.device, mode=SV_MODE_SAMPLE, V=w.V, d=w.d, diag=diag, logits=logits,
                               hidden=hidden)
@@ -313,8 +375,7 @@ def spec_verify_scheduled(w: Weights, h, h_draft, draft, u, T: float, survival_t
     _check_dev(h_draft, torch.bfloat16, "h_draft")
     _check_dev(draft, torch.int32, "draft")
     _check_dev(u, torch.float32, "u")
-    B, K1, _ = h.shape
-    K = K1 - 1
+    B, K = _check_call_shapes(w, h, draft=draft, h_draft=h_draft, u=u, out=out, mode=SV_MODE_SCHEDULED)
     mine = ([] if out is not None else ["out"]) + ([] if ws is not None else ["ws"])
     out = out or make_outputs(B, K, h.device, mode=SV_MODE_SCHEDULED, V=w.V, d=w.d, diag=diag, logits=logits,
                               hidden=hidden)
@@ -332,9 +393,15 @@ def spec_draft_propose(w: Weights, h_draft, coins, T: float, *, draft_out=None, 
                        stream=None):
     """Returns (draft ids int32 [rows], top-1 confidences fp32 [rows]) for h_draft [rows, d] (or [B, K, d])."""
     _check_dev(h_draft, torch.bfloat16, "h_draft")
+    if h_draft.dim() < 1 or h_draft.shape[-1] != w.d:
+        raise SpecVerifyError(f"h_draft must be [..., {w.d}], got {tuple(h_draft.shape)}")
     rows = h_draft.numel() // h_draft.shape[-1]
     if coins is not None:
         _check_dev(coins, torch.float32, "coins")
+        if coins.numel() != rows:
+            raise SpecVerifyError(f"coins must hold one coin per draft row ({rows}), got {coins.numel()}")
+    _room(draft_out, rows, torch.int32, "draft_out")
+    _room(conf_out, rows, torch.float32, "conf_out")
     dev = h_draft.device
     mine = [t is None for t in (draft_out, conf_out, ws)]
     draft_out = draft_out if draft_out is not None else torch.empty(rows, dtype=torch.int32, device=dev)
@@ -360,9 +427,10 @@ def spec_verify_tree(w: Weights, h, h_draft, tokens, parent, u, T: float, *, out
     if not greedy:
         _check_dev(h_draft, torch.bfloat16, "h_draft")
         _check_dev(u, torch.float32, "u")
-    B, K1, _ = h.shape
-    K = K1 - 1
     mode = SV_MODE_GREEDY if greedy else SV_MODE_SAMPLE
+    B, K = _check_call_shapes(w, h, draft=tokens, h_draft=None if greedy else h_draft, u=None if greedy else u,
+                              out=out, mode=mode)
+    _shape(parent, (B, K), "parent")
     mine = ([] if out is not None else ["out"]) + ([] if ws is not None else ["ws"])
     out = out or make_outputs(B, K, h.device, mode=mode, V=w.V, d=w.d, diag=diag, logits=logits, hidden=hidden)
     if out.path is None:
@@ -394,6 +462,14 @@ def spec_commit(accepted_len, seq_len, *, Kmax: int, kv=None, block_table=None, 
     for t, n in ((kv, "kv"), (rec_state, "rec_state"), (rec_snap, "rec_snap")):
         _check_dev(t, torch.uint8, n)
     B = seq_len.numel()
+    _shape(accepted_len, (B,), "accepted_len")
+    _shape(verify_len, (B,), "verify_len")
+    _shape(path, (B, Kmax + 1), "path")
+    _room(dev_status, 1, torch.int32, "dev_status")
+    if block_table is not None and (block_table.dim() != 2 or block_table.shape[0] != B):
+        raise SpecVerifyError(f"block_table must be [{B}, max_blocks], got {tuple(block_table.shape)}")
+    if rec_state is not None and (rec_state.dim() != 2 or rec_state.shape[0] != B):
+        raise SpecVerifyError(f"rec_state must be [{B}, n], got {tuple(rec_state.shape)}")
     c = SvCache()
     c.seq_len = _ptr(seq_len)
     if kv is not None:
@@ -404,7 +480,7 @@ def spec_commit(accepted_len, seq_len, *, Kmax: int, kv=None, block_table=None, 
         c.layer_stride, c.half_stride = kv.stride(0), kv.stride(1)
         c.block_table, c.max_blocks = _ptr(block_table), block_table.shape[-1]
     if rec_state is not None or rec_snap is not None:
-        if rec_state is None or rec_snap is None or rec_snap.shape[:2] != (B, Kmax + 1):
+        if rec_state is None or rec_snap is None or tuple(rec_snap.shape) != (B, Kmax + 1, rec_state.shape[-1]):
             raise SpecVerifyError("rec_state [B, n] and rec_snap [B, Kmax+1, n] go together")
         c.rec_state, c.rec_snap, c.rec_bytes = _ptr(rec_state), _ptr(rec_snap), rec_state.shape[-1]
     rc = load().spec_commit(ctypes.byref(c), _ptr(accepted_len), _ptr(verify_len), _ptr(path), B, int(Kmax),
