@@ -130,3 +130,41 @@ def test_tiny_config_tau_gpu():
     assert float(np.mean(A + 1)) == pytest.approx(cf, rel=0.01)
     c = out.counters.cpu().numpy()
     assert c[0] == A.sum() and c[1] == 4 * wk.B and c[2] == (A + 1).sum()
+
+
+def test_tree_first_token_chi_square_v8_gpu():
+    """Tree verification keeps the target distribution (reading R15; the multi-candidate
+    rule is lossless for children drawn independently from their parent's q).  V = 8, d =
+    64, a star tree (root and three children) with the same hidden rows for 4 x 10^5
+    requests: each request's three candidates are fresh draws from the root's q, with fresh
+    coins.  The first emitted token follows the root's p (chi-square, alpha = 0.01), and a
+    request emits a second token exactly when one candidate was accepted."""
+    w = wl.Workload("tree8", 34, B=1, K=3, d=64, d_ff=0, V=8, T=1.0, sigma=0.9)
+    data = wl.generate(w)
+    W = oracle.Weights.from_bits(data)
+    h64, hd64 = oracle.from_bf16_bits(data["h"])[0], oracle.from_bf16_bits(data["h_draft"])[0]
+    p0 = oracle.softmax_t(oracle.lm_logits(W.w_lm, h64[0]), 1.0)
+    q0 = oracle.softmax_t(oracle.lm_logits(W.w_lm, hd64[0]), 1.0)
+    K, V, N = 3, 8, 400_000
+    rng = np.random.default_rng(2027)
+    tokens = np.minimum(np.searchsorted(np.cumsum(q0), rng.random((N, K)), side="right"), V - 1)
+    parent = np.zeros((N, K), np.int32)
+    coins = (rng.integers(0, 1 << 24, size=(N, K + 1)) * 2.0 ** -24).astype(np.float32)
+    dev = torch.device("cuda")
+    wd = pt.dev_weights(data)
+    h = pt.dev_bf16(data["h"]).expand(N, K + 1, 64).contiguous()
+    hd = pt.dev_bf16(data["h_draft"]).expand(N, K, 64).contiguous()
+    out = bd.spec_verify_tree(wd, h, hd, torch.from_numpy(tokens.astype(np.int32)).to(dev),
+                              torch.from_numpy(parent).to(dev), torch.from_numpy(coins).to(dev), 1.0)
+    torch.cuda.synchronize()
+    assert int(out.dev_status.item()) == 0
+    A = out.accepted_len.cpu().numpy()
+    em = out.emitted.cpu().numpy()
+    assert np.all((A == 0) | (A == 1))
+    hist = np.bincount(em[:, 0], minlength=V)
+    chi = float(((hist - N * p0) ** 2 / (N * p0)).sum())
+    assert chi < scipy.stats.chi2.ppf(0.99, V - 1), (chi, hist, N * p0)
+    # an accepted candidate is one of the drafted tokens of the root
+    acc = A == 1
+    assert np.all((em[acc, 0][:, None] == tokens[acc]).any(axis=1))
+    assert np.all(em[acc, 1] >= 0) and np.all(em[~acc, 1] == -1)
