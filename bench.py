@@ -96,7 +96,8 @@ def roofline(bytes_, flops, ms, peaks_m, kernel):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "the benchmark measures one GPU (one process per GPU); --gpus must be 1",
+                          "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
     from draft_block_verification_spec_amd import binding as bd
