@@ -7,7 +7,10 @@ captures it on fixed buffers, then replays it several times with unrelated eager
 synchronisations in between.  Every replay must equal the eager call bit for bit, also
 after new inputs are copied into the captured input buffers.  The greedy, sampled and
 allocation-free entry points are covered, on the streaming kernels (the 16-token block)
-and on the tiled ones (40 requests of 8 rows).
+and on the tiled ones (40 requests of 8 rows), and the scheduled one (24 requests, the
+verify GEMMs gated on the device-side row count).  Before each replay the logits and
+diagnostics are refilled with NaN, as the eager reference's fresh buffers are, so every
+replay must also write every row the eager call writes.
 """
 import numpy as np
 import pytest
@@ -32,15 +35,20 @@ def _inputs(wk, data, dev, seed):
 def _same(a, b, what):
     for n in FIELDS:
         assert torch.equal(getattr(a, n), getattr(b, n)), f"{what}: {n}"
+    if a.verify_len is not None:
+        assert torch.equal(a.verify_len, b.verify_len), f"{what}: verify_len"
     if a.logits is not None:
         assert torch.equal(a.logits.nan_to_num(), b.logits.nan_to_num()), f"{what}: logits"
     if a.diag is not None:
         assert torch.equal(a.diag.nan_to_num(), b.diag.nan_to_num()), f"{what}: diag"
 
 
-def _eager_work(dev):
+def _eager_work(dev, out):
     x = torch.randn(512, 512, device=dev)
     (x @ x).sum().item()
+    for t in (out.logits, out.diag):
+        if t is not None:
+            t.fill_(float("nan"))
     torch.cuda.synchronize()
 
 
@@ -50,14 +58,16 @@ def _check_graph(wk, mode, noalloc=False):
     w = pt.dev_weights(data)
     h, hd, draft, u = _inputs(wk, data, dev, 1)
     B, K = wk.B, wk.K
-    m = bd.SV_MODE_GREEDY if mode == "greedy" else bd.SV_MODE_SAMPLE
-    logits = wk.V * (B * (K + 1) + (B * K if m == bd.SV_MODE_SAMPLE else 0)) <= (1 << 26)
+    m = {"greedy": bd.SV_MODE_GREEDY, "sample": bd.SV_MODE_SAMPLE, "scheduled": bd.SV_MODE_SCHEDULED}[mode]
+    logits = wk.V * (B * (K + 1) + (B * K if m != bd.SV_MODE_GREEDY else 0)) <= (1 << 26)
     out = bd.make_outputs(B, K, dev, mode=m, V=wk.V, d=wk.d, diag=True, logits=logits)
     ws = None if noalloc else bd.workspace(m, B, K, w, dev)
 
     def call(o, wsp):
         if mode == "greedy":
             return bd.spec_verify_greedy(w, h, draft, out=o, ws=wsp)
+        if mode == "scheduled":
+            return bd.spec_verify_scheduled(w, h, hd, draft, u, wk.T, wk.threshold, wk.budget, out=o, ws=wsp)
         if noalloc:
             return bd.spec_verify_sample_noalloc(w, h, hd, draft, u, wk.T, out=o)
         return bd.spec_verify_sample(w, h, hd, draft, u, wk.T, out=o, ws=wsp)
@@ -77,7 +87,7 @@ def _check_graph(wk, mode, noalloc=False):
     with torch.cuda.graph(g):
         call(out, ws)
     for rep in range(3):
-        _eager_work(dev)
+        _eager_work(dev, out)
         g.replay()
         torch.cuda.synchronize()
         _same(out, ref, f"{wk.name} {mode} replay {rep}")
@@ -93,7 +103,7 @@ def _check_graph(wk, mode, noalloc=False):
     # the new inputs change the row statistics, so a replay that reused the old ones would fail
     assert not torch.equal(ref2.diag.nan_to_num(), ref.diag.nan_to_num())
     for rep in range(2):
-        _eager_work(dev)
+        _eager_work(dev, out)
         g.replay()
         torch.cuda.synchronize()
         _same(out, ref2, f"{wk.name} {mode} new inputs, replay {rep}")
@@ -111,3 +121,7 @@ def test_graph_replay_tiled(mode):
 
 def test_graph_replay_noalloc():
     _check_graph(wl.BLOCK16, "sample", noalloc=True)
+
+
+def test_graph_replay_scheduled():
+    _check_graph(wl.SMALL_SCHED, "scheduled")
