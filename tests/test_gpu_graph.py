@@ -10,8 +10,12 @@ allocation-free entry points are covered, on the streaming kernels (the 16-token
 and on the tiled ones (40 requests of 8 rows), and the scheduled one (24 requests, the
 verify GEMMs gated on the device-side row count).  Before each replay the logits and
 diagnostics are refilled with NaN, as the eager reference's fresh buffers are, so every
-replay must also write every row the eager call writes.
+replay must also write every row the eager call writes.  The drafter step (sampled and
+argmax, streaming and tiled) and the commit (chain and tree, in place: its state is
+restored before each replay) are captured the same way.
 """
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -43,12 +47,13 @@ def _same(a, b, what):
         assert torch.equal(a.diag.nan_to_num(), b.diag.nan_to_num()), f"{what}: diag"
 
 
-def _eager_work(dev, out):
+def _eager_work(dev, out=None, refill=()):
+    """Unrelated eager work, then the output buffers refilled as fresh ones are."""
     x = torch.randn(512, 512, device=dev)
     (x @ x).sum().item()
-    for t in (out.logits, out.diag):
-        if t is not None:
-            t.fill_(float("nan"))
+    fills = [(t, float("nan")) for t in ((out.logits, out.diag) if out is not None else ()) if t is not None]
+    for t, v in fills + list(refill):
+        t.fill_(v)
     torch.cuda.synchronize()
 
 
@@ -125,3 +130,104 @@ def test_graph_replay_noalloc():
 
 def test_graph_replay_scheduled():
     _check_graph(wl.SMALL_SCHED, "scheduled")
+
+
+@pytest.mark.parametrize("wk", [wl.BLOCK16, wl.SMALL_BATCH], ids=lambda w: w.name)
+def test_graph_replay_propose(wk):
+    """The drafter step over every draft row: 15 rows on the streaming kernels, 280 rows on
+    the tiled ones; sampled (the rows' coins) and argmax."""
+    dev = torch.device("cuda", 0)
+    data = wl.generate(wk)
+    w = pt.dev_weights(data)
+    rows = pt.dev_bf16(data["h_draft"]).reshape(-1, wk.d).contiguous()
+    n = rows.shape[0]
+    coins = torch.from_numpy(np.ascontiguousarray(data["draft_coins"], dtype=np.float32).reshape(-1)).to(dev)
+    d2 = wl.generate(wk, 1, weights=False)
+    rows2 = pt.dev_bf16(d2["h_draft"]).reshape(-1, wk.d).contiguous()
+    coins2 = torch.from_numpy(np.ascontiguousarray(d2["draft_coins"], dtype=np.float32).reshape(-1)).to(dev)
+    rows0, coins0 = rows.clone(), coins.clone()
+    for T in (wk.T, 0.0):
+        c = coins if T > 0 else None
+        rows.copy_(rows0)
+        coins.copy_(coins0)
+        ws = bd.workspace(bd.SV_MODE_PROPOSE, n, 0, w, dev)
+        x = torch.empty(n, dtype=torch.int32, device=dev)
+        conf = torch.empty(n, dtype=torch.float32, device=dev)
+
+        def call():
+            bd.spec_draft_propose(w, rows, c, T, draft_out=x, conf_out=conf, ws=ws)
+
+        def eager_reference():
+            rx, rc = bd.spec_draft_propose(w, rows, c, T)
+            torch.cuda.synchronize()
+            return rx.clone(), rc.clone()
+
+        call()
+        torch.cuda.synchronize()
+        ref = eager_reference()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call()
+        for k in range(3):
+            _eager_work(dev, refill=((x, -7), (conf, float("nan"))))
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(x, ref[0]) and torch.equal(conf, ref[1]), f"{wk.name} T={T} replay {k}"
+        rows.copy_(rows2)
+        coins.copy_(coins2)
+        torch.cuda.synchronize()
+        ref2 = eager_reference()
+        # new rows change the drafts (the confidences are 1 at T = 0)
+        assert not (torch.equal(ref2[0], ref[0]) and torch.equal(ref2[1], ref[1]))
+        for k in range(2):
+            _eager_work(dev, refill=((x, -7), (conf, float("nan"))))
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(x, ref2[0]) and torch.equal(conf, ref2[1]), f"{wk.name} T={T} new rows, replay {k}"
+
+
+def _cuda(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+@pytest.mark.parametrize("tree", [False, True], ids=["chain", "tree"])
+def test_graph_replay_commit(tree):
+    """The commit of the small paged-cache case (chain and tree).  It works in place, so the
+    cache, lengths, recurrent states and status are restored eagerly before each replay."""
+    cw = replace(wl.COMMIT_SMALL, name="commit_small_tree", index=22, tree=True) if tree else wl.COMMIT_SMALL
+    c = wl.commit_case(cw, 0)
+    kv0, seq0, rs0 = _cuda(c["kv"]), _cuda(c["seq_len"]), _cuda(c["rec_state"])
+    kv, seq, rs = kv0.clone(), seq0.clone(), rs0.clone()
+    sn, acc, vl, bt = _cuda(c["rec_snap"]), _cuda(c["accepted_len"]), _cuda(c["verify_len"]), _cuda(c["block_table"])
+    path = _cuda(c["path"]) if tree else None
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def call():
+        bd.spec_commit(acc, seq, Kmax=cw.Kmax, kv=kv, block_table=bt, rec_state=rs, rec_snap=sn, verify_len=vl,
+                       path=path, dev_status=status)
+
+    def restore():
+        kv.copy_(kv0)
+        seq.copy_(seq0)
+        rs.copy_(rs0)
+        status.zero_()
+        torch.cuda.synchronize()
+
+    restore()
+    call()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (kv, seq, rs, status)]
+    # a chain's accepted entries are already in place; a tree's are moved along the path
+    assert not torch.equal(ref[1], seq0) and not torch.equal(ref[2], rs0), "the case commits nothing"
+    assert torch.equal(ref[0], kv0) != tree, "cache bytes moved as the case expects"
+    restore()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for k in range(3):
+        _eager_work(torch.device("cuda", 0))
+        restore()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want, name in zip((kv, seq, rs, status), ref, ("kv", "seq_len", "rec_state", "dev_status")):
+            assert torch.equal(got, want), f"{cw.name} replay {k}: {name}"
