@@ -43,8 +43,10 @@ def _final_rows(lg, B, K, T):
     return rows
 
 
-def _run_sample(wk, rep=0, check_hidden=True, fp8=False):
+def _run_sample(wk, rep=0, check_hidden=True, fp8=False, edit=None):
     data, W, w = _weights(wk, rep, fp8)
+    if edit is not None:  # inputs changed on the host before either side sees them
+        data = edit(data, wk)
     T = wk.T
     draft = pt.oracle_drafts(W, data, T)["draft"]
     h64 = oracle.from_bf16_bits(data["h"])
@@ -100,8 +102,10 @@ def test_sample_parity_tiny_steps():
     _run_sample(wl.TINY.with_batch(2000))
 
 
-def _run_greedy(wk, rep=0, fp8=False):
+def _run_greedy(wk, rep=0, fp8=False, edit=None):
     data, W, w = _weights(wk, rep, fp8)
+    if edit is not None:
+        data = edit(data, wk)
     draft = pt.oracle_drafts(W, data, 0.0)["draft"]
     ref = oracle.verify_greedy(W, oracle.from_bf16_bits(data["h"]), draft)
     out = bd.spec_verify_greedy(w, pt.dev_bf16(data["h"]), _i32(draft), diag=True, logits=True,
@@ -150,6 +154,41 @@ def _run_greedy(wk, rep=0, fp8=False):
 #    same way (outputs [0, 8192) on 256 x 256 tiles, the rest on 256 x 128).
 MLP160 = wl.Workload("mlp160", 14, B=20, K=7, d=256, d_ff=1536, V=5003, T=1.0, sigma=(0.3, 1.2))
 LM_SPLIT = wl.Workload("lm_split", 15, B=128, K=7, d=256, d_ff=12288, V=24000, T=1.0, sigma=(0.3, 1.2))
+
+
+# Blocks longer than the 64 acceptance decisions one wave takes at a time (the batched
+# acceptance kernels; the small-batch tail takes at most 32 rows).  With no MLP and no
+# drafter noise every draft row equals its target row, so p = q: every draft is accepted
+# (exactly: the ratio is exp(0)) and the final token is the bonus draw from row K.  With
+# the draft rows from position 66 on taken from another draw, the drafts there no longer
+# follow the target and the first rejection falls in the second block of 64 (the oracle
+# puts it at 66 for both requests, in both modes; no greedy row is within the near-tie band).
+LONG70 = wl.Workload("long70", 90, B=2, K=70, d=64, d_ff=0, V=1000, T=1.0, sigma=0.0)
+LONG64 = wl.Workload("long64", 91, B=1, K=64, d=64, d_ff=0, V=1000, T=1.0, sigma=0.0)
+
+
+def _draft_rows_from_another_draw(j0):
+    def edit(data, wk):
+        hd = data["h_draft"].copy()
+        hd[:, j0:] = wl.generate(wk, 1, weights=False)["h_draft"][:, j0:]
+        return {**data, "h_draft": hd}
+    return edit
+
+
+@pytest.mark.parametrize("wk", [LONG70, LONG64], ids=lambda w: w.name)
+def test_long_blocks_accept_every_draft(wk):
+    _, out, _ = _run_sample(wk)
+    assert (out.accepted_len.cpu().numpy() == wk.K).all()
+    _, out = _run_greedy(wk)
+    assert (out.accepted_len.cpu().numpy() == wk.K).all()
+
+
+def test_long_block_rejects_in_second_block():
+    edit = _draft_rows_from_another_draw(66)
+    ref, out, _ = _run_sample(LONG70, edit=edit)
+    assert (out.accepted_len.cpu().numpy() == 66).all() and (ref["accepted"] == 66).all()
+    ref, out = _run_greedy(LONG70, edit=edit)
+    assert (out.accepted_len.cpu().numpy() == 66).all() and (ref["accepted"] == 66).all()
 
 
 def test_sample_parity_160_rows():
