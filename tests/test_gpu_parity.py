@@ -157,7 +157,7 @@ LM_SPLIT = wl.Workload("lm_split", 15, B=128, K=7, d=256, d_ff=12288, V=24000, T
 
 
 # Blocks longer than the 64 acceptance decisions one wave takes at a time (the batched
-# acceptance kernels; the small-batch tail takes at most 32 rows).  With no MLP and no
+# acceptance kernels), and a 32-row batch on the small-batch tail.  With no MLP and no
 # drafter noise every draft row equals its target row, so p = q: every draft is accepted
 # (exactly: the ratio is exp(0)) and the final token is the bonus draw from row K.  With
 # the draft rows from position 66 on taken from another draw, the drafts there no longer
@@ -165,6 +165,7 @@ LM_SPLIT = wl.Workload("lm_split", 15, B=128, K=7, d=256, d_ff=12288, V=24000, T
 # puts it at 66 for both requests, in both modes; no greedy row is within the near-tie band).
 LONG70 = wl.Workload("long70", 90, B=2, K=70, d=64, d_ff=0, V=1000, T=1.0, sigma=0.0)
 LONG64 = wl.Workload("long64", 91, B=1, K=64, d=64, d_ff=0, V=1000, T=1.0, sigma=0.0)
+SAME15 = wl.Workload("same_rows15", 92, B=2, K=15, d=64, d_ff=0, V=1000, T=1.0, sigma=0.0)
 
 
 def _draft_rows_from_another_draw(j0):
@@ -175,8 +176,8 @@ def _draft_rows_from_another_draw(j0):
     return edit
 
 
-@pytest.mark.parametrize("wk", [LONG70, LONG64], ids=lambda w: w.name)
-def test_long_blocks_accept_every_draft(wk):
+@pytest.mark.parametrize("wk", [LONG70, LONG64, SAME15], ids=lambda w: w.name)
+def test_equal_rows_accept_every_draft(wk):
     _, out, _ = _run_sample(wk)
     assert (out.accepted_len.cpu().numpy() == wk.K).all()
     _, out = _run_greedy(wk)
