@@ -7,7 +7,7 @@ captures it on fixed buffers, then replays it several times with unrelated eager
 synchronisations in between.  Every replay must equal the eager call bit for bit, also
 after new inputs are copied into the captured input buffers.  The greedy, sampled and
 allocation-free entry points are covered, on the streaming kernels (the 16-token block)
-and on the tiled ones (40 requests of 8 rows), and the scheduled one (24 requests, the
+and on the tiled ones (40 requests of 8 rows), the block with FP8 weights, and the scheduled one (24 requests, the
 verify GEMMs gated on the device-side row count).  Before each replay the logits and
 diagnostics are refilled with NaN, as the eager reference's fresh buffers are, so every
 replay must also write every row the eager call writes.  The drafter step (sampled and
@@ -57,10 +57,12 @@ def _eager_work(dev, out=None, refill=()):
     torch.cuda.synchronize()
 
 
-def _check_graph(wk, mode, noalloc=False):
+def _check_graph(wk, mode, noalloc=False, fp8=False):
     dev = torch.device("cuda", 0)
     data = wl.generate(wk)
-    w = pt.dev_weights(data)
+    if fp8:
+        data = wl.to_fp8(data)
+    w = pt.dev_fp8_weights(data) if fp8 else pt.dev_weights(data)
     h, hd, draft, u = _inputs(wk, data, dev, 1)
     B, K = wk.B, wk.K
     m = {"greedy": bd.SV_MODE_GREEDY, "sample": bd.SV_MODE_SAMPLE, "scheduled": bd.SV_MODE_SCHEDULED}[mode]
@@ -126,6 +128,12 @@ def test_graph_replay_tiled(mode):
 
 def test_graph_replay_noalloc():
     _check_graph(wl.BLOCK16, "sample", noalloc=True)
+
+
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+def test_graph_replay_fp8(mode):
+    """FP8 E4M3 weights with row scales on the streaming kernels."""
+    _check_graph(wl.BLOCK16, mode, fp8=True)
 
 
 def test_graph_replay_scheduled():
