@@ -116,13 +116,16 @@ def _run(wk, rep, kind, T):
     return out, data, parent, tokens, ref
 
 
+TREE63 = wl.Workload("tree63", 93, B=2, K=63, d=64, d_ff=0, V=1000, T=1.0, sigma=0.4)
+
+
 @pytest.mark.parametrize("T", [0.0, 1.0], ids=["greedy", "sample"])
 @pytest.mark.parametrize("kind", ["random", "topk"])
 # B = 12 (K = 7): 96 greedy / 180 sampled LM-head rows (128 x 128 and 192 x 192 tiles);
 # B = 20: 160 / 300 rows (one and two row tiles of 160 x 256, four statistics slots per
-# column tile).
-@pytest.mark.parametrize("wk", [wl.SMALL, wl.SMALL_WIDE, wl.SMALL_BATCH.with_batch(12), wl.SMALL_BATCH.with_batch(20)],
-                         ids=lambda w: f"{w.name}-b{w.B}")
+# column tile); the largest tree the entry point takes (K = 63: 64 nodes).
+@pytest.mark.parametrize("wk", [wl.SMALL, wl.SMALL_WIDE, wl.SMALL_BATCH.with_batch(12), wl.SMALL_BATCH.with_batch(20),
+                                TREE63], ids=lambda w: f"{w.name}-b{w.B}")
 def test_tree_reduced(wk, kind, T):
     _run(wk, 0, kind, T if T == 0.0 else wk.T)
 
