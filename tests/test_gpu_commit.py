@@ -16,6 +16,10 @@ from tests.commit_session import Session, ToyTarget
 pytestmark = pytest.mark.gpu
 
 SMALL_TREE = replace(wl.COMMIT_SMALL, name="commit_small_tree", index=22, tree=True)
+# the longest verify block the commit takes (Kmax = 63: one lane per depth in one wave)
+LONG63 = wl.CommitWorkload("commit_long63", 94, B=6, Kmax=63, n_layers=2, entry_bytes=48, block_size=4,
+                           rec_bytes=48, ctx=(0, 40), invalid=1)
+LONG63_TREE = replace(LONG63, name="commit_long63_tree", index=95, tree=True)
 
 
 def _dev(a):
@@ -48,7 +52,8 @@ def _run(cw, c, use_kv=True, use_rec=True, pass_verify_len=True):
             int(status.item()))
 
 
-@pytest.mark.parametrize("cw", [wl.COMMIT_SMALL, SMALL_TREE], ids=["chain", "tree"])
+@pytest.mark.parametrize("cw", [wl.COMMIT_SMALL, SMALL_TREE, LONG63, LONG63_TREE],
+                         ids=["chain", "tree", "chain63", "tree63"])
 @pytest.mark.parametrize("rep", [0, 1])
 def test_commit_matches_oracle(cw, rep):
     c = wl.commit_case(cw, rep)
