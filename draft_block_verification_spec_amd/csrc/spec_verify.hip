@@ -552,7 +552,7 @@ SV_API int spec_verify_scheduled(const sv_weights *w, const uint16_t *h, const u
   if (rc) return rc;
   if (!u || !(T > 0.f) || !isfinite(T)) return SV_EINVAL;
   if (!(survival_threshold > 0.f) || !(survival_threshold <= 1.f)) return SV_EINVAL;
-  if (budget_rows < B || (long)B * Kmax > 8192) return SV_EINVAL;
+  if (budget_rows < B || B > 8192 || (long)B * Kmax > 8192) return SV_EINVAL;
   if (Kmax > 0 && (!h_draft || !aligned16(h_draft))) return SV_EINVAL;
   Plan p;
   if (!make_plan(SV_MODE_SCHEDULED, B, Kmax, w, budget_rows, p)) return SV_EINVAL;

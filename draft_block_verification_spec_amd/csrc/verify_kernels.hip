@@ -9,6 +9,7 @@
 //    answer spoiled?": at temperature 0 the check is an argmax match.
 //  * DSpark summary page: the verify length of each request follows the
 //    estimated survival probability of its draft prefix, under a capacity budget.
+#include <atomic>
 #include "sv_device.h"
 
 namespace sv {
@@ -1638,7 +1639,25 @@ hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t st) {
   if (rows > 0)
     hipLaunchKernelGGL(k_row_conf, dim3((rows + (NT / 64) - 1) / (NT / 64)), dim3(NT), 0, st, a.parts_d, a.nslots_d,
                        rows, a.invT, a.conf, a.dev_status, a.diag, a.diag_row0);
+  // keys [B*Kmax], histogram [1025], lengths [B]: up to 68 KiB at the largest batch the
+  // entry point takes (B <= 8192, B*Kmax <= 8192), above the 64 KiB a launch gets unless
+  // the kernel's dynamic LDS limit is raised (once per device)
   const size_t shm = sizeof(int) * ((size_t)a.B * a.Kmax + 1025 + a.B);
+  constexpr size_t shm_max = sizeof(int) * (8192 + 1025 + 8192);
+  if (shm > shm_max) return hipErrorInvalidValue;
+  if (shm > 65536) {
+    static std::atomic<unsigned long long> attr_set{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const unsigned long long bit = 1ull << (dev & 63);
+    if (!(attr_set.load(std::memory_order_acquire) & bit)) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_schedule), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)shm_max);
+      if (e != hipSuccess) return e;
+      attr_set.fetch_or(bit, std::memory_order_release);
+    }
+  }
   hipLaunchKernelGGL(k_schedule, dim3(1), dim3(1024), shm, st, a);
   return hipGetLastError();
 }

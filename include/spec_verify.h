@@ -188,7 +188,8 @@ int spec_verify_sample_noalloc(const sv_weights *w, const uint16_t *h, const uin
  * positions with the largest floor(1024 * s) are kept (ties: lower request, then lower
  * position).  Request b then runs the sampled rule on its first k_b drafts, with
  * u[b, 0..k_b-1] and the final coin u[b, Kmax].  Requires budget_rows >= B and
- * 0 < survival_threshold <= 1 and B*Kmax <= 8192.  verify_len (if given) receives k_b. */
+ * 0 < survival_threshold <= 1, B <= 8192 and B*Kmax <= 8192.  verify_len (if given)
+ * receives k_b. */
 int spec_verify_scheduled(const sv_weights *w, const uint16_t *h, const uint16_t *h_draft,
                           const int32_t *draft, const float *u, float T, float survival_threshold,
                           int budget_rows, int B, int Kmax, void *ws, size_t ws_bytes,

@@ -147,6 +147,8 @@ static void invalid_arguments() {
   const float thrs[] = {0.f, 1.5f, NAN};
   for (float thr : thrs)
     EXPECT(spec_verify_scheduled(&w, P16, P16, P32, PF, 1.f, thr, 64, 4, 15, ws, wsn, &o, nullptr) == SV_EINVAL);
+  EXPECT(spec_verify_scheduled(&w, P16, P16, P32, PF, 1.f, 0.3f, 16384, 8193, 1, ws, wsn, &o, nullptr) == SV_EINVAL);
+  EXPECT(spec_verify_scheduled(&w, P16, P16, P32, PF, 1.f, 0.3f, 16384, 8193, 0, ws, wsn, &o, nullptr) == SV_EINVAL);
   sv_outputs o2 = outputs();
   o2.accepted_len = nullptr;
   EXPECT(spec_verify_greedy(&w, P16, P32, 1, 4, ws, wsn, &o2, nullptr) == SV_EINVAL);

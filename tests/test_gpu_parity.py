@@ -428,6 +428,17 @@ def test_scheduled_parity_budget_192_binding():
     assert (vl + 1).sum() == 192
 
 
+# The largest batch the scheduled call takes: 8192 requests of one draft each, so the
+# schedule's keys, key histogram and lengths need 68 KiB of LDS (over the 64 KiB a launch
+# gets by default); the budget binds (3808 of the 8192 drafts kept).
+SCHED_MAX = wl.Workload("sched_max", 96, B=8192, K=1, d=64, d_ff=0, V=257, T=1.0, sigma=(0.3, 1.2),
+                        gain=(1.0, 8.0), threshold=0.3, budget=12000)
+
+
+def test_scheduled_parity_largest_batch():
+    _run_scheduled(SCHED_MAX)
+
+
 def _run_scheduled(wk, expect_bound=True):
     data = wl.generate(wk)
     W = oracle.Weights.from_bits(data)
