@@ -19,6 +19,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libspecverify.so")
 
 SV_OK, SV_EINVAL, SV_EWORKSPACE, SV_EHIP, SV_ESCRATCH = 0, -1, -2, -3, -4
+SV_MAX_K = 8190  # largest K (Kmax) of a greedy, sampled or scheduled call
 SV_STATIC_SCRATCH_BYTES = 32 << 20
 SV_DEV_OK, SV_DEV_BAD_TOKEN, SV_DEV_NONFINITE, SV_DEV_BAD_COMMIT, SV_DEV_BAD_TREE, SV_DEV_TIMEOUT = 0, 1, 2, 3, 4, 5
 SV_MODE_GREEDY, SV_MODE_SAMPLE, SV_MODE_SCHEDULED, SV_MODE_PROPOSE = 0, 1, 2, 3

@@ -392,6 +392,9 @@ hipError_t run_mlp(const Plan &p, const sv_weights *w, const uint16_t *h, int M,
 int check_common(const sv_weights *w, const uint16_t *h, const int32_t *draft, int B, int K, void *ws,
                  const sv_outputs *out) {
   if (!valid_weights(w) || !h || B < 1 || K < 0 || !out) return SV_EINVAL;
+  // the acceptance kernels keep a request's row normalisers in LDS: 2 K + 2 floats,
+  // within the 64 KiB a launch gets
+  if (K > SV_MAX_K) return SV_EINVAL;
   if (K > 0 && !draft) return SV_EINVAL;
   if (!out->accepted_len || !out->emitted || !out->tau) return SV_EINVAL;
   if (!aligned16(h) || !aligned16(w->w_lm)) return SV_EINVAL;

@@ -62,6 +62,7 @@ extern "C" {
 
 #define SV_OK 0
 #define SV_EINVAL (-1)      /* bad sizes, NULL required pointer, misalignment, T <= 0, budget < B */
+#define SV_MAX_K 8190       /* largest K (Kmax) of a greedy, sampled or scheduled call */
 #define SV_EWORKSPACE (-2)  /* ws_bytes smaller than sv_workspace_bytes() */
 #define SV_EHIP (-3)        /* a HIP launch or runtime call failed */
 #define SV_ESCRATCH (-4)    /* spec_verify_sample_noalloc: the sizes need more than SV_STATIC_SCRATCH_BYTES */

@@ -116,6 +116,11 @@ def test_entry_points_reject_invalid_arguments(lib):
     for thr in (0.0, 1.5, float("nan")):
         assert lib.spec_verify_scheduled(ctypes.byref(w), P, P, P, P, 1.0, thr, 64, 4, 15, ws, wsn, ctypes.byref(o),
                                          None) == b.SV_EINVAL
+    # K beyond SV_MAX_K = 8190 (the acceptance kernels' LDS), sampled, greedy and scheduled
+    assert lib.spec_verify_sample(ctypes.byref(w), P, P, P, P, 1.0, 1, 8191, ws, wsn, ctypes.byref(o), None) == b.SV_EINVAL
+    assert lib.spec_verify_greedy(ctypes.byref(w), P, P, 1, 8191, ws, wsn, ctypes.byref(o), None) == b.SV_EINVAL
+    assert lib.spec_verify_scheduled(ctypes.byref(w), P, P, P, P, 1.0, 0.3, 16, 1, 8192, ws, wsn, ctypes.byref(o),
+                                     None) == b.SV_EINVAL
     # scheduled: more than 8192 requests, or more than 8192 draft positions
     for B, K in ((8193, 0), (8193, 1), (4097, 2)):
         assert lib.spec_verify_scheduled(ctypes.byref(w), P, P, P, P, 1.0, 0.3, 16384, B, K, ws, wsn,
